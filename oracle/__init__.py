@@ -1,0 +1,4 @@
+"""Float64 CPU oracle for FAVOR+ attention (test infrastructure only; the
+product path never imports it)."""
+from .favor_oracle import *  # noqa: F401,F403
+from .favor_oracle import __all__  # noqa: F401

@@ -1,0 +1,159 @@
+"""Float64 CPU oracle for FAVOR+ attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's smoke entry and the benchmark's CPU-baseline leg
+may import this module.  The product path (the HIP library and its Python
+binding) never calls it and shares no code with it.
+
+Everything here is plain NumPy in float64, written from the three source pages:
+
+* "Linear Attention > Performer: Unbiased Softmax Approximation" (P1): the
+  feature-map equation, the code cell In[25] (feature map and reassociated
+  attention) and the experiment of In[26] / Out[27].
+* "Performer -- 用随机特征把 softmax attention 拉成线性复杂度" (P2, study notes on
+  performer-2020): section 核心要点 (key points: kernel view, reordering,
+  linearised denominator), the 换顺序 diagram and 案例 2 (causal prefix sum).
+* "Linear Attention > Kernel Feature Maps" (P3): the softmax-kernel equation
+  and section 4, positive random features.
+
+Conventions: X is (L, d) per head, the projection W is (m, d) with rows
+omega_i, and every function takes the values actually handed to the device,
+upcast to float64.  No stabiliser, no 1/sqrt(d) temperature and no rescaling
+of eps are applied: the caller pre-scales Q and K if it wants a temperature.
+
+Readings of points the pages leave open (each also listed in the design doc):
+* causal denominator = phi(q_i) . sum_{j<=i} phi(k_j) + eps, by analogy with
+  the non-causal denominator (P2 key points; P1 In[25]);
+* the causal sum includes the diagonal j = i (P2 案例 2 says j <= i);
+* eps is added after the dot product and never to the numerator (P1 In[25]);
+* the 1/sqrt(m) factor is kept (P1 feature-map equation, P3 section 4).
+
+Pins: tests/test_oracle_pins.py checks every function here against the worked
+example's printed table, closed forms, Monte-Carlo moments and brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "favor_features", "attn_quadratic", "attn_noncausal", "attn_causal",
+    "attn_rows", "softmax_attention", "per_head", "head_projection",
+]
+
+
+def favor_features(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Positive random features, phi(x) = exp(-|x|^2/2) / sqrt(m) *
+    [exp(omega_1 . x), ..., exp(omega_m . x)].
+
+    Follows the feature-map equation of P1 (and P3 section 4): the projection
+    x W^T, minus half the squared norm of x, exponentiated, divided by sqrt(m).
+    x: (..., d), w: (m, d).  Returns (..., m) float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    m = w.shape[0]
+    proj = x @ w.T
+    half_sq_norm = 0.5 * np.sum(x * x, axis=-1, keepdims=True)
+    return np.exp(proj - half_sq_norm) / np.sqrt(m)
+
+
+def attn_quadratic(q, k, v, w, eps: float = 1e-6, causal: bool = False) -> np.ndarray:
+    """The definition: A = phi(Q) phi(K)^T (an L x L matrix of kernel
+    estimates), optionally masked to keys j <= query i, then
+    O = (A V) / (A 1 + eps) row by row.
+
+    This is the left-to-right product order of the 换顺序 diagram in P2 (the
+    order FAVOR+ avoids), with the normaliser of P2's key points.
+    """
+    fq = favor_features(q, w)
+    fk = favor_features(k, w)
+    a = fq @ fk.T
+    if causal:
+        a = np.tril(a)
+    num = a @ np.asarray(v, dtype=np.float64)
+    den = a.sum(axis=1) + eps
+    return num / den[:, None]
+
+
+def attn_noncausal(q, k, v, w, eps: float = 1e-6) -> np.ndarray:
+    """Reassociated non-causal attention, in the order of P1 In[25] and the
+    right-hand side of P2's 换顺序 diagram: first the m x d state
+    M = phi(K)^T V and the key sum z = phi(K)^T 1, then
+    O = (phi(Q) M) / (phi(Q) z + eps)."""
+    fq = favor_features(q, w)
+    fk = favor_features(k, w)
+    v = np.asarray(v, dtype=np.float64)
+    state = fk.T @ v
+    key_sum = fk.sum(axis=0)
+    num = fq @ state
+    den = fq @ key_sum + eps
+    return num / den[:, None]
+
+
+def attn_causal(q, k, v, w, eps: float = 1e-6) -> np.ndarray:
+    """Causal attention by the running prefix sum of P2 案例 2: walking the
+    tokens in order, S_i = S_{i-1} + phi(k_i) v_i^T (an m x d matrix) and
+    z_i = z_{i-1} + phi(k_i); the output is
+    o_i = phi(q_i)^T S_i / (phi(q_i)^T z_i + eps).
+
+    One Python step per token; O(L m d) time and O(m d) state.
+    """
+    fq = favor_features(q, w)
+    fk = favor_features(k, w)
+    v = np.asarray(v, dtype=np.float64)
+    L, d = v.shape
+    m = fq.shape[1]
+    state = np.zeros((m, d))
+    key_sum = np.zeros(m)
+    out = np.empty((L, d))
+    for i in range(L):
+        state += np.outer(fk[i], v[i])
+        key_sum += fk[i]
+        out[i] = (fq[i] @ state) / (fq[i] @ key_sum + eps)
+    return out
+
+
+def attn_rows(q, k, v, w, rows, eps: float = 1e-6, causal: bool = False) -> np.ndarray:
+    """Selected output rows by the definition: for each query i,
+    a_j = phi(q_i) . phi(k_j) over the keys it sees (all keys, or j <= i when
+    causal), o_i = sum_j a_j v_j / (sum_j a_j + eps).
+
+    Used for sampled-row checks at sizes where the full output is too big.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    fq = favor_features(np.asarray(q)[rows], w)
+    fk = favor_features(k, w)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((len(rows), v.shape[1]))
+    for r, i in enumerate(rows):
+        seen = slice(0, i + 1) if causal else slice(None)
+        a = fk[seen] @ fq[r]
+        out[r] = (a @ v[seen]) / (a.sum() + eps)
+    return out
+
+
+def softmax_attention(q, k, v, scale: float = 1.0) -> np.ndarray:
+    """Exact attention softmax(scale * Q K^T) V, the quantity the random
+    features estimate (P3's softmax-kernel equation; P2 key points write the
+    weights with a 1/sqrt(d) temperature).  The row maximum is subtracted
+    before exponentiating, which leaves the softmax unchanged."""
+    s = scale * (np.asarray(q, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ np.asarray(v, dtype=np.float64)
+
+
+def head_projection(w: np.ndarray, h: int) -> np.ndarray:
+    """The projection of head h: W is (Hw, m, d) with Hw = 1 (shared by all
+    heads) or Hw = H (one per head)."""
+    return w[0] if w.shape[0] == 1 else w[h]
+
+
+def per_head(fn, q, k, v, w, **kw) -> np.ndarray:
+    """Apply a single-head function to every (b, h) of [B, H, L, d] inputs."""
+    B, H, L, _ = q.shape
+    out = np.empty(q.shape[:3] + (v.shape[-1],))
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = fn(q[b, h], k[b, h], v[b, h], head_projection(w, h), **kw)
+    return out
