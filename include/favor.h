@@ -1,0 +1,121 @@
+/*
+ * favor.h -- C ABI of the MI355X (gfx950) FAVOR+ attention library.
+ *
+ * FAVOR+ replaces softmax attention by positive random features:
+ *   phi(x) = exp(W x - |x|^2/2) / sqrt(m)      (feature-map equation of
+ *            "Linear Attention > Performer: Unbiased Softmax Approximation";
+ *            section 4 of "Linear Attention > Kernel Feature Maps")
+ * and computes attention in the reassociated order
+ *   O = phi(Q) (phi(K)^T V) / (phi(Q) (phi(K)^T 1) + eps)
+ * (code cell In[25] of the Performer page; key points and the reordering
+ * diagram of the performer-2020 study notes), or, causally, with the running
+ * m x d state S_i = sum_{j<=i} phi(k_j) v_j^T (case 2 of the study notes).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    owned by the caller; the library never allocates, frees or keeps them.
+ *  - Q, K, V, O, X are contiguous row-major [B, H, L, d]; Phi is [B, H, L, m].
+ *  - W is float32 [Hw, m, d] (row i of a head is omega_i) with Hw = 1 (one
+ *    projection shared by all heads) or Hw = H (one per head).  W is used as
+ *    given: the library samples nothing and applies no 1/sqrt(d) temperature;
+ *    a caller who wants one pre-scales Q and K.
+ *  - dtype FAVOR_BF16: Q, K, V, X and O are bfloat16; W is rounded to bf16
+ *    (round to nearest even) for the matrix cores; features, states and sums
+ *    are accumulated in float32.  FAVOR_F32: everything is float32.
+ *  - Supported shapes: d in {32, 64, 128}; m a multiple of 32 with
+ *    32 <= m <= 512; L >= 1; B, H >= 1; B*H*L*max(d,m) < 2^31.
+ *  - stream is a hipStream_t passed as void* (NULL = default stream).  Calls
+ *    only enqueue work; results are valid once the stream has been
+ *    synchronised.
+ *  - Errors are returned, never thrown.  Arguments are validated before
+ *    anything is enqueued: a non-OK return means nothing was launched, except
+ *    FAVOR_ERR_HIP, which reports a launch failure (hipGetLastError).
+ *    Pointer values other than NULL cannot be checked on the host.
+ *  - Calls are thread-safe as long as concurrent calls use distinct
+ *    workspaces.
+ */
+#ifndef FAVOR_H
+#define FAVOR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FAVOR_F32 = 0, FAVOR_BF16 = 1 } favor_dtype;
+
+typedef enum {
+  FAVOR_OK = 0,
+  FAVOR_ERR_NULL = 1,         /* a required pointer is NULL                      */
+  FAVOR_ERR_SHAPE = 2,        /* B, H, L < 1, Hw not in {1, H}, or size overflow  */
+  FAVOR_ERR_UNSUPPORTED = 3,  /* d, m or dtype outside the supported set         */
+  FAVOR_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required         */
+  FAVOR_ERR_HIP = 5,          /* the HIP runtime reported an error               */
+  FAVOR_ERR_INTERNAL = 6      /* library bug; please report                      */
+} favor_status;
+
+/* Version of this ABI (incremented on incompatible changes). */
+int favor_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* favor_status_string(favor_status s);
+
+/*
+ * Bytes of device workspace that favor_attn_noncausal (causal = 0) or
+ * favor_attn_causal (causal = 1) needs for these shapes on the current
+ * device (the split of L over workgroups depends on its compute-unit
+ * count).  Returns 0 when the arguments are invalid.  The workspace holds
+ * float32 partial states and has no meaning between calls; it needs no
+ * initialisation.  Its base must be 256-byte aligned.
+ */
+size_t favor_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype);
+
+/*
+ * Phi = phi(X) for every row of X: Phi[b,h,l,:] = exp(W_h x - |x|^2/2)/sqrt(m)
+ * (Performer page, feature-map equation), written as float32.  Used to check
+ * the fused feature map; the attention entry points never store features.
+ */
+favor_status favor_features(const void* X, const float* W, int Hw, float* Phi,
+                            int B, int H, int L, int d, int m,
+                            favor_dtype dtype, void* stream);
+
+/*
+ * Non-causal FAVOR+ attention (Performer page, In[25]; study notes, key
+ * points): per (b, h), the state M = phi(K)^T V (m x d) and key sum
+ * z = phi(K)^T 1 are reduced over L, then O = (phi(Q) M) / (phi(Q) z + eps),
+ * eps added to the denominator only.  Deterministic: the reduction order
+ * depends only on the shapes and the device's compute-unit count.
+ */
+favor_status favor_attn_noncausal(const void* Q, const void* K, const void* V,
+                                  const float* W, int Hw, void* O,
+                                  int B, int H, int L, int d, int m, float eps,
+                                  favor_dtype dtype, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/*
+ * Causal FAVOR+ attention (study notes, case 2): with S_i = sum_{j<=i}
+ * phi(k_j) v_j^T and z_i = sum_{j<=i} phi(k_j) (the diagonal included),
+ * o_i = phi(q_i)^T S_i / (phi(q_i)^T z_i + eps).  The denominator is the
+ * causal analogue of the non-causal one (the notes give the numerator
+ * only).  Computed in chunks of 64 tokens: inside a chunk the masked
+ * chunk-by-chunk score tile is multiplied by V; across chunks the m x d
+ * state is carried as a prefix sum.  Deterministic as above.
+ */
+favor_status favor_attn_causal(const void* Q, const void* K, const void* V,
+                               const float* W, int Hw, void* O,
+                               int B, int H, int L, int d, int m, float eps,
+                               favor_dtype dtype, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Dispatcher: favor_attn_causal when causal != 0, else favor_attn_noncausal. */
+favor_status favor_attn(const void* Q, const void* K, const void* V,
+                        const float* W, int Hw, void* O,
+                        int B, int H, int L, int d, int m, float eps, int causal,
+                        favor_dtype dtype, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAVOR_H */

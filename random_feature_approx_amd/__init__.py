@@ -1,0 +1,170 @@
+"""Python binding of the gfx950 FAVOR+ library (libfavor.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/favor.h.  PyTorch provides device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing, or the tensors are not on a HIP device, calls raise.
+
+Functions
+    features(x, w)                          phi(x) as float32 [B, H, L, m]
+    attn(q, k, v, w, causal=False, eps=1e-6) FAVOR+ attention, output like q
+    attn_noncausal(...), attn_causal(...)    the two paths explicitly
+    workspace_bytes(B, H, L, d, m, causal, dtype)
+
+Shapes: q, k, v are [B, H, L, d] (bfloat16 or float32, same dtype, contiguous);
+w is float32 [m, d] (shared by all heads) or [H, m, d] (one per head).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal",
+           "workspace_bytes", "FavorError", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libfavor.so"
+_lib = None
+
+STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid shape", 3: "unsupported d, m or dtype",
+          4: "workspace missing or too small", 5: "HIP runtime error", 6: "internal error"}
+F32, BF16 = 0, 1
+
+
+class FavorError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, 'unknown status')} (status {code})")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIBNAME)
+
+
+def load():
+    """Load libfavor.so (built by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m random_feature_approx_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.favor_abi_version.restype = i
+    lib.favor_abi_version.argtypes = []
+    lib.favor_status_string.restype = ctypes.c_char_p
+    lib.favor_status_string.argtypes = [i]
+    lib.favor_workspace_bytes.restype = sz
+    lib.favor_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.favor_features.restype = i
+    lib.favor_features.argtypes = [vp, vp, i, vp, i, i, i, i, i, i, vp]
+    attn_args = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    for name in ("favor_attn_noncausal", "favor_attn_causal"):
+        getattr(lib, name).restype = i
+        getattr(lib, name).argtypes = attn_args
+    lib.favor_attn.restype = i
+    lib.favor_attn.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    if lib.favor_abi_version() != 1:
+        raise RuntimeError("libfavor.so has an unexpected ABI version")
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _check_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("FAVOR+ tensors must live on a HIP device (no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError("FAVOR+ tensors must be contiguous")
+
+
+def _proj(w, H, m_d):
+    """Return (w, Hw) with w float32 [Hw, m, d] contiguous on the device."""
+    torch = _torch()
+    if w.dtype != torch.float32:
+        raise TypeError("the projection W must be float32")
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+    if w.dim() != 3 or tuple(w.shape[1:]) != m_d or w.shape[0] not in (1, H):
+        raise ValueError(f"W must be [m, d] or [H, m, d], got {tuple(w.shape)}")
+    return w.contiguous(), int(w.shape[0])
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def workspace_bytes(B: int, H: int, L: int, d: int, m: int, causal: bool, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(load().favor_workspace_bytes(B, H, L, d, m, int(bool(causal)), code))
+
+
+def features(x, w):
+    """phi(x) = exp(W x - |x|^2/2)/sqrt(m) as float32 [B, H, L, m]."""
+    lib = load()
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, L, d]")
+    B, H, L, d = x.shape
+    w, hw = _proj(w, H, (w.shape[-2], d))
+    m = int(w.shape[1])
+    _check_device(x, w)
+    phi = torch.empty((B, H, L, m), dtype=torch.float32, device=x.device)
+    st = lib.favor_features(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), hw,
+                            ctypes.c_void_p(phi.data_ptr()), B, H, L, d, m, _dtype_code(x), _stream())
+    if st != 0:
+        raise FavorError("favor_features", st)
+    return phi
+
+
+def attn(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, workspace=None):
+    """FAVOR+ attention; returns O with the shape and dtype of q."""
+    lib = load()
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, L, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, L, d = q.shape
+    w, hw = _proj(w, H, (w.shape[-2], d))
+    m = int(w.shape[1])
+    _check_device(q, k, v, w)
+    code = _dtype_code(q)
+    o = torch.empty_like(q) if out is None else out
+    _check_device(o)
+    need = int(lib.favor_workspace_bytes(B, H, L, d, m, int(bool(causal)), code))
+    if need == 0:
+        raise FavorError("favor_workspace_bytes", 2)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    fn = lib.favor_attn_causal if causal else lib.favor_attn_noncausal
+    st = fn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(w.data_ptr()), hw, ctypes.c_void_p(o.data_ptr()), B, H, L, d, m,
+            float(eps), code, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream())
+    if st != 0:
+        raise FavorError("favor_attn_causal" if causal else "favor_attn_noncausal", st)
+    return o
+
+
+def attn_noncausal(q, k, v, w, eps: float = 1e-6, **kw):
+    return attn(q, k, v, w, causal=False, eps=eps, **kw)
+
+
+def attn_causal(q, k, v, w, eps: float = 1e-6, **kw):
+    return attn(q, k, v, w, causal=True, eps=eps, **kw)

@@ -1,0 +1,149 @@
+// C ABI of the FAVOR+ library: argument validation, the work split (plan),
+// workspace layout and dispatch to the kernels.  See include/favor.h.
+#include "favor_internal.hpp"
+
+#include <stdint.h>
+
+namespace favor {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+static favor_status check_shapes(int B, int H, int L, int d, int m, int Hw, favor_dtype dt) {
+  if (B < 1 || H < 1 || L < 1) return FAVOR_ERR_SHAPE;
+  if (Hw != 1 && Hw != H) return FAVOR_ERR_SHAPE;
+  if (dt != FAVOR_F32 && dt != FAVOR_BF16) return FAVOR_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 128) return FAVOR_ERR_UNSUPPORTED;
+  if (m < 32 || m > 512 || (m % 32) != 0) return FAVOR_ERR_UNSUPPORTED;
+  const int64_t big = (int64_t)B * H * L * (d > m ? d : m);
+  if (big >= ((int64_t)1 << 31)) return FAVOR_ERR_SHAPE;
+  return FAVOR_OK;
+}
+
+bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus) {
+  if (check_shapes(B, H, L, d, m, Hw, dt) != FAVOR_OK || num_cus <= 0) return false;
+  p.B = B; p.H = H; p.L = L; p.D = d; p.M = m; p.Hw = Hw; p.causal = causal ? 1 : 0; p.dt = dt;
+  p.BH = B * H;
+  p.esize = dt == FAVOR_BF16 ? 2 : 4;
+  // reduction split: about two workgroups per compute unit, ranges of at
+  // least 256 tokens, whole 64-token chunks.
+  p.fbw = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
+  const int nfb = m / 32;
+  p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
+  const int target = 2 * num_cus;
+  const int per_head = p.BH * p.fgroups;
+  int splits = (target + per_head - 1) / per_head;
+  const int max_splits = (L + 255) / 256;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int len = (L + splits - 1) / splits;
+  len = (len + 63) / 64 * 64;
+  p.split_len = len;
+  p.splits = (L + len - 1) / len;
+  // apply: groups of 4 waves x TB x 32 tokens of one head
+  const int tb = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
+  p.apply_tile = tb * 32;
+  const int gph = (L + 4 * p.apply_tile - 1) / (4 * p.apply_tile);
+  const int total = p.BH * gph;
+  p.apply_steps = (total + target - 1) / target;
+  if (p.apply_steps < 1) p.apply_steps = 1;
+  p.apply_groups = (total + p.apply_steps - 1) / p.apply_steps;
+  const int rs = d * p.esize + 16;
+  int fch = 81920 / (2 * rs + p.esize);
+  fch = fch / 32 * 32;
+  p.fch = fch < m ? fch : m;
+  // workspace
+  size_t off = 0;
+  p.off_part = off;
+  off += align256((size_t)p.BH * p.splits * m * d * sizeof(float));
+  p.off_partz = off;
+  off += align256((size_t)p.BH * p.splits * m * sizeof(float));
+  p.off_mstate = off;
+  off += align256((size_t)p.BH * m * d * p.esize);
+  p.off_zstate = off;
+  off += align256((size_t)p.BH * m * p.esize);
+  p.total = off;
+  return true;
+}
+
+}  // namespace favor
+
+using namespace favor;
+
+extern "C" {
+
+int favor_abi_version(void) { return 1; }
+
+const char* favor_status_string(favor_status s) {
+  switch (s) {
+    case FAVOR_OK: return "ok";
+    case FAVOR_ERR_NULL: return "null pointer argument";
+    case FAVOR_ERR_SHAPE: return "invalid shape";
+    case FAVOR_ERR_UNSUPPORTED: return "unsupported d, m or dtype";
+    case FAVOR_ERR_WORKSPACE: return "workspace missing or too small";
+    case FAVOR_ERR_HIP: return "HIP runtime error";
+    case FAVOR_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+size_t favor_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype) {
+  Plan p;
+  if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count())) return 0;
+  return p.total;
+}
+
+favor_status favor_features(const void* X, const float* W, int Hw, float* Phi, int B, int H, int L, int d, int m,
+                            favor_dtype dtype, void* stream) {
+  if (!X || !W || !Phi) return FAVOR_ERR_NULL;
+  favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
+  if (st != FAVOR_OK) return st;
+  Plan p;
+  if (!make_plan(p, B, H, L, d, m, Hw, 0, dtype, device_cu_count())) return FAVOR_ERR_HIP;
+  return launch_features(p, X, W, Phi, (hipStream_t)stream) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+static favor_status attn_common(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
+                                int H, int L, int d, int m, float eps, int causal, favor_dtype dtype, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!Q || !K || !V || !W || !O) return FAVOR_ERR_NULL;
+  favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
+  if (st != FAVOR_OK) return st;
+  Plan p;
+  if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count())) return FAVOR_ERR_HIP;
+  if (!ws || ws_bytes < p.total || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
+  Tensors t{Q, K, V, W, O, eps, (char*)ws};
+  hipError_t e = causal ? launch_causal(p, t, (hipStream_t)stream) : launch_noncausal(p, t, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return FAVOR_ERR_UNSUPPORTED;
+  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+favor_status favor_attn_noncausal(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
+                                  int H, int L, int d, int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, 0, dtype, ws, ws_bytes, stream);
+}
+
+favor_status favor_attn_causal(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
+                               int H, int L, int d, int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, 1, dtype, ws, ws_bytes, stream);
+}
+
+favor_status favor_attn(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B, int H,
+                        int L, int d, int m, float eps, int causal, favor_dtype dtype, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, causal, dtype, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

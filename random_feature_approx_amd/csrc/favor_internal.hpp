@@ -1,0 +1,50 @@
+// Host-side plan and launcher declarations shared by the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "../../include/favor.h"
+
+namespace favor {
+
+// How one call is split over workgroups, and where its scratch lives inside
+// the caller's workspace.  Computed only from the shapes and the device's
+// compute-unit count, so workspace sizing and the call agree.
+struct Plan {
+  int B, H, L, D, M, Hw, causal;
+  favor_dtype dt;
+  int BH;
+  int esize;            // bytes per element of Q, K, V, O
+  // K-side reduction (non-causal state, or causal span aggregates)
+  int splits;           // token ranges per head
+  int split_len;        // tokens per range (multiple of 64)
+  int fgroups;          // feature groups per head (workgroups that share K, V tiles)
+  int fbw;              // 32-feature blocks per wave
+  // Q-side apply (non-causal)
+  int apply_tile;       // tokens per wave per step
+  int apply_groups;     // total workgroups
+  int apply_steps;      // 4-tile steps per workgroup
+  int fch;              // features per LDS chunk
+  // workspace offsets (bytes)
+  size_t off_part, off_partz, off_mstate, off_zstate, total;
+};
+
+bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus);
+int device_cu_count();
+
+struct Tensors {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* w;
+  void* o;
+  float eps;
+  char* ws;
+};
+
+hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
+hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
+
+}  // namespace favor

@@ -1,0 +1,659 @@
+// Non-causal FAVOR+ on gfx950: the fused feature map, the K-side state
+// reduction, its fixed-order combine, and the Q-side apply.
+//
+// Formulas (see include/favor.h for the sources):
+//   phi(x) = exp(W x - |x|^2/2) / sqrt(m)
+//          = exp2(x . (W log2 e) - (|x|^2/2 + ln(m)/2) log2 e)
+//   M = phi(K)^T V,  z = phi(K)^T 1,  O = phi(Q) M / (phi(Q) z + eps)
+//
+// Every step runs on the matrix cores except the exponentials, the norms and
+// the final division: the projection x W^T is a 32x32 MFMA block per 32
+// tokens x 32 features, its accumulator is exponentiated in registers and
+// fed, without leaving registers, as the operand of the next contraction
+// (phi^T V on the K side, M^T phi^T on the Q side).
+#include "favor_device.hpp"
+#include "favor_internal.hpp"
+
+#include <math.h>
+
+namespace favor {
+
+// LDS row stride in bytes for a [rows][D] tile of element size ES: 16 bytes
+// of padding move consecutive rows to different LDS banks.
+template <int D, int ES> struct Rows {
+  static constexpr int CPR = D * ES / 16;      // 16-byte chunks per row
+  static constexpr int RS = D * ES + 16;       // padded row stride (bytes)
+};
+
+// Load the 16-byte chunks of a [TT][D] tile that thread `tid` owns into
+// registers; rows at or beyond nvalid read as zero.
+template <class E, int D, int TT, int NT>
+struct TileLoader {
+  static constexpr int CPR = Rows<D, sizeof(E)>::CPR;
+  static constexpr int NCH = (TT * CPR + NT - 1) / NT;
+  u32x4 r[NCH];
+  __device__ __forceinline__ void load(const E* src, int nvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      int c = tid + i * NT;
+      int row = c / CPR, cc = c % CPR;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (c < TT * CPR && row < nvalid)
+        v = __builtin_nontemporal_load((const u32x4*)((const char*)src + ((size_t)row * D) * sizeof(E) + cc * 16));
+      r[i] = v;
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      int c = tid + i * NT;
+      if (c < TT * CPR) {
+        int row = c / CPR, cc = c % CPR;
+        *(u32x4*)(lds + row * Rows<D, sizeof(E)>::RS + cc * 16) = r[i];
+      }
+    }
+  }
+  // Store with the elements converted to the projection operand type.
+  __device__ __forceinline__ void store_proj(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      int c = tid + i * NT;
+      if (c < TT * CPR) {
+        int row = c / CPR, cc = c % CPR;
+        u32x4 v = r[i];
+        if constexpr (sizeof(E) == 2)
+          v = u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
+        *(u32x4*)(lds + row * Rows<D, sizeof(E)>::RS + cc * 16) = v;
+      }
+    }
+  }
+  // Squared norm of each row, reduced over the CPR consecutive lanes that
+  // hold it; the lane holding chunk 0 of a row writes bias(row) to sb.
+  __device__ __forceinline__ void row_bias(float* sb, int tid, int nvalid, float half_ln_m) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      int c = tid + i * NT;
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(E) == 2) {
+          float a = bf16_lo(r[i][j]), b = bf16_hi(r[i][j]);
+          ss = fmaf(a, a, ss);
+          ss = fmaf(b, b, ss);
+        } else {
+          float a = as_f32(r[i][j]);
+          ss = fmaf(a, a, ss);
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+      int row = c / CPR;
+      if (c < TT * CPR && (c % CPR) == 0)
+        sb[row] = row < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
+    }
+  }
+};
+
+// Projection fragment of W (lane = feature f, d-major slots), scaled by
+// log2 e and converted to the projection operand type (fp16 for bf16 inputs).
+template <class Tr, int D>
+__device__ __forceinline__ typename Tr::frag w_frag(const float* wrow, int hh, int s, bool ok) {
+  const int d0 = (D / 2) * hh + Tr::VPS * s;
+  if constexpr (Tr::VPS == 8) {
+    f32x4 a = ok ? *(const f32x4*)(wrow + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 b = ok ? *(const f32x4*)(wrow + d0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 f;
+    f[0] = pack_f16(a[0] * kLog2e, a[1] * kLog2e);
+    f[1] = pack_f16(a[2] * kLog2e, a[3] * kLog2e);
+    f[2] = pack_f16(b[0] * kLog2e, b[1] * kLog2e);
+    f[3] = pack_f16(b[2] * kLog2e, b[3] * kLog2e);
+    return f;
+  } else {
+    return ok ? wrow[d0] * kLog2e : 0.f;
+  }
+}
+
+// Operand fragment of a row-major [.][D] tile in LDS for the lane's row,
+// d-major slots (k-step s, lane half hh).
+template <class Tr, int D>
+__device__ __forceinline__ typename Tr::frag row_frag(const char* rowp, int hh, int s) {
+  const int d0 = (D / 2) * hh + Tr::VPS * s;
+  if constexpr (Tr::VPS == 8) return *(const u32x4*)(rowp + d0 * 2);
+  else return *(const float*)(rowp + d0 * 4);
+}
+
+// Operand fragment holding, for column `col` (lane%32 of a 32-column block
+// starting at col0) of a row-major LDS tile, the 32-row block starting at row0
+// in c-row order for k-step s.  bf16: two transposed reads of 4 rows each;
+// f32: one element.
+template <class Tr, int RS>
+__device__ __forceinline__ typename Tr::frag col_frag(const char* base, int row0, int col0, int s, int lane) {
+  const int hh = lane >> 5;
+  if constexpr (Tr::VPS == 8) {
+    const int i16 = lane & 15, g = (lane >> 4) & 1;
+    const char* p = base + (row0 + 16 * s + 4 * hh + (i16 >> 2)) * RS + (col0 + 16 * g + 4 * (i16 & 3)) * 2;
+    u32x2 lo = lds_read_tr16(p);
+    u32x2 hi = lds_read_tr16(p + 8 * RS);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  } else {
+    return *(const float*)(base + (row0 + crow(s, hh)) * RS + (col0 + (lane & 31)) * 4);
+  }
+}
+
+// ===========================================================================
+// favor_features: Phi = phi(X), float32 [BH, L, M]
+// ===========================================================================
+struct FeatArgs {
+  const void* x;
+  const float* w;
+  float* phi;
+  int L, M, H, Hw;
+};
+
+template <class Tr, int D>
+__global__ __launch_bounds__(256) void k_features(FeatArgs a) {
+  using E = typename Tr::elem;
+  using F = typename Tr::frag;
+  constexpr int NKD = D / Tr::KS;
+  const int bh = blockIdx.y, head = bh % a.H;
+  const int lane = lane_id(), w = wave_id(), hh = lane >> 5, l32 = lane & 31;
+  const int tok = blockIdx.x * 128 + w * 32 + l32;
+  const bool tok_ok = tok < a.L;
+  const E* xrow = (const E*)a.x + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * D;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
+  F xf[NKD];
+  float ss = 0.f;
+#pragma unroll
+  for (int s = 0; s < NKD; ++s) {
+    const int d0 = (D / 2) * hh + Tr::VPS * s;
+    if constexpr (Tr::VPS == 8) {
+      u32x4 v = tok_ok ? *(const u32x4*)(xrow + d0) : u32x4{0u, 0u, 0u, 0u};
+      xf[s] = Tr::to_proj(v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p = bf16_lo(v[j]), q = bf16_hi(v[j]);
+        ss = fmaf(p, p, fmaf(q, q, ss));
+      }
+    } else {
+      float v = tok_ok ? xrow[d0] : 0.f;
+      xf[s] = v;
+      ss = fmaf(v, v, ss);
+    }
+  }
+  ss += __shfl_xor(ss, 32);
+  const float bias = -(0.5f * ss + 0.5f * logf((float)a.M)) * kLog2e;
+  float* out = a.phi + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * a.M;
+  for (int fb = 0; fb < (a.M >> 5); ++fb) {
+    const float* wrow = wh + (size_t)(fb * 32 + l32) * D;
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int s = 0; s < NKD; ++s) acc = Tr::pmma(w_frag<Tr, D>(wrow, hh, s, true), xf[s], acc);
+    if (tok_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = exp2_fast(acc[4 * i + j] + bias);
+        *(f32x4*)(out + fb * 32 + 8 * i + 4 * hh) = v;
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// K-side reduction: per (token split, feature group, head) partial
+//   M_part[f][d] = sum_t phi(k_t)[f] v_t[d],  z_part[f] = sum_t phi(k_t)[f]
+// Wave w of the workgroup owns FBW blocks of 32 features; all four waves
+// share the K and V tiles staged in LDS.
+// ===========================================================================
+struct RedArgs {
+  const void* k;
+  const void* v;
+  const float* w;
+  float* part;   // [BH][splits][M][D]
+  float* partz;  // [BH][splits][M]
+  int L, M, H, Hw, splits, split_len;
+};
+
+template <class Tr, int D, int FBW>
+__global__ __launch_bounds__(256) void k_reduce(RedArgs a) {
+  using E = typename Tr::elem;
+  using F = typename Tr::frag;
+  constexpr int TT = 32;                    // tokens per tile
+  constexpr int NKD = D / Tr::KS;           // k-steps over d
+  constexpr int NDB = D / 32;               // 32-wide d blocks
+  constexpr int NKT = TT / Tr::KS;          // k-steps over a token tile
+  constexpr int RS = Rows<D, sizeof(E)>::RS;
+  __shared__ __attribute__((aligned(16))) char sK[TT * RS];
+  __shared__ __attribute__((aligned(16))) char sV[TT * RS];
+  __shared__ __attribute__((aligned(16))) float sBias[TT];
+
+  const int split = blockIdx.x, fg = blockIdx.y, bh = blockIdx.z;
+  const int head = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int nfb = a.M >> 5;
+  const int fb0 = (fg * 4 + w) * FBW;
+  const E* K = (const E*)a.k + (size_t)bh * a.L * D;
+  const E* V = (const E*)a.v + (size_t)bh * a.L * D;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
+  const float half_ln_m = 0.5f * logf((float)a.M);
+
+  F wf[FBW][NKD];
+#pragma unroll
+  for (int i = 0; i < FBW; ++i) {
+    const bool ok = fb0 + i < nfb;
+    const float* wrow = wh + (size_t)((ok ? fb0 + i : 0) * 32 + l32) * D;
+#pragma unroll
+    for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D>(wrow, hh, s, ok);
+  }
+  f32x16 st[FBW][NDB];
+  float zs[FBW];
+#pragma unroll
+  for (int i = 0; i < FBW; ++i) {
+    zs[i] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st[i][db] = zero16();
+  }
+
+  const int t0 = split * a.split_len;
+  const int t1 = min(a.L, t0 + a.split_len);
+  TileLoader<E, D, TT, 256> lk, lv;
+  if (t0 < t1) {
+    lk.load(K + (size_t)t0 * D, t1 - t0, tid);
+    lv.load(V + (size_t)t0 * D, t1 - t0, tid);
+  }
+  for (int t = t0; t < t1; t += TT) {
+    const int nvalid = min(TT, t1 - t);
+    __syncthreads();
+    lk.store_proj(sK, tid);
+    lv.store(sV, tid);
+    lk.row_bias(sBias, tid, nvalid, half_ln_m);
+    __syncthreads();
+    if (t + TT < t1) {                       // prefetch the next tile
+      lk.load(K + (size_t)(t + TT) * D, t1 - t - TT, tid);
+      lv.load(V + (size_t)(t + TT) * D, t1 - t - TT, tid);
+    }
+    F kf[NKD];
+#pragma unroll
+    for (int s = 0; s < NKD; ++s) kf[s] = row_frag<Tr, D>(sK + l32 * RS, hh, s);
+    float bv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 b4 = *(const f32x4*)(sBias + 8 * i + 4 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[4 * i + j] = b4[j];
+    }
+    F vf[NDB][NKT];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < NKT; ++s2) vf[db][s2] = col_frag<Tr, RS>(sV, 0, db * 32, s2, lane);
+
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) {
+      if (fb0 + i < nfb) {
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) acc = Tr::pmma(kf[s], wf[i][s], acc);   // P[t][f], lane = f
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = exp2_fast(acc[r] + bv[r]);
+#pragma unroll
+        for (int s2 = 0; s2 < NKT; ++s2) {
+          F pf = CFrag<Tr>::make(acc, s2);
+          if constexpr (Tr::VPS == 8) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zs[i] = dot2_bf16(pf[j], 0x3f803f80u, zs[i]);
+          } else {
+            zs[i] += pf;
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) st[i][db] = Tr::mma(pf, vf[db][s2], st[i][db]);
+        }
+      }
+    }
+  }
+
+  float* P = a.part + ((size_t)bh * a.splits + split) * a.M * D;
+  float* Pz = a.partz + ((size_t)bh * a.splits + split) * a.M;
+#pragma unroll
+  for (int i = 0; i < FBW; ++i) {
+    if (fb0 + i < nfb) {
+      const int f0 = (fb0 + i) * 32;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) P[(size_t)(f0 + crow(r, hh)) * D + db * 32 + l32] = st[i][db][r];
+      float z = zs[i] + __shfl_xor(zs[i], 32);
+      if (hh == 0) Pz[f0 + l32] = z;
+    }
+  }
+}
+
+// ===========================================================================
+// Combine: sum the partial states of a head in split order (deterministic)
+// and store the operand-type state used by the apply step.
+// ===========================================================================
+template <class E>
+__global__ __launch_bounds__(256) void k_combine(const float* part, const float* partz, E* mstate, E* zstate,
+                                                 int splits, int MD, int M) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx < MD) {
+    const float* p = part + (size_t)bh * splits * MD + idx;
+    float s = 0.f;
+    for (int i = 0; i < splits; ++i) s += p[(size_t)i * MD];
+    mstate[(size_t)bh * MD + idx] = (E)s;
+  } else if (idx < MD + M) {
+    const int j = idx - MD;
+    const float* p = partz + (size_t)bh * splits * M + j;
+    float s = 0.f;
+    for (int i = 0; i < splits; ++i) s += p[(size_t)i * M];
+    zstate[(size_t)bh * M + j] = (E)s;
+  }
+}
+
+// ===========================================================================
+// Q-side apply: O = phi(Q) M / (phi(Q) z + eps).
+// A workgroup walks a contiguous range of "groups" (4 waves x TB x 32 tokens
+// of one head).  W (log2 e scaled), M and z of the current head sit in LDS in
+// chunks of FCH features; with a single chunk they are loaded once per head.
+// Output is computed transposed, O^T = M^T phi(Q)^T, so each lane owns one
+// token and divides by its own denominator.
+// ===========================================================================
+struct ApplyArgs {
+  const void* q;
+  const float* w;
+  const void* mstate;   // [BH][M][D] operand type
+  const void* zstate;   // [BH][M]
+  void* o;
+  int L, M, H, Hw;
+  float eps;
+  int groups_per_head, groups_total, steps, fch;
+};
+
+template <class Tr, int D, int TB>
+__global__ __launch_bounds__(256) void k_apply(ApplyArgs a) {
+  using E = typename Tr::elem;
+  using F = typename Tr::frag;
+  constexpr int NKD = D / Tr::KS;
+  constexpr int NDB = D / 32;
+  constexpr int ES = sizeof(E);
+  constexpr int RS = Rows<D, ES>::RS;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int FCH = a.fch;
+  char* sW = smem;
+  char* sM = smem + FCH * RS;
+  E* sZ = (E*)(smem + 2 * FCH * RS);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int nch = (a.M + FCH - 1) / FCH;
+  const float half_ln_m = 0.5f * logf((float)a.M);
+  const int g0 = blockIdx.x * a.steps;
+  const int g1 = min(a.groups_total, g0 + a.steps);
+  int cur_bh = -1;
+  for (int g = g0; g < g1; ++g) {
+    const int bh = g / a.groups_per_head;
+    const int tbase = (g % a.groups_per_head) * (4 * TB * 32) + w * TB * 32;
+    const int head = bh % a.H;
+    const bool reload = nch > 1 || bh != cur_bh;
+    cur_bh = bh;
+    const E* Q = (const E*)a.q + (size_t)bh * a.L * D;
+
+    F qf[TB][NKD];
+    float bias[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int tok = tbase + tb * 32 + l32;
+      const bool ok = tok < a.L;
+      const E* qrow = Q + (size_t)(ok ? tok : 0) * D;
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) {
+        const int d0 = (D / 2) * hh + Tr::VPS * s;
+        if constexpr (Tr::VPS == 8) {
+          u32x4 v = ok ? __builtin_nontemporal_load((const u32x4*)(qrow + d0)) : u32x4{0u, 0u, 0u, 0u};
+          qf[tb][s] = Tr::to_proj(v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float p = bf16_lo(v[j]), q = bf16_hi(v[j]);
+            ss = fmaf(p, p, fmaf(q, q, ss));
+          }
+        } else {
+          float v = ok ? qrow[d0] : 0.f;
+          qf[tb][s] = v;
+          ss = fmaf(v, v, ss);
+        }
+      }
+      ss += __shfl_xor(ss, 32);
+      bias[tb] = -(0.5f * ss + half_ln_m) * kLog2e;
+    }
+
+    f32x16 oacc[TB][NDB];
+    float den[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      den[tb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[tb][db] = zero16();
+    }
+
+    for (int ch = 0; ch < nch; ++ch) {
+      const int f0 = ch * FCH;
+      const int nf = min(FCH, a.M - f0);
+      if (reload) {
+        __syncthreads();
+        const float* wh = a.w + ((size_t)(a.Hw == 1 ? 0 : head) * a.M + f0) * D;
+        for (int e = tid * 4; e < nf * D; e += 256 * 4) {
+          f32x4 x = *(const f32x4*)(wh + e);
+          const int row = e / D, col = e % D;
+          if constexpr (ES == 2) {
+            u32x2 pk = {pack_f16(x[0] * kLog2e, x[1] * kLog2e), pack_f16(x[2] * kLog2e, x[3] * kLog2e)};
+            *(u32x2*)(sW + row * RS + col * 2) = pk;
+          } else {
+            *(f32x4*)(sW + row * RS + col * 4) = x * kLog2e;
+          }
+        }
+        const char* ms = (const char*)a.mstate + ((size_t)bh * a.M + f0) * D * ES;
+        constexpr int CPR = Rows<D, ES>::CPR;
+        for (int c = tid; c < nf * CPR; c += 256) {
+          const int row = c / CPR, cc = c % CPR;
+          *(u32x4*)(sM + row * RS + cc * 16) = *(const u32x4*)(ms + (size_t)row * D * ES + cc * 16);
+        }
+        const E* zs = (const E*)a.zstate + (size_t)bh * a.M + f0;
+        for (int j = tid; j < nf; j += 256) sZ[j] = zs[j];
+        __syncthreads();
+      }
+      for (int fb = 0; fb < (nf >> 5); ++fb) {
+        F wfr[NKD];
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) wfr[s] = row_frag<Tr, D>(sW + (fb * 32 + l32) * RS, hh, s);
+        f32x16 pacc[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          pacc[tb] = zero16();
+#pragma unroll
+          for (int s = 0; s < NKD; ++s) pacc[tb] = Tr::pmma(wfr[s], qf[tb][s], pacc[tb]);   // P^T[f][t], lane = t
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pacc[tb][r] = exp2_fast(pacc[tb][r] + bias[tb]);
+        }
+        if constexpr (Tr::VPS == 8) {
+          u32x2 zf[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zf[i] = *(const u32x2*)(sZ + fb * 32 + 8 * i + 4 * hh);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            F mf[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) mf[db] = col_frag<Tr, RS>(sM, fb * 32, db * 32, s2, lane);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+              F pf = CFrag<Tr>::make(pacc[tb], s2);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) den[tb] = dot2_bf16(pf[k], zf[2 * s2 + (k >> 1)][k & 1], den[tb]);
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) oacc[tb][db] = Tr::mma(mf[db], pf, oacc[tb][db]);
+            }
+          }
+        } else {
+          float zf[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 z4 = *(const f32x4*)((const float*)sZ + fb * 32 + 8 * i + 4 * hh);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zf[4 * i + j] = z4[j];
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 16; ++s2) {
+            F mf[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) mf[db] = col_frag<Tr, RS>(sM, fb * 32, db * 32, s2, lane);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+              den[tb] = fmaf(pacc[tb][s2], zf[s2], den[tb]);
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) oacc[tb][db] = Tr::mma(mf[db], pacc[tb][s2], oacc[tb][db]);
+            }
+          }
+        }
+      }
+    }
+
+    E* O = (E*)a.o + (size_t)bh * a.L * D;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int tok = tbase + tb * 32 + l32;
+      const float inv = 1.0f / (den[tb] + __shfl_xor(den[tb], 32) + a.eps);
+      if (tok < a.L) {
+        E* orow = O + (size_t)tok * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d0 = db * 32 + 8 * i + 4 * hh;
+            if constexpr (ES == 2) {
+              u32x2 pk = {pack_bf16(oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv),
+                          pack_bf16(oacc[tb][db][4 * i + 2] * inv, oacc[tb][db][4 * i + 3] * inv)};
+              *(u32x2*)(orow + d0) = pk;
+            } else {
+              f32x4 v = {oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv, oacc[tb][db][4 * i + 2] * inv,
+                         oacc[tb][db][4 * i + 3] * inv};
+              *(f32x4*)(orow + d0) = v;
+            }
+          }
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// host launchers
+// ===========================================================================
+template <class Tr, int D>
+static hipError_t features_t(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s) {
+  FeatArgs a{x, w, phi, p.L, p.M, p.H, p.Hw};
+  dim3 grid((p.L + 127) / 128, p.BH);
+  hipLaunchKernelGGL((k_features<Tr, D>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s) {
+  if (p.dt == FAVOR_BF16) {
+    switch (p.D) {
+      case 32: return features_t<TrBF16, 32>(p, x, w, phi, s);
+      case 64: return features_t<TrBF16, 64>(p, x, w, phi, s);
+      case 128: return features_t<TrBF16, 128>(p, x, w, phi, s);
+    }
+  } else {
+    switch (p.D) {
+      case 32: return features_t<TrF32, 32>(p, x, w, phi, s);
+      case 64: return features_t<TrF32, 64>(p, x, w, phi, s);
+      case 128: return features_t<TrF32, 128>(p, x, w, phi, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class Tr, int D>
+hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
+                           hipStream_t s) {
+  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len};
+  dim3 grid(p.splits, p.fgroups, p.BH);
+  if constexpr (Tr::VPS == 8 && D <= 64) {
+    if (p.fbw != 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_reduce<Tr, D, 2>), grid, dim3(256), 0, s, a);
+  } else {
+    if (p.fbw != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_reduce<Tr, D, 1>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
+                         hipStream_t s) {
+  if (p.dt == FAVOR_BF16) {
+    switch (p.D) {
+      case 32: return launch_reduce_t<TrBF16, 32>(p, k, v, w, part, partz, s);
+      case 64: return launch_reduce_t<TrBF16, 64>(p, k, v, w, part, partz, s);
+      case 128: return launch_reduce_t<TrBF16, 128>(p, k, v, w, part, partz, s);
+    }
+  } else {
+    switch (p.D) {
+      case 32: return launch_reduce_t<TrF32, 32>(p, k, v, w, part, partz, s);
+      case 64: return launch_reduce_t<TrF32, 64>(p, k, v, w, part, partz, s);
+      case 128: return launch_reduce_t<TrF32, 128>(p, k, v, w, part, partz, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class Tr, int D, int TB>
+static hipError_t apply_t(const Plan& p, const Tensors& t, const void* mstate, const void* zstate, hipStream_t s) {
+  using E = typename Tr::elem;
+  const int gph = (p.L + 4 * TB * 32 - 1) / (4 * TB * 32);
+  const int total = p.BH * gph;
+  ApplyArgs a{t.q, t.w, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch};
+  const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
+  const size_t lds = 2 * (size_t)p.fch * Rows<D, sizeof(E)>::RS + (size_t)p.fch * sizeof(E);
+  hipLaunchKernelGGL((k_apply<Tr, D, TB>), dim3(nblk), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* mstate, const void* zstate,
+                               hipStream_t s) {
+  if (p.dt == FAVOR_BF16) {
+    switch (p.D) {
+      case 32: return apply_t<TrBF16, 32, 2>(p, t, mstate, zstate, s);
+      case 64: return apply_t<TrBF16, 64, 2>(p, t, mstate, zstate, s);
+      case 128: return apply_t<TrBF16, 128, 1>(p, t, mstate, zstate, s);
+    }
+  } else {
+    switch (p.D) {
+      case 32: return apply_t<TrF32, 32, 1>(p, t, mstate, zstate, s);
+      case 64: return apply_t<TrF32, 64, 1>(p, t, mstate, zstate, s);
+      case 128: return apply_t<TrF32, 128, 1>(p, t, mstate, zstate, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
+  float* part = (float*)(t.ws + p.off_part);
+  float* partz = (float*)(t.ws + p.off_partz);
+  void* mstate = t.ws + p.off_mstate;
+  void* zstate = t.ws + p.off_zstate;
+  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
+  if (e != hipSuccess) return e;
+  const int MD = p.M * p.D;
+  dim3 cgrid((MD + p.M + 255) / 256, p.BH);
+  if (p.dt == FAVOR_BF16)
+    hipLaunchKernelGGL((k_combine<bf16>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate, p.splits,
+                       MD, p.M);
+  else
+    hipLaunchKernelGGL((k_combine<float>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
+                       p.splits, MD, p.M);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_apply(p, t, mstate, zstate, s);
+}
+
+}  // namespace favor

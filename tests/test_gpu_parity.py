@@ -1,0 +1,143 @@
+"""GPU parity: the HIP library against the float64 oracle on the same seeded
+inputs and the same W.
+
+Tolerances (stated for the method's float paths): per-row infinity-norm
+relative error <= 1e-4 for float32 inputs and <= 2e-2 for bfloat16 inputs with
+float32 accumulation.  Feature values are checked elementwise against a bound
+derived from the bf16 rounding of W (see test_features_bf16_within_bound).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _util import TOL, row_rel_err, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_attn(favor, x, dtype, causal, eps=1e-6):
+    import torch
+    q, k, v = (to_device(x[n], dtype) for n in ("q", "k", "v"))
+    w = torch.from_numpy(x["w"]).cuda()
+    o = favor.attn(q, k, v, w, causal=causal, eps=eps)
+    torch.cuda.synchronize()
+    return to_f64(o)
+
+
+def _ref(x, causal, eps=1e-6, heads=None):
+    fn = oracle.attn_causal if causal else oracle.attn_noncausal
+    return oracle.per_head(fn, x["q64"], x["k64"], x["v64"], x["w64"], eps=eps)
+
+
+# ---------------------------------------------------------------------------
+# feature map
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,m,L", [(32, 256, 64), (64, 256, 200), (128, 512, 33), (64, 32, 1)])
+def test_features_f32(gpu, d, m, L):
+    import torch
+    x = synth.random_case(100 + d + m, 1, 2, L, d, m, "f32")
+    phi = gpu.features(to_device(x["q"], "f32"), torch.from_numpy(x["w"]).cuda())
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.favor_features(x["q64"][0, h], x["w64"][h]) for h in range(2)])[None]
+    rel = np.abs(to_f64(phi) - ref) / ref
+    assert rel.max() < 1e-4
+
+
+@pytest.mark.parametrize("d,m,L", [(32, 256, 64), (64, 256, 300), (128, 512, 65), (64, 96, 7)])
+def test_features_bf16_within_bound(gpu, d, m, L):
+    """bf16 inputs are converted exactly to the fp16 projection operands; W is
+    scaled by log2(e) and rounded to fp16, so each exponent (base 2) moves by
+    at most 2^-11 * log2(e) * sum_d |x_d w_fd| (one half-ulp per product term)
+    plus float32 rounding; the relative error of phi is bounded by
+    2^that - 1."""
+    import torch
+    x = synth.random_case(200 + d + m, 1, 2, L, d, m, "bf16")
+    phi = to_f64(gpu.features(to_device(x["q"], "bf16"), torch.from_numpy(x["w"]).cuda()))
+    for h in range(2):
+        q = x["q64"][0, h]
+        w = x["w64"][h]
+        ref = oracle.favor_features(q, w)
+        e2 = 2.0 ** -11 * math.log2(math.e) * (np.abs(q) @ np.abs(w).T) + 1e-5 * (1 + np.abs(q @ w.T))
+        bound = np.exp2(e2) - 1 + 1e-6
+        assert np.all(np.abs(phi[0, h] - ref) <= bound * ref)
+
+
+# ---------------------------------------------------------------------------
+# non-causal attention
+# ---------------------------------------------------------------------------
+
+def test_noncausal_worked_example(gpu):
+    """The worked example's shape: n=64, d=32, m=256, float32, W shared."""
+    x = synth.make_inputs(synth.WORKLOADS["t1"])
+    out = _run_attn(gpu, x, "f32", causal=False)
+    assert row_rel_err(out, _ref(x, False)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype,d,m,B,H,L", [
+    ("bf16", 64, 256, 1, 3, 4096),      # encoder shape, 3 heads
+    ("bf16", 64, 256, 2, 2, 1000),      # ragged tail
+    ("bf16", 64, 256, 1, 1, 1),         # one token
+    ("bf16", 64, 32, 1, 2, 333),        # smallest m
+    ("bf16", 64, 512, 1, 2, 777),       # two feature groups
+    ("bf16", 32, 128, 1, 2, 260),
+    ("bf16", 128, 512, 1, 2, 300),
+    ("f32", 32, 256, 1, 2, 500),
+    ("f32", 64, 96, 1, 2, 129),
+    ("f32", 128, 512, 1, 1, 200),
+])
+def test_noncausal_parity(gpu, dtype, d, m, B, H, L):
+    x = synth.random_case(1000 + d + m + L, B, H, L, d, m, dtype)
+    out = _run_attn(gpu, x, dtype, causal=False)
+    assert row_rel_err(out, _ref(x, False)) <= TOL[dtype]
+
+
+def test_noncausal_shared_projection(gpu):
+    x = synth.random_case(7, 2, 3, 300, 64, 256, "bf16", heads_w=1)
+    out = _run_attn(gpu, x, "bf16", causal=False)
+    assert row_rel_err(out, _ref(x, False)) <= TOL["bf16"]
+
+
+def test_noncausal_encoder_full_size_sampled(gpu):
+    """The full encoder workload (B=8, H=12, L=4096, d=64, m=256, bf16) in the
+    launch configuration the benchmark uses; every head is checked on 64
+    sampled rows by the oracle's per-row definition."""
+    wl = synth.WORKLOADS["encoder"]
+    x = synth.make_inputs(wl)
+    out = _run_attn(gpu, x, "bf16", causal=False)
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for b in range(wl.B):
+        for h in range(wl.H):
+            rows = np.sort(rng.choice(wl.L, 64, replace=False))
+            ref = oracle.attn_rows(x["q64"][b, h], x["k64"][b, h], x["v64"][b, h], x["w64"][h], rows)
+            worst = max(worst, row_rel_err(out[b, h, rows], ref))
+    assert worst <= TOL["bf16"]
+
+
+def test_noncausal_deterministic(gpu):
+    import torch
+    x = synth.random_case(9, 1, 4, 2048, 64, 256, "bf16")
+    q, k, v = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    w = torch.from_numpy(x["w"]).cuda()
+    first = gpu.attn(q, k, v, w)
+    for _ in range(5):
+        assert torch.equal(gpu.attn(q, k, v, w), first)
+
+
+def test_noncausal_constant_values(gpu):
+    """V = 1 gives O = den / (den + eps) in every column (eps in the
+    denominator only); with a large eps this is visibly below 1."""
+    import torch
+    x = synth.random_case(11, 1, 2, 100, 64, 128, "f32")
+    q, k = (to_device(x[n], "f32") for n in ("q", "k"))
+    v = torch.ones_like(q)
+    w = torch.from_numpy(x["w"]).cuda()
+    eps = 1000.0
+    out = to_f64(gpu.attn(q, k, v, w, eps=eps))
+    ref = oracle.per_head(oracle.attn_noncausal, x["q64"], x["k64"], np.ones_like(x["v64"]), x["w64"], eps=eps)
+    assert row_rel_err(out, ref) <= TOL["f32"]
+    assert out.max() < 0.9
