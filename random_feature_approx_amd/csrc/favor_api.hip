@@ -41,7 +41,10 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   const int nfb = m / 32;
   p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
   const int target = 2 * num_cus;
-  const int per_head = p.BH * p.fgroups;
+  // non-causal: reduction workgroups = BH * splits * fgroups; causal: the
+  // chunk scan runs one workgroup per (span, head) and walks feature groups
+  // in turn, so spans alone fill the device.
+  const int per_head = causal ? p.BH : p.BH * p.fgroups;
   int splits = (target + per_head - 1) / per_head;
   const int max_splits = (L + 255) / 256;
   if (splits > max_splits) splits = max_splits;
@@ -72,6 +75,12 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   off += align256((size_t)p.BH * m * d * p.esize);
   p.off_zstate = off;
   off += align256((size_t)p.BH * m * p.esize);
+  // causal with several feature groups: float32 partial numerators and
+  // denominators carried from one group to the next
+  p.off_num = off;
+  if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * d * sizeof(float));
+  p.off_den = off;
+  if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * sizeof(float));
   p.total = off;
   return true;
 }

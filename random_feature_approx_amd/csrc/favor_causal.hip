@@ -1,7 +1,415 @@
-// Causal FAVOR+ (placeholder until the chunked scan lands).
+// Causal FAVOR+ on gfx950.
+//
+// o_i = phi(q_i)^T S_i / (phi(q_i)^T z_i + eps), S_i = sum_{j<=i} phi(k_j) v_j^T,
+// z_i = sum_{j<=i} phi(k_j)   (prefix-sum form of the study notes' case 2;
+// the denominator is its analogue of the non-causal normaliser).
+//
+// L is cut into spans (one workgroup each) and spans into chunks of 64 tokens.
+//   1. k_reduce (shared with the non-causal path) computes every span's
+//      aggregate [sum phi(k) v^T | sum phi(k)] in float32.
+//   2. k_span_scan turns the aggregates into exclusive prefixes in place, in
+//      span order (deterministic).
+//   3. k_causal walks the chunks of a span starting from its prefix.  For a
+//      chunk c with queries Q_c, keys K_c and values V_c:
+//        num = tril(phi(Q_c) phi(K_c)^T) V_c + phi(Q_c) S      (masked tile
+//              includes the diagonal)
+//        den = rowsum(tril(phi(Q_c) phi(K_c)^T)) + phi(Q_c) z + eps
+//        S += phi(K_c)^T V_c,  z += phi(K_c)^T 1.
+//      Each wave owns a slice of the features and its slice of S in
+//      accumulator registers; the contributions of the slices are summed
+//      through LDS.  A feature group that does not fit one workgroup is
+//      processed group after group, the partial numerators and denominators
+//      kept in float32 in the workspace.
 #include "favor_device.hpp"
 #include "favor_internal.hpp"
+#include "favor_tiles.hpp"
 
 namespace favor {
-hipError_t launch_causal(const Plan&, const Tensors&, hipStream_t) { return hipErrorNotSupported; }
+
+// ---------------------------------------------------------------------------
+// exclusive prefix of the span aggregates, in place:  a[s] <- sum_{s'<s} a[s']
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, int spans, int MD, int M) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  float* p;
+  int stride;
+  if (idx < MD) {
+    p = part + (size_t)bh * spans * MD + idx;
+    stride = MD;
+  } else if (idx < MD + M) {
+    p = partz + (size_t)bh * spans * M + (idx - MD);
+    stride = M;
+  } else {
+    return;
+  }
+  float run = 0.f;
+  for (int s = 0; s < spans; ++s) {
+    const float t = p[(size_t)s * stride];
+    p[(size_t)s * stride] = run;
+    run += t;
+  }
+}
+
+struct CausalArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* w;
+  void* o;
+  const float* prefix;    // [BH][spans][M][D] exclusive prefixes of S
+  const float* prefixz;   // [BH][spans][M]
+  float* num;             // [BH][L][D] partial numerators (fgroups > 1)
+  float* den;             // [BH][L]
+  int L, M, H, Hw, spans, span_len, fgroups;
+  float eps;
+};
+
+// LDS layout (bytes), computed identically on host and device.
+template <class Tr, int D, int FBW>
+struct CausalLds {
+  using E = typename Tr::elem;
+  static constexpr int C = 64;                                  // tokens per chunk
+  static constexpr int RS = Rows<D, sizeof(E)>::RS;             // Q, K, V rows
+  static constexpr int FW = 32 * FBW;                           // features per wave
+  static constexpr int RSF = FW * (int)sizeof(E) + 16;          // phi(K) rows
+  static constexpr int RSR = (D + 4) * 4;                       // reduction rows (float)
+  static constexpr int kQ = 0, kK = C * RS, kV = 2 * C * RS, kPhi = 3 * C * RS;
+  static constexpr int kStageEnd = kPhi + 4 * C * RSF;
+  static constexpr int kRed = 0, kRedDen = 4 * C * RSR;
+  static constexpr int kRedEnd = kRedDen + 4 * C * 4;
+  static constexpr int kUnion = kStageEnd > kRedEnd ? kStageEnd : kRedEnd;
+  static constexpr int kBq = kUnion, kBk = kBq + C * 4, kZ = kBk + C * 4;
+  static constexpr int kTotal = kZ + 4 * FW * 4;
+};
+
+template <class Tr, int D, int FBW>
+__global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
+  using E = typename Tr::elem;
+  using F = typename Tr::frag;
+  using LY = CausalLds<Tr, D, FBW>;
+  constexpr int C = LY::C;
+  constexpr int NKD = D / Tr::KS;
+  constexpr int NDB = D / 32;
+  constexpr int NKT = 32 / Tr::KS;            // k-steps per 32-token block
+  constexpr int RS = LY::RS, RSF = LY::RSF, RSR = LY::RSR, FW = LY::FW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* sQ = smem + LY::kQ;
+  char* sK = smem + LY::kK;
+  char* sV = smem + LY::kV;
+  float* sBq = (float*)(smem + LY::kBq);
+  float* sBk = (float*)(smem + LY::kBk);
+
+  const int span = blockIdx.x, bh = blockIdx.y;
+  const int head = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  char* sPhi = smem + LY::kPhi + w * C * RSF;          // this wave's phi(K) [token][feature]
+  float* sZ = (float*)(smem + LY::kZ) + w * FW;        // this wave's running z (float)
+  float* sRed = (float*)(smem + LY::kRed);
+  float* sRedDen = (float*)(smem + LY::kRedDen);
+  const int nfb = a.M >> 5;
+  const size_t hoff = (size_t)bh * a.L * D;
+  const E* Qg = (const E*)a.q + hoff;
+  const E* Kg = (const E*)a.k + hoff;
+  const E* Vg = (const E*)a.v + hoff;
+  E* Og = (E*)a.o + hoff;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
+  const float half_ln_m = 0.5f * logf((float)a.M);
+  const int t0 = span * a.span_len;
+  const int t1 = min(a.L, t0 + a.span_len);
+
+  for (int fg = 0; fg < a.fgroups; ++fg) {
+    const int fb0 = (fg * 4 + w) * FBW;
+    F wf[FBW][NKD];
+    f32x16 st[FBW][NDB];
+    float zreg[FBW];
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) {
+      const bool ok = fb0 + i < nfb;
+      const int fbase = (ok ? fb0 + i : 0) * 32;
+      const float* wrow = wh + (size_t)(fbase + l32) * D;
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D>(wrow, hh, s, ok);
+      const float* pre = a.prefix + ((size_t)bh * a.spans + span) * a.M * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st[i][db][r] = ok ? pre[(size_t)(fbase + crow(r, hh)) * D + db * 32 + l32] : 0.f;
+      zreg[i] = ok ? a.prefixz[((size_t)bh * a.spans + span) * a.M + fbase + l32] : 0.f;
+      sZ[i * 32 + l32] = zreg[i];
+    }
+
+    TileLoader<E, D, C, 256> lq, lk, lv;
+    if (t0 < t1) {
+      lq.load(Qg + (size_t)t0 * D, t1 - t0, tid);
+      lk.load(Kg + (size_t)t0 * D, t1 - t0, tid);
+      lv.load(Vg + (size_t)t0 * D, t1 - t0, tid);
+    }
+    for (int c0 = t0; c0 < t1; c0 += C) {
+      const int nv = min(C, t1 - c0);
+      __syncthreads();                                   // previous reduction finished
+      lq.store_proj(sQ, tid);
+      lk.store_proj(sK, tid);
+      lv.store(sV, tid);
+      lq.row_bias(sBq, tid, nv, half_ln_m);
+      lk.row_bias(sBk, tid, nv, half_ln_m);
+      __syncthreads();
+      if (c0 + C < t1) {
+        lq.load(Qg + (size_t)(c0 + C) * D, t1 - c0 - C, tid);
+        lk.load(Kg + (size_t)(c0 + C) * D, t1 - c0 - C, tid);
+        lv.load(Vg + (size_t)(c0 + C) * D, t1 - c0 - C, tid);
+      }
+
+      // ---- feature maps of this wave's features, lane = token -------------
+      F pq[FBW][2][NKT], pk[FBW][2][NKT];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        F qf[NKD], kf[NKD];
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) {
+          qf[s] = row_frag<Tr, D>(sQ + (tb * 32 + l32) * RS, hh, s);
+          kf[s] = row_frag<Tr, D>(sK + (tb * 32 + l32) * RS, hh, s);
+        }
+        const float bq = sBq[tb * 32 + l32], bk = sBk[tb * 32 + l32];
+#pragma unroll
+        for (int i = 0; i < FBW; ++i) {
+          f32x16 aq = zero16(), ak = zero16();
+#pragma unroll
+          for (int s = 0; s < NKD; ++s) {
+            aq = Tr::pmma(wf[i][s], qf[s], aq);          // P^T[f][t]
+            ak = Tr::pmma(wf[i][s], kf[s], ak);
+          }
+          // features past m (a partly filled last group) are exactly zero
+          const bool fvalid = fb0 + i < nfb;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            aq[r] = fvalid ? exp2_fast(aq[r] + bq) : 0.f;
+            ak[r] = fvalid ? exp2_fast(ak[r] + bk) : 0.f;
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            pq[i][tb][s2] = CFrag<Tr>::make(aq, s2);
+            pk[i][tb][s2] = CFrag<Tr>::make(ak, s2);
+          }
+          // phi(K) into this wave's [token][feature] tile (for the state update)
+          char* prow = sPhi + (tb * 32 + l32) * RSF + (i * 32) * (int)sizeof(E);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            if constexpr (Tr::VPS == 8) {
+              u32x2 v2 = {pack_bf16(ak[4 * g], ak[4 * g + 1]), pack_bf16(ak[4 * g + 2], ak[4 * g + 3])};
+              *(u32x2*)(prow + (8 * g + 4 * hh) * 2) = v2;
+            } else {
+              f32x4 v4 = {ak[4 * g], ak[4 * g + 1], ak[4 * g + 2], ak[4 * g + 3]};
+              *(f32x4*)(prow + (8 * g + 4 * hh) * 4) = v4;
+            }
+          }
+        }
+      }
+
+      f32x16 nacc[NDB][2];
+      float dacc[2];
+#pragma unroll
+      for (int tqb = 0; tqb < 2; ++tqb) {
+        dacc[tqb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) nacc[db][tqb] = zero16();
+      }
+
+      // ---- intra-chunk: A^T[tk][tq] = phi(K) phi(Q)^T over this wave's features
+#pragma unroll
+      for (int tqb = 0; tqb < 2; ++tqb) {
+#pragma unroll
+        for (int tkb = 0; tkb <= tqb; ++tkb) {
+          f32x16 at = zero16();
+#pragma unroll
+          for (int i = 0; i < FBW; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < NKT; ++s2) at = Tr::mma(pk[i][tkb][s2], pq[i][tqb][s2], at);
+          if (tkb == tqb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (crow(r, hh) > l32) at[r] = 0.f;        // key after query
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F af = CFrag<Tr>::make(at, s2);              // B operand: lane = tq, k = tk (c-row)
+            if constexpr (Tr::VPS == 8) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) dacc[tqb] = dot2_bf16(af[j], 0x3f803f80u, dacc[tqb]);
+            } else {
+              dacc[tqb] += af;
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              F vf = col_frag<Tr, RS>(sV, tkb * 32, db * 32, s2, lane);   // V^T[d][tk]
+              nacc[db][tqb] = Tr::mma(vf, af, nacc[db][tqb]);
+            }
+          }
+        }
+      }
+
+      // ---- inter-chunk: phi(Q) S and phi(Q) z with the state before this chunk
+#pragma unroll
+      for (int i = 0; i < FBW; ++i) {
+        float zf[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 z4 = *(const f32x4*)(sZ + i * 32 + 8 * g + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) zf[4 * g + j] = z4[j];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < NKT; ++s2) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            F sf = CFrag<Tr>::make(st[i][db], s2);           // S^T[d][f] operand
+#pragma unroll
+            for (int tqb = 0; tqb < 2; ++tqb) nacc[db][tqb] = Tr::mma(sf, pq[i][tqb][s2], nacc[db][tqb]);
+          }
+#pragma unroll
+          for (int tqb = 0; tqb < 2; ++tqb) {
+            if constexpr (Tr::VPS == 8) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const unsigned zz = pack_bf16(zf[8 * s2 + 2 * k], zf[8 * s2 + 2 * k + 1]);
+                dacc[tqb] = dot2_bf16(pq[i][tqb][s2][k], zz, dacc[tqb]);
+              }
+            } else {
+              dacc[tqb] = fmaf(pq[i][tqb][s2], zf[s2], dacc[tqb]);
+            }
+          }
+        }
+      }
+
+      // ---- state update: S += phi(K)^T V, z += phi(K)^T 1 ------------------
+#pragma unroll
+      for (int i = 0; i < FBW; ++i) {
+        float zc = 0.f;
+#pragma unroll
+        for (int tkb = 0; tkb < 2; ++tkb)
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F kt = col_frag<Tr, RSF>(sPhi, tkb * 32, i * 32, s2, lane);    // phi(K)^T[f][t]
+            if constexpr (Tr::VPS == 8) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) zc = dot2_bf16(kt[j], 0x3f803f80u, zc);
+            } else {
+              zc += kt;
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              F vf = col_frag<Tr, RS>(sV, tkb * 32, db * 32, s2, lane);
+              st[i][db] = Tr::mma(kt, vf, st[i][db]);
+            }
+          }
+        zc += __shfl_xor(zc, 32);
+        zreg[i] += zc;
+      }
+      // publish z for the next chunk (wave-private; read after this wave's
+      // next feature maps, so LDS order within the wave suffices)
+#pragma unroll
+      for (int i = 0; i < FBW; ++i)
+        if (hh == 0) sZ[i * 32 + l32] = zreg[i];
+
+      // ---- sum the four waves' contributions -------------------------------
+      __syncthreads();                                   // staging area is free
+#pragma unroll
+      for (int tqb = 0; tqb < 2; ++tqb) {
+        float* rrow = sRed + (size_t)w * C * (RSR / 4) + (tqb * 32 + l32) * (RSR / 4);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v4 = {nacc[db][tqb][4 * g], nacc[db][tqb][4 * g + 1], nacc[db][tqb][4 * g + 2],
+                        nacc[db][tqb][4 * g + 3]};
+            *(f32x4*)(rrow + db * 32 + 8 * g + 4 * hh) = v4;
+          }
+        const float dsum = dacc[tqb] + __shfl_xor(dacc[tqb], 32);
+        if (hh == 0) sRedDen[w * C + tqb * 32 + l32] = dsum;
+      }
+      __syncthreads();
+      {
+        constexpr int DP = D / 4;                        // outputs per thread
+        const int tq = tid >> 2, d0 = (tid & 3) * DP;
+        float acc[DP];
+#pragma unroll
+        for (int j = 0; j < DP; ++j) acc[j] = 0.f;
+        float dsum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float* rrow = sRed + (size_t)ww * C * (RSR / 4) + tq * (RSR / 4) + d0;
+#pragma unroll
+          for (int j = 0; j < DP; j += 4) {
+            f32x4 v4 = *(const f32x4*)(rrow + j);
+            acc[j] += v4[0];
+            acc[j + 1] += v4[1];
+            acc[j + 2] += v4[2];
+            acc[j + 3] += v4[3];
+          }
+          dsum += sRedDen[ww * C + tq];
+        }
+        const int tok = c0 + tq;
+        if (tq < nv) {
+          const size_t oi = (size_t)tok * D + d0;
+          if (a.fgroups > 1) {
+            if (fg > 0) {
+#pragma unroll
+              for (int j = 0; j < DP; ++j) acc[j] += a.num[hoff + oi + j];
+              dsum += a.den[(size_t)bh * a.L + tok];
+            }
+            if (fg + 1 < a.fgroups) {
+#pragma unroll
+              for (int j = 0; j < DP; ++j) a.num[hoff + oi + j] = acc[j];
+              if ((tid & 3) == 0) a.den[(size_t)bh * a.L + tok] = dsum;
+            }
+          }
+          if (fg + 1 == a.fgroups) {
+            const float inv = 1.0f / (dsum + a.eps);
+#pragma unroll
+            for (int j = 0; j < DP; ++j) Og[oi + j] = (E)(acc[j] * inv);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class Tr, int D, int FBW>
+static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
+  using LY = CausalLds<Tr, D, FBW>;
+  float* part = (float*)(t.ws + p.off_part);
+  float* partz = (float*)(t.ws + p.off_partz);
+  CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
+               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps};
+  hipLaunchKernelGGL((k_causal<Tr, D, FBW>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
+  float* part = (float*)(t.ws + p.off_part);
+  float* partz = (float*)(t.ws + p.off_partz);
+  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
+  if (e != hipSuccess) return e;
+  const int MD = p.M * p.D;
+  hipLaunchKernelGGL(k_span_scan, dim3((MD + p.M + 255) / 256, p.BH), dim3(256), 0, s, part, partz, p.splits, MD,
+                     p.M);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.dt == FAVOR_BF16) {
+    switch (p.D) {
+      case 32: return causal_t<TrBF16, 32, 2>(p, t, s);
+      case 64: return causal_t<TrBF16, 64, 2>(p, t, s);
+      case 128: return causal_t<TrBF16, 128, 1>(p, t, s);
+    }
+  } else {
+    switch (p.D) {
+      case 32: return causal_t<TrF32, 32, 1>(p, t, s);
+      case 64: return causal_t<TrF32, 64, 1>(p, t, s);
+      case 128: return causal_t<TrF32, 128, 1>(p, t, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace favor

@@ -27,7 +27,7 @@ struct Plan {
   int apply_steps;      // 4-tile steps per workgroup
   int fch;              // features per LDS chunk
   // workspace offsets (bytes)
-  size_t off_part, off_partz, off_mstate, off_zstate, total;
+  size_t off_part, off_partz, off_mstate, off_zstate, off_num, off_den, total;
 };
 
 bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus);
@@ -46,5 +46,7 @@ struct Tensors {
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
+                         hipStream_t s);
 
 }  // namespace favor

@@ -141,3 +141,66 @@ def test_noncausal_constant_values(gpu):
     ref = oracle.per_head(oracle.attn_noncausal, x["q64"], x["k64"], np.ones_like(x["v64"]), x["w64"], eps=eps)
     assert row_rel_err(out, ref) <= TOL["f32"]
     assert out.max() < 0.9
+
+
+# ---------------------------------------------------------------------------
+# causal attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d,m,B,H,L", [
+    ("bf16", 64, 256, 1, 2, 64),        # one chunk
+    ("bf16", 64, 256, 1, 2, 100),       # ragged second chunk
+    ("bf16", 64, 256, 1, 2, 1000),      # several spans and chunks
+    ("bf16", 64, 256, 1, 1, 1),         # one token
+    ("bf16", 64, 32, 2, 1, 300),        # smallest m
+    ("bf16", 32, 128, 1, 2, 333),
+    ("bf16", 128, 512, 1, 1, 257),      # several feature groups
+    ("f32", 32, 256, 1, 1, 200),        # two feature groups
+    ("f32", 64, 96, 1, 2, 130),
+    ("f32", 128, 512, 1, 1, 300),       # wide-feature shape, four feature groups
+])
+def test_causal_parity(gpu, dtype, d, m, B, H, L):
+    x = synth.random_case(3000 + d + m + L, B, H, L, d, m, dtype)
+    out = _run_attn(gpu, x, dtype, causal=True)
+    assert row_rel_err(out, _ref(x, True)) <= TOL[dtype]
+
+
+def test_causal_last_row_matches_noncausal(gpu):
+    x = synth.random_case(13, 1, 2, 777, 64, 256, "f32")
+    c = _run_attn(gpu, x, "f32", causal=True)
+    n = _run_attn(gpu, x, "f32", causal=False)
+    assert row_rel_err(c[:, :, -1], n[:, :, -1]) <= TOL["f32"]
+
+
+def test_causal_first_row_is_first_value(gpu):
+    """Row 0 sees only key 0: o_0 = v_0 * a / (a + eps)."""
+    x = synth.random_case(14, 1, 2, 128, 32, 64, "f32")
+    out = _run_attn(gpu, x, "f32", causal=True)
+    for h in range(2):
+        a = oracle.favor_features(x["q64"][0, h, :1], x["w64"][h])[0] @ \
+            oracle.favor_features(x["k64"][0, h, :1], x["w64"][h])[0]
+        np.testing.assert_allclose(out[0, h, 0], x["v64"][0, h, 0] * a / (a + 1e-6), rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["causal_lm", "long"])
+def test_causal_full_size_sampled(gpu, name):
+    """Full causal workloads in the benchmark's launch configuration; every
+    head is checked on sampled rows (first, last, span/chunk edges, random)
+    by the oracle's per-row definition."""
+    wl = synth.WORKLOADS[name]
+    x = synth.make_inputs(wl, with64=False)
+    import torch
+    q, k, v = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    o = gpu.attn(q, k, v, torch.from_numpy(x["w"]).cuda(), causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    fixed = np.array([0, 1, 63, 64, 65, 1023, 1024, 2047, 2048, wl.L - 1])
+    worst = 0.0
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    for b, h in heads[:: max(1, len(heads) // 8)]:
+        rows = np.unique(np.concatenate([fixed[fixed < wl.L], rng.choice(wl.L, 12, replace=False)]))
+        q64, k64, v64 = (synth.as_f64(x[n][b, h], "bf16") for n in ("q", "k", "v"))
+        ref = oracle.attn_rows(q64, k64, v64, x["w64"][h], rows, causal=True)
+        got = o[b, h, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+        worst = max(worst, row_rel_err(got, ref))
+    assert worst <= TOL["bf16"]
