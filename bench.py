@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""FAVOR+ forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+
+A step is one pass of the whole hot path over one batch of seeded synthetic
+input already resident in HBM: for the default workload ("long": B=1, H=8,
+L=65536, d=64, m=256, bf16) the non-causal forward and the causal forward of
+the same Q, K, V.  `value` is B*H*L / step time, i.e. tokens per second
+through both forward variants.  Prints one JSON line on stdout; progress goes
+to stderr.
+
+The JSON line also carries
+  * "roofline": the dominant kernel's algorithmic bytes (or flops) per launch
+    divided by its average launch duration, timed live with HIP events that
+    the library records on the launch stream during the timed steps;
+  * "cpu_baseline": the float64 NumPy oracle timed on the host cores on a
+    bounded sample of the same workload (a reported baseline, not a target);
+  * "paths" and "kernels": per-path and per-kernel timings.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FAVOR+ fwd tokens/sec (B·H·L/s) causal & non-causal; % of MFMA/HBM roofline"
+PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E, GB/s
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks
+KERNEL_SOURCES = ["favor_device.hpp", "favor_tiles.hpp", "favor_nc.hip", "favor_causal.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "random_feature_approx_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(kernel: str, path: str, wl) -> dict:
+    """Algorithmic work of one launch: bytes the method must move and flops it
+    must do for the tokens that launch processes (per token: the non-causal
+    K side and Q side each move 2*d*s bytes and do 4*m*d flops; the causal
+    scan moves Q, K, V, O (4*d*s) and does 8*m*d)."""
+    T = wl.tokens
+    s = 2 if wl.dtype == "bf16" else 4
+    d, m = wl.d, wl.m
+    if kernel == "k_causal":
+        return {"bytes": 4 * d * s * T, "flops": 8 * m * d * T}
+    if kernel in ("k_reduce", "k_apply"):
+        return {"bytes": 2 * d * s * T, "flops": 4 * m * d * T}
+    if kernel in ("k_combine", "k_span_scan"):
+        return {"bytes": 0, "flops": 0}
+    return {"bytes": 0, "flops": 0}
+
+
+def roofline_entry(kernel: str, path: str, wl, avg_ms: float, traffic) -> dict:
+    a = algorithmic(kernel, path, wl)
+    t = avg_ms * 1e-3
+    peak_mfma = PEAK_MFMA_TFLOPS[wl.dtype]
+    intensity = a["flops"] / a["bytes"] if a["bytes"] else float("inf")
+    ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if intensity <= ridge:
+        achieved = a["bytes"] / t / 1e9
+        entry = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = a["flops"] / t / 1e12
+        entry = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                 "frac": round(achieved / peak_mfma, 4)}
+    entry["traffic"] = traffic
+    entry["kernel"] = kernel
+    entry["path"] = path
+    entry["avg_launch_ms"] = round(avg_ms, 5)
+    entry["alg_bytes_per_launch"] = a["bytes"]
+    entry["alg_flops_per_launch"] = a["flops"]
+    entry["mfma_frac_alg"] = round(a["flops"] / t / 1e12 / peak_mfma, 4)
+    entry["hbm_frac_alg"] = round(a["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
+    return entry
+
+
+def stored_traffic(kernel: str, path: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters (scaled by a
+    plain copy kernel), valid only while the kernel sources are unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    e = rec.get("kernels", {}).get(f"{workload}/{path}/{kernel}")
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, x, seconds: float) -> dict:
+    """Time the float64 oracle on whole heads of the workload until about
+    `seconds` per path have elapsed; report tokens/s for a full step (every
+    path over the same tokens)."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    per_token_s = {}
+    sample = []
+    for path in wl.paths:
+        fn = oracle.attn_causal if path == "causal" else oracle.attn_noncausal
+        done, elapsed = 0, 0.0
+        for b, h in heads:
+            q, k, v = (synth.as_f64(x[n][b, h], wl.dtype) for n in ("q", "k", "v"))
+            w = x["w"][h if x["w"].shape[0] > 1 else 0].astype(np.float64)
+            t0 = time.perf_counter()
+            fn(q, k, v, w, eps=wl.eps)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if elapsed >= seconds:
+                break
+        per_token_s[path] = elapsed / (done * wl.L)
+        sample.append(f"{path}: {done} of {len(heads)} heads ({done * wl.L} tokens, {elapsed:.1f} s)")
+        log(f"cpu oracle {path}: {done} heads in {elapsed:.1f} s")
+    value = 1.0 / sum(per_token_s.values())
+    return {"value": round(value, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "float64 NumPy oracle on whole heads of the same workload; " + "; ".join(sample)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long", choices=["t1", "encoder", "causal_lm", "long", "wide"])
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time budget per path (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is described "
+              "in DESIGN.md and not run here", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py is a single-process benchmark; do not launch it with several ranks", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import random_feature_approx_amd as favor
+    import synth
+
+    favor.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.WORKLOADS[args.workload]
+    log(f"workload {wl.name}: B={wl.B} H={wl.H} L={wl.L} d={wl.d} m={wl.m} {wl.dtype} paths={wl.paths}")
+    x = synth.make_inputs(wl, with64=False)
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    w = torch.from_numpy(x["w"]).to(dev)
+    outs = {p: torch.empty_like(q) for p in wl.paths}
+    wss = {}
+    for p in wl.paths:
+        nbytes = favor.workspace_bytes(wl.B, wl.H, wl.L, wl.d, wl.m, p == "causal",
+                                       favor.BF16 if wl.dtype == "bf16" else favor.F32)
+        wss[p] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def run(path):
+        favor.attn(q, k, v, w, causal=(path == "causal"), eps=wl.eps, out=outs[path], workspace=wss[path])
+
+    for _ in range(args.warmup):
+        for p in wl.paths:
+            run(p)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    K = args.steps
+    kernels = list(favor.KERNELS)
+    for kname in kernels:
+        favor.timing_start(kname, 2 * K + 4)
+    ev = {p: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for p in wl.paths}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        for p in wl.paths:
+            ev[p][i][0].record()
+            run(p)
+            ev[p][i][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / K
+    log(f"timed {K} steps: {ms_step:.4f} ms/step")
+
+    path_ms = {p: sum(a.elapsed_time(b) for a, b in ev[p]) / K for p in wl.paths}
+    # per-kernel launch durations; a kernel used by both paths alternates in
+    # launch order (non-causal first within a step)
+    per_kernel = {}
+    for kname in kernels:
+        durs = favor.timing_stop(kname, 2 * K + 4)
+        if not durs:
+            continue
+        users = [p for p in wl.paths if kname in ("k_reduce",) or
+                 (kname in ("k_combine", "k_apply") and p == "noncausal") or
+                 (kname in ("k_span_scan", "k_causal") and p == "causal")]
+        for j, p in enumerate(users):
+            mine = durs[j::len(users)]
+            per_kernel[f"{p}/{kname}"] = {"avg_ms": sum(mine) / len(mine), "launches": len(mine)}
+    dom_key = max(per_kernel, key=lambda k: per_kernel[k]["avg_ms"])
+    dom_path, dom_kernel = dom_key.split("/")
+    roof = roofline_entry(dom_kernel, dom_path, wl, per_kernel[dom_key]["avg_ms"],
+                          stored_traffic(dom_kernel, dom_path, wl.name))
+    kern_report = {}
+    for key, val in per_kernel.items():
+        p, kn = key.split("/")
+        r = roofline_entry(kn, p, wl, val["avg_ms"], None) if algorithmic(kn, p, wl)["bytes"] else {}
+        kern_report[key] = {"avg_ms": round(val["avg_ms"], 5), "launches": val["launches"],
+                            "hbm_frac_alg": r.get("hbm_frac_alg"), "mfma_frac_alg": r.get("mfma_frac_alg")}
+
+    tokens = wl.tokens
+    value = tokens / (ms_step * 1e-3)
+    paths_report = {p: {"ms": round(path_ms[p], 5), "tokens_per_s": round(tokens / (path_ms[p] * 1e-3), 1)}
+                    for p in wl.paths}
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, x, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, Q and K scaled as the workload states; orthogonal random W)",
+        "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} L={wl.L} d={wl.d} m={wl.m} {wl.dtype}, "
+                               f"{' + '.join(wl.paths)} per step",
+                   "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d, "m": wl.m, "paths": list(wl.paths),
+                   "chunk": wl.chunk, "eps": wl.eps},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "paths": paths_report,
+        "kernels": kern_report,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -19,9 +19,13 @@
  *    projection shared by all heads) or Hw = H (one per head).  W is used as
  *    given: the library samples nothing and applies no 1/sqrt(d) temperature;
  *    a caller who wants one pre-scales Q and K.
- *  - dtype FAVOR_BF16: Q, K, V, X and O are bfloat16; W is rounded to bf16
- *    (round to nearest even) for the matrix cores; features, states and sums
- *    are accumulated in float32.  FAVOR_F32: everything is float32.
+ *  - dtype FAVOR_BF16: Q, K, V, X and O are bfloat16.  The projection x W^T
+ *    runs on fp16 matrix-core operands: x is converted exactly (|x| must stay
+ *    below 65504; magnitudes under 2^-14 keep an absolute error below
+ *    2^-25) and W log2(e) is rounded to fp16 (nearest even).  Features phi
+ *    and the m x d states enter the other products as bf16 (nearest even);
+ *    every product accumulates in float32, and states and sums are float32.
+ *    FAVOR_F32: everything is float32.
  *  - Supported shapes: d in {32, 64, 128}; m a multiple of 32 with
  *    32 <= m <= 512; L >= 1; B, H >= 1; B*H*L*max(d,m) < 2^31.
  *  - stream is a hipStream_t passed as void* (NULL = default stream).  Calls
@@ -113,6 +117,31 @@ favor_status favor_attn(const void* Q, const void* K, const void* V,
                         const float* W, int Hw, void* O,
                         int B, int H, int L, int d, int m, float eps, int causal,
                         favor_dtype dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing (for benchmarks and profiling; host-side only, allocates no
+ * device memory).  favor_timing_start(k, capacity) creates `capacity` pairs
+ * of HIP timing events; every later launch of kernel k by this library
+ * records one pair around itself on the launch's own stream, until the pool
+ * is used up.  favor_timing_stop(k, ms, max, &n) waits for the recorded
+ * events, writes the duration of each timed launch in milliseconds to
+ * ms[0..min(n, max)-1] in launch order, sets n to the number of timed
+ * launches, and destroys the events.  Not thread-safe: use from one host
+ * thread while no other thread calls the library.
+ */
+typedef enum {
+  FAVOR_KERNEL_FEATURES = 0,   /* fused feature map (favor_features)            */
+  FAVOR_KERNEL_REDUCE = 1,     /* K-side state reduction / causal span totals    */
+  FAVOR_KERNEL_COMBINE = 2,    /* non-causal fixed-order combine of the partials */
+  FAVOR_KERNEL_APPLY = 3,      /* non-causal Q-side apply                         */
+  FAVOR_KERNEL_SPAN_SCAN = 4,  /* causal exclusive prefix over spans              */
+  FAVOR_KERNEL_CAUSAL = 5,     /* causal chunked scan                             */
+  FAVOR_KERNEL_COUNT = 6
+} favor_kernel;
+
+favor_status favor_timing_start(favor_kernel k, int capacity);
+favor_status favor_timing_stop(favor_kernel k, double* ms, int max_launches, int* launches);
+const char* favor_kernel_name(favor_kernel k);
 
 #ifdef __cplusplus
 }

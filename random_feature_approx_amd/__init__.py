@@ -20,7 +20,7 @@ import ctypes
 import os
 
 __all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal",
-           "workspace_bytes", "FavorError", "STATUS"]
+           "workspace_bytes", "FavorError", "STATUS", "KERNELS", "timing_start", "timing_stop"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBNAME = "libfavor.so"
@@ -29,6 +29,7 @@ _lib = None
 STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid shape", 3: "unsupported d, m or dtype",
           4: "workspace missing or too small", 5: "HIP runtime error", 6: "internal error"}
 F32, BF16 = 0, 1
+KERNELS = {"k_features": 0, "k_reduce": 1, "k_combine": 2, "k_apply": 3, "k_span_scan": 4, "k_causal": 5}
 
 
 class FavorError(RuntimeError):
@@ -66,6 +67,12 @@ def load():
         getattr(lib, name).argtypes = attn_args
     lib.favor_attn.restype = i
     lib.favor_attn.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.favor_timing_start.restype = i
+    lib.favor_timing_start.argtypes = [i, i]
+    lib.favor_timing_stop.restype = i
+    lib.favor_timing_stop.argtypes = [i, ctypes.POINTER(ctypes.c_double), i, ctypes.POINTER(i)]
+    lib.favor_kernel_name.restype = ctypes.c_char_p
+    lib.favor_kernel_name.argtypes = [i]
     if lib.favor_abi_version() != 1:
         raise RuntimeError("libfavor.so has an unexpected ABI version")
     _lib = lib
@@ -168,3 +175,21 @@ def attn_noncausal(q, k, v, w, eps: float = 1e-6, **kw):
 
 def attn_causal(q, k, v, w, eps: float = 1e-6, **kw):
     return attn(q, k, v, w, causal=True, eps=eps, **kw)
+
+
+def timing_start(kernel: str, capacity: int) -> None:
+    """Time the next `capacity` launches of a kernel with HIP events recorded
+    by the library on the launch's own stream."""
+    st = load().favor_timing_start(KERNELS[kernel], int(capacity))
+    if st != 0:
+        raise FavorError("favor_timing_start", st)
+
+
+def timing_stop(kernel: str, capacity: int = 4096):
+    """Per-launch durations (ms) recorded since timing_start, in launch order."""
+    buf = (ctypes.c_double * capacity)()
+    n = ctypes.c_int(0)
+    st = load().favor_timing_stop(KERNELS[kernel], buf, capacity, ctypes.byref(n))
+    if st != 0:
+        raise FavorError("favor_timing_stop", st)
+    return [buf[i] for i in range(min(n.value, capacity))]

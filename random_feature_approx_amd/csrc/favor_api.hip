@@ -85,6 +85,35 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+namespace {
+struct Timer {
+  hipEvent_t* ev = nullptr;   // 2 * cap events
+  int cap = 0, used = 0;
+  bool open = false;          // a begin is waiting for its end
+};
+Timer g_timers[FAVOR_KERNEL_COUNT];
+}  // namespace
+
+void timing_begin(favor_kernel k, hipStream_t s) {
+  Timer& t = g_timers[k];
+  if (t.ev && t.used < t.cap) {
+    hipEventRecord(t.ev[2 * t.used], s);
+    t.open = true;
+  }
+}
+
+void timing_end(favor_kernel k, hipStream_t s) {
+  Timer& t = g_timers[k];
+  if (t.open) {
+    hipEventRecord(t.ev[2 * t.used + 1], s);
+    ++t.used;
+    t.open = false;
+  }
+}
+
 }  // namespace favor
 
 using namespace favor;
@@ -147,6 +176,62 @@ favor_status favor_attn_causal(const void* Q, const void* K, const void* V, cons
                                int H, int L, int d, int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes,
                                void* stream) {
   return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, 1, dtype, ws, ws_bytes, stream);
+}
+
+static void timer_free(Timer& t) {
+  if (t.ev) {
+    for (int i = 0; i < 2 * t.cap; ++i) hipEventDestroy(t.ev[i]);
+    delete[] t.ev;
+  }
+  t = Timer();
+}
+
+favor_status favor_timing_start(favor_kernel k, int capacity) {
+  if ((int)k < 0 || k >= FAVOR_KERNEL_COUNT || capacity < 1) return FAVOR_ERR_SHAPE;
+  Timer& t = g_timers[k];
+  timer_free(t);
+  t.ev = new hipEvent_t[2 * (size_t)capacity];
+  for (int i = 0; i < 2 * capacity; ++i) {
+    if (hipEventCreate(&t.ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(t.ev[j]);
+      delete[] t.ev;
+      t = Timer();
+      return FAVOR_ERR_HIP;
+    }
+  }
+  t.cap = capacity;
+  return FAVOR_OK;
+}
+
+favor_status favor_timing_stop(favor_kernel k, double* ms, int max_launches, int* launches) {
+  if ((int)k < 0 || k >= FAVOR_KERNEL_COUNT) return FAVOR_ERR_SHAPE;
+  if (!launches || (max_launches > 0 && !ms)) return FAVOR_ERR_NULL;
+  Timer& t = g_timers[k];
+  favor_status st = FAVOR_OK;
+  for (int i = 0; i < t.used; ++i) {
+    float e = 0.f;
+    if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&e, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) {
+      st = FAVOR_ERR_HIP;
+      break;
+    }
+    if (i < max_launches) ms[i] = e;
+  }
+  *launches = t.used;
+  timer_free(t);
+  return st;
+}
+
+const char* favor_kernel_name(favor_kernel k) {
+  switch (k) {
+    case FAVOR_KERNEL_FEATURES: return "k_features";
+    case FAVOR_KERNEL_REDUCE: return "k_reduce";
+    case FAVOR_KERNEL_COMBINE: return "k_combine";
+    case FAVOR_KERNEL_APPLY: return "k_apply";
+    case FAVOR_KERNEL_SPAN_SCAN: return "k_span_scan";
+    case FAVOR_KERNEL_CAUSAL: return "k_causal";
+    default: return "unknown";
+  }
 }
 
 favor_status favor_attn(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B, int H,

@@ -382,7 +382,9 @@ static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
   float* partz = (float*)(t.ws + p.off_partz);
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
                p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps};
+  timing_begin(FAVOR_KERNEL_CAUSAL, s);
   hipLaunchKernelGGL((k_causal<Tr, D, FBW>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
+  timing_end(FAVOR_KERNEL_CAUSAL, s);
   return hipGetLastError();
 }
 
@@ -392,8 +394,10 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
   if (e != hipSuccess) return e;
   const int MD = p.M * p.D;
+  timing_begin(FAVOR_KERNEL_SPAN_SCAN, s);
   hipLaunchKernelGGL(k_span_scan, dim3((MD + p.M + 255) / 256, p.BH), dim3(256), 0, s, part, partz, p.splits, MD,
                      p.M);
+  timing_end(FAVOR_KERNEL_SPAN_SCAN, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dt == FAVOR_BF16) {

@@ -43,6 +43,11 @@ struct Tensors {
   char* ws;
 };
 
+// Kernel timing hooks (see favor_timing_start): record the next free event
+// pair of kernel k around a launch on stream s.
+void timing_begin(favor_kernel k, hipStream_t s);
+void timing_end(favor_kernel k, hipStream_t s);
+
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);

@@ -431,7 +431,9 @@ template <class Tr, int D>
 static hipError_t features_t(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s) {
   FeatArgs a{x, w, phi, p.L, p.M, p.H, p.Hw};
   dim3 grid((p.L + 127) / 128, p.BH);
+  timing_begin(FAVOR_KERNEL_FEATURES, s);
   hipLaunchKernelGGL((k_features<Tr, D>), grid, dim3(256), 0, s, a);
+  timing_end(FAVOR_KERNEL_FEATURES, s);
   return hipGetLastError();
 }
 
@@ -459,11 +461,14 @@ hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const fl
   dim3 grid(p.splits, p.fgroups, p.BH);
   if constexpr (Tr::VPS == 8 && D <= 64) {
     if (p.fbw != 2) return hipErrorInvalidValue;
+    timing_begin(FAVOR_KERNEL_REDUCE, s);
     hipLaunchKernelGGL((k_reduce<Tr, D, 2>), grid, dim3(256), 0, s, a);
   } else {
     if (p.fbw != 1) return hipErrorInvalidValue;
+    timing_begin(FAVOR_KERNEL_REDUCE, s);
     hipLaunchKernelGGL((k_reduce<Tr, D, 1>), grid, dim3(256), 0, s, a);
   }
+  timing_end(FAVOR_KERNEL_REDUCE, s);
   return hipGetLastError();
 }
 
@@ -493,7 +498,9 @@ static hipError_t apply_t(const Plan& p, const Tensors& t, const void* mstate, c
   ApplyArgs a{t.q, t.w, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
   const size_t lds = 2 * (size_t)p.fch * Rows<D, sizeof(E)>::RS + (size_t)p.fch * sizeof(E);
+  timing_begin(FAVOR_KERNEL_APPLY, s);
   hipLaunchKernelGGL((k_apply<Tr, D, TB>), dim3(nblk), dim3(256), lds, s, a);
+  timing_end(FAVOR_KERNEL_APPLY, s);
   return hipGetLastError();
 }
 
@@ -524,12 +531,14 @@ hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int MD = p.M * p.D;
   dim3 cgrid((MD + p.M + 255) / 256, p.BH);
+  timing_begin(FAVOR_KERNEL_COMBINE, s);
   if (p.dt == FAVOR_BF16)
     hipLaunchKernelGGL((k_combine<bf16>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate, p.splits,
                        MD, p.M);
   else
     hipLaunchKernelGGL((k_combine<float>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
                        p.splits, MD, p.M);
+  timing_end(FAVOR_KERNEL_COMBINE, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_apply(p, t, mstate, zstate, s);
