@@ -1,0 +1,95 @@
+"""The C ABI: the built library loads, exports every function include/favor.h
+declares, and rejects bad arguments before touching a device (these calls
+launch nothing, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "favor.h")
+
+
+def _lib():
+    import random_feature_approx_amd as favor
+    if not os.path.exists(favor.library_path()):
+        pytest.fail("libfavor.so is not built (run __graft_entry__.build())")
+    return favor.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(favor_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for must in ("favor_features", "favor_attn_noncausal", "favor_attn_causal", "favor_attn",
+                 "favor_workspace_bytes", "favor_status_string", "favor_abi_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.favor_abi_version() == 1
+    for code in range(7):
+        assert lib.favor_status_string(code)
+    assert lib.favor_status_string(99) == b"unknown status"
+
+
+NULL = None
+
+
+def _nc(lib, q=1, k=1, v=1, w=1, hw=1, o=1, B=1, H=1, L=16, d=64, m=256, eps=1e-6, dt=1, ws=None, nbytes=0):
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.favor_attn_noncausal(p(q), p(k), p(v), p(w), hw, p(o), B, H, L, d, m, eps, dt, p(ws), nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(w=0), 1), (dict(o=0), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(L=0), 2), (dict(hw=3, H=2), 2), (dict(B=1 << 14, H=1 << 14, L=64), 2),
+    (dict(d=48), 3), (dict(d=256), 3), (dict(m=48), 3), (dict(m=16), 3), (dict(m=544), 3), (dict(dt=7), 3),
+])
+def test_validation_errors(kw, code):
+    assert _nc(_lib(), **kw) == code
+
+
+def test_causal_and_dispatcher_validate_the_same_way():
+    lib = _lib()
+    assert lib.favor_attn_causal(None, None, None, None, 1, None, 1, 1, 16, 64, 256, 1e-6, 1, None, 0, None) == 1
+    assert lib.favor_attn(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 1,
+                          ctypes.c_void_p(1), 1, 1, 16, 60, 256, 1e-6, 1, 1, None, 0, None) == 3
+    assert lib.favor_features(None, None, 1, None, 1, 1, 16, 64, 256, 1, None) == 1
+    assert lib.favor_features(ctypes.c_void_p(1), ctypes.c_void_p(1), 1, ctypes.c_void_p(1),
+                              1, 1, 16, 64, 100, 1, None) == 3
+
+
+def test_workspace_bytes_rejects_bad_shapes():
+    lib = _lib()
+    assert lib.favor_workspace_bytes(0, 1, 16, 64, 256, 0, 1) == 0
+    assert lib.favor_workspace_bytes(1, 1, 16, 64, 100, 1, 1) == 0
+
+
+def test_timing_api_argument_checks():
+    lib = _lib()
+    assert lib.favor_timing_start(99, 4) == 2
+    assert lib.favor_timing_start(0, 0) == 2
+    n = ctypes.c_int(-1)
+    assert lib.favor_timing_stop(0, None, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.favor_kernel_name(5) == b"k_causal"
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import random_feature_approx_amd as favor
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        favor.attn(x, x, x, torch.zeros(256, 64))
