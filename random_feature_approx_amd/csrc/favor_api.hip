@@ -40,11 +40,13 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.fbw = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
   const int nfb = m / 32;
   p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
+  p.rnw = (dt == FAVOR_F32 && d == 128) ? 4 : 8;
+  p.rfgroups = (nfb + p.rnw - 1) / p.rnw;
   const int target = 2 * num_cus;
-  // non-causal: reduction workgroups = BH * splits * fgroups; causal: the
+  // non-causal: reduction workgroups = BH * splits * rfgroups; causal: the
   // chunk scan runs one workgroup per (span, head) and walks feature groups
   // in turn, so spans alone fill the device.
-  const int per_head = causal ? p.BH : p.BH * p.fgroups;
+  const int per_head = causal ? p.BH : p.BH * p.rfgroups;
   int splits = (target + per_head - 1) / per_head;
   const int max_splits = (L + 255) / 256;
   if (splits > max_splits) splits = max_splits;

@@ -85,6 +85,76 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Batches of the same transposed read issued from inline assembly.  The
+// compiler cannot prove that the builtin does not read LDS that an
+// outstanding global->LDS copy is filling, and waits for every copy
+// (vmcnt(0)) before it.  Each batch below is a single statement that issues
+// its reads and then waits for them (lgkmcnt(0)), so no result can be used,
+// moved or copied before its data has arrived; the caller orders the reads
+// after the copies it depends on.
+__device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(uintptr_t)LDS_PTR(const char, p); }
+
+__device__ __forceinline__ void lds_read_tr16_x4(const void* p0, const void* p1, const void* p2, const void* p3,
+                                                 u32x2& r0, u32x2& r1, u32x2& r2, u32x2& r3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2)), "v"(lds_addr(p3))
+      : "memory");
+}
+
+// Two groups of transposed reads at compile-time offsets from two addresses
+// (four reads each): group g reads at a_g + O[g][0..3].
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void lds_read_tr16_2x4(unsigned a0, unsigned a1, u32x2 (&r)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %9 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %6, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1), "n"(O0), "n"(O1), "n"(O2), "n"(O3)
+      : "memory");
+}
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void lds_read_tr16_1x4(unsigned a0, u32x2 (&r)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a0), "n"(O0), "n"(O1), "n"(O2), "n"(O3)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_read_tr16_x8(const void* const p[8], u32x2 (&r)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(lds_addr(p[0])), "v"(lds_addr(p[1])), "v"(lds_addr(p[2])), "v"(lds_addr(p[3])), "v"(lds_addr(p[4])),
+        "v"(lds_addr(p[5])), "v"(lds_addr(p[6])), "v"(lds_addr(p[7]))
+      : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Element-type traits: the operand fragment one lane supplies per k-step.
 // ---------------------------------------------------------------------------

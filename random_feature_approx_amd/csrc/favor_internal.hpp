@@ -19,7 +19,10 @@ struct Plan {
   // K-side reduction (non-causal state, or causal span aggregates)
   int splits;           // token ranges per head
   int split_len;        // tokens per range (multiple of 64)
-  int fgroups;          // feature groups per head (workgroups that share K, V tiles)
+  int rnw;              // waves per reduction workgroup (one 32-feature block each)
+  int rfgroups;         // reduction feature groups per head (workgroups sharing K, V tiles)
+  // causal chunk scan
+  int fgroups;          // feature groups walked in turn by one workgroup
   int fbw;              // 32-feature blocks per wave
   // Q-side apply (non-causal)
   int apply_tile;       // tokens per wave per step

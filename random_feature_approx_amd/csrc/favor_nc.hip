@@ -94,24 +94,50 @@ struct RedArgs {
   int L, M, H, Hw, splits, split_len;
 };
 
-template <class Tr, int D, int FBW>
-__global__ __launch_bounds__(256) void k_reduce(RedArgs a) {
+// Pipeline shape of the K-side kernels: tiles of TT tokens, STAGES tiles of
+// K and V resident in LDS.
+template <class Tr, int D, int NT>
+struct RedLds {
+  using E = typename Tr::elem;
+  static constexpr int ROWB = D * (int)sizeof(E);
+  // 32 tokens for long rows; otherwise 64, or enough rows to give every
+  // thread one 16-byte chunk
+  static constexpr int TT = ROWB >= 256 ? 32 : (NT * 16 / ROWB > 64 ? NT * 16 / ROWB : 64);
+  using DT = DmaTile<E, D, TT, NT>;
+  static constexpr int PAIR = 2 * DT::BYTES;
+  static constexpr int STAGES = 65536 / PAIR >= 4 ? 4 : (65536 / PAIR >= 3 ? 3 : 2);
+  static constexpr int RS = Rows<D, sizeof(E)>::RS;
+  static constexpr int kRing = 0;                       // [STAGES][K tile | V tile]
+  static constexpr int kKh = STAGES * PAIR;             // converted K, padded rows
+  static constexpr int kBias = kKh + TT * RS;
+  static constexpr int kTotal = kBias + TT * 4;
+};
+
+// NW waves per workgroup, each owning one block of 32 features: many
+// independent waves per SIMD let the matrix cores and the exponentials of
+// different waves overlap.
+template <class Tr, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
+  constexpr int FBW = 1;
+  constexpr int NT = NW * 64;
   using E = typename Tr::elem;
   using F = typename Tr::frag;
-  constexpr int TT = 32;                    // tokens per tile
+  using LY = RedLds<Tr, D, NT>;
+  using DT = typename LY::DT;
+  constexpr int TT = LY::TT, S = LY::STAGES;
   constexpr int NKD = D / Tr::KS;           // k-steps over d
   constexpr int NDB = D / 32;               // 32-wide d blocks
-  constexpr int NKT = TT / Tr::KS;          // k-steps over a token tile
-  constexpr int RS = Rows<D, sizeof(E)>::RS;
-  __shared__ __attribute__((aligned(16))) char sK[TT * RS];
-  __shared__ __attribute__((aligned(16))) char sV[TT * RS];
-  __shared__ __attribute__((aligned(16))) float sBias[TT];
+  constexpr int NKT = 32 / Tr::KS;          // k-steps over a 32-token block
+  constexpr int RS = LY::RS;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* sKh = smem + LY::kKh;
+  float* sBias = (float*)(smem + LY::kBias);
 
   const int split = blockIdx.x, fg = blockIdx.y, bh = blockIdx.z;
   const int head = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int nfb = a.M >> 5;
-  const int fb0 = (fg * 4 + w) * FBW;
+  const int fb0 = (fg * NW + w) * FBW;
   const E* K = (const E*)a.k + (size_t)bh * a.L * D;
   const E* V = (const E*)a.v + (size_t)bh * a.L * D;
   const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
@@ -136,57 +162,133 @@ __global__ __launch_bounds__(256) void k_reduce(RedArgs a) {
 
   const int t0 = split * a.split_len;
   const int t1 = min(a.L, t0 + a.split_len);
-  TileLoader<E, D, TT, 256> lk, lv;
-  if (t0 < t1) {
-    lk.load(K + (size_t)t0 * D, t1 - t0, tid);
-    lv.load(V + (size_t)t0 * D, t1 - t0, tid);
-  }
-  for (int t = t0; t < t1; t += TT) {
-    const int nvalid = min(TT, t1 - t);
-    __syncthreads();
-    lk.store_proj(sK, tid);
-    lv.store(sV, tid);
-    lk.row_bias(sBias, tid, nvalid, half_ln_m);
-    __syncthreads();
-    if (t + TT < t1) {                       // prefetch the next tile
-      lk.load(K + (size_t)(t + TT) * D, t1 - t - TT, tid);
-      lv.load(V + (size_t)(t + TT) * D, t1 - t - TT, tid);
-    }
-    F kf[NKD];
-#pragma unroll
-    for (int s = 0; s < NKD; ++s) kf[s] = row_frag<Tr, D>(sK + l32 * RS, hh, s);
-    float bv[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 b4 = *(const f32x4*)(sBias + 8 * i + 4 * hh);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[4 * i + j] = b4[j];
-    }
-    F vf[NDB][NKT];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int s2 = 0; s2 < NKT; ++s2) vf[db][s2] = col_frag<Tr, RS>(sV, 0, db * 32, s2, lane);
+  const int ntiles = t0 < t1 ? (t1 - t0 + TT - 1) / TT : 0;
 
+  // ---- per-lane constants (tile-invariant addressing) ----------------------
+  constexpr int ES = (int)sizeof(E);
+  constexpr int ROWB = DT::ROWB, CPR = DT::CPR, SWZ = DT::SWZ;
+  const typename DT::Lane dplan = DT::lane_plan(w, lane);
+  int prep_src[DT::NI], prep_dst[DT::NI], prep_row[DT::NI];
 #pragma unroll
-    for (int i = 0; i < FBW; ++i) {
-      if (fb0 + i < nfb) {
-        f32x16 acc = zero16();
+  for (int i = 0; i < DT::NI; ++i) {
+    const int c = tid + i * NT;
+    const int r = c / CPR, cc = c % CPR;
+    prep_src[i] = r * ROWB + ((cc ^ (r & SWZ)) << 4);
+    prep_dst[i] = r * RS + cc * 16;
+    prep_row[i] = r;
+  }
+  const bool prep_lead = (tid % CPR) == 0;
+  const int kf_base = l32 * RS + (D / 2) * hh * ES;
+  // transposed V reads: rows 4hh + i16/4 (+16 s, +8, +32 tb), column 32 db + 16 g + 4 (i16 & 3)
+  int tr_base[NDB];
 #pragma unroll
-        for (int s = 0; s < NKD; ++s) acc = Tr::pmma(kf[s], wf[i][s], acc);   // P[t][f], lane = f
+  for (int db = 0; db < NDB; ++db)
+    tr_base[db] = DT::at(4 * hh + ((lane & 15) >> 2), db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+  auto issue = [&](int tt) {
+    char* slot = smem + LY::kRing + (tt % S) * LY::PAIR;
+    const int r0 = t0 + tt * TT;
+    DT::issue_plan(slot, (const char*)(K + (size_t)r0 * D), t1 - r0, dplan, w);
+    DT::issue_plan(slot + DT::BYTES, (const char*)(V + (size_t)r0 * D), t1 - r0, dplan, w);
+  };
+  for (int tt = 0; tt < S - 1 && tt < ntiles; ++tt) issue(tt);
+  // the projection rows of W (loaded before the copies) are complete once at
+  // most the copies are outstanding
+  wait_vmcnt_steps<2 * DT::NI, S - 1>(min(ntiles, S - 1));
+
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int issued = min(ntiles, tt + S - 1);
+    wait_vmcnt_steps<2 * DT::NI, S - 2>(issued - tt - 1);
+    raw_barrier();                            // tile tt landed everywhere; tile tt-1 fully consumed
+    if (tt + S - 1 < ntiles) issue(tt + S - 1);
+    const char* slot = smem + LY::kRing + (tt % S) * LY::PAIR;
+    const int nvalid = min(TT, t1 - (t0 + tt * TT));
+    // ---- stage K: projection operand type, row norms -> bias -------------
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = exp2_fast(acc[r] + bv[r]);
+    for (int i = 0; i < DT::NI; ++i) {
+      u32x4 v = *(const u32x4*)(slot + prep_src[i]);
+      float ss = 0.f;
 #pragma unroll
-        for (int s2 = 0; s2 < NKT; ++s2) {
-          F pf = CFrag<Tr>::make(acc, s2);
-          if constexpr (Tr::VPS == 8) {
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (ES == 2) {
+          const float lo = bf16_lo(v[j]), hi = bf16_hi(v[j]);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+          v[j] = pack_f16(lo, hi);
+        } else {
+          const float x = as_f32(v[j]);
+          ss = fmaf(x, x, ss);
+        }
+      }
+      *(u32x4*)(sKh + prep_dst[i]) = v;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) zs[i] = dot2_bf16(pf[j], 0x3f803f80u, zs[i]);
-          } else {
-            zs[i] += pf;
+      for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+      if (prep_lead) sBias[prep_row[i]] = prep_row[i] < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
+    }
+    wait_lgkm0();
+    raw_barrier();
+    const char* sV = slot + DT::BYTES;
+#pragma unroll
+    for (int tb = 0; tb < TT / 32; ++tb) {
+      F kf[NKD];
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) kf[s] = *(const F*)(sKh + kf_base + tb * 32 * RS + s * Tr::VPS * ES);
+      F vf[NDB][NKT];
+      if constexpr (Tr::VPS == 8) {
+        // V shares LDS with copies still in flight: transposed reads issued
+        // from assembly, which wait only for themselves
+        const unsigned vbase = lds_addr(sV) + tb * 32 * ROWB;
+        if constexpr (NDB == 1) {
+          u32x2 r[4];
+          lds_read_tr16_1x4<0, 8 * ROWB, 16 * ROWB, 24 * ROWB>(vbase + tr_base[0], r);
+          vf[0][0] = u32x4{r[0][0], r[0][1], r[1][0], r[1][1]};
+          vf[0][1] = u32x4{r[2][0], r[2][1], r[3][0], r[3][1]};
+        } else {
+#pragma unroll
+          for (int db = 0; db < NDB; db += 2) {
+            u32x2 r[8];
+            lds_read_tr16_2x4<0, 8 * ROWB, 16 * ROWB, 24 * ROWB>(vbase + tr_base[db], vbase + tr_base[db + 1], r);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              vf[db + j][0] = u32x4{r[4 * j][0], r[4 * j][1], r[4 * j + 1][0], r[4 * j + 1][1]};
+              vf[db + j][1] = u32x4{r[4 * j + 2][0], r[4 * j + 2][1], r[4 * j + 3][0], r[4 * j + 3][1]};
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) vf[db][s2] = col_frag_swz<Tr, DT>(sV, tb * 32, db * 32, s2, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < FBW; ++i) {
+        if (fb0 + i < nfb) {
+          // the accumulator starts at each token's bias, so the projection
+          // lands directly on the base-2 exponent
+          f32x16 acc;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 b4 = *(const f32x4*)(sBias + tb * 32 + 8 * g + 4 * hh);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * g + j] = b4[j];
           }
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) st[i][db] = Tr::mma(pf, vf[db][s2], st[i][db]);
+          for (int s = 0; s < NKD; ++s) acc = Tr::pmma(kf[s], wf[i][s], acc);   // P[t][f] + bias[t], lane = f
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = exp2_fast(acc[r]);
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F pf = CFrag<Tr>::make(acc, s2);
+            if constexpr (Tr::VPS == 8) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) zs[i] = dot2_bf16(pf[j], 0x3f803f80u, zs[i]);
+            } else {
+              zs[i] += pf;
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) st[i][db] = Tr::mma(pf, vf[db][s2], st[i][db]);
+          }
         }
       }
     }
@@ -458,16 +560,13 @@ template <class Tr, int D>
 hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
                            hipStream_t s) {
   RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len};
-  dim3 grid(p.splits, p.fgroups, p.BH);
-  if constexpr (Tr::VPS == 8 && D <= 64) {
-    if (p.fbw != 2) return hipErrorInvalidValue;
-    timing_begin(FAVOR_KERNEL_REDUCE, s);
-    hipLaunchKernelGGL((k_reduce<Tr, D, 2>), grid, dim3(256), 0, s, a);
-  } else {
-    if (p.fbw != 1) return hipErrorInvalidValue;
-    timing_begin(FAVOR_KERNEL_REDUCE, s);
-    hipLaunchKernelGGL((k_reduce<Tr, D, 1>), grid, dim3(256), 0, s, a);
-  }
+  // waves per workgroup: 8, or 4 where a wave's registers exceed half a SIMD's
+  constexpr int NW = (Tr::VPS == 1 && D == 128) ? 4 : 8;
+  if (p.rnw != NW) return hipErrorInvalidValue;
+  dim3 grid(p.splits, p.rfgroups, p.BH);
+  const size_t lds = RedLds<Tr, D, NW * 64>::kTotal;
+  timing_begin(FAVOR_KERNEL_REDUCE, s);
+  hipLaunchKernelGGL((k_reduce<Tr, D, NW>), grid, dim3(NW * 64), lds, s, a);
   timing_end(FAVOR_KERNEL_REDUCE, s);
   return hipGetLastError();
 }
