@@ -69,9 +69,10 @@ const char* favor_status_string(favor_status s);
  * Bytes of device workspace that favor_attn_noncausal (causal = 0) or
  * favor_attn_causal (causal = 1) needs for these shapes on the current
  * device (the split of L over workgroups depends on its compute-unit
- * count).  Returns 0 when the arguments are invalid.  The workspace holds
- * float32 partial states and has no meaning between calls; it needs no
- * initialisation.  Its base must be 256-byte aligned.
+ * count).  Returns 0 when the arguments are invalid.  The size covers both
+ * Hw = 1 and Hw = H.  The workspace holds float32 partial states and the
+ * projection operand prepared from W; it has no meaning between calls and
+ * needs no initialisation.  Its base must be 256-byte aligned.
  */
 size_t favor_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype);
 
@@ -136,7 +137,8 @@ typedef enum {
   FAVOR_KERNEL_APPLY = 3,      /* non-causal Q-side apply                         */
   FAVOR_KERNEL_SPAN_SCAN = 4,  /* causal exclusive prefix over spans              */
   FAVOR_KERNEL_CAUSAL = 5,     /* causal chunked scan                             */
-  FAVOR_KERNEL_COUNT = 6
+  FAVOR_KERNEL_WPREP = 6,      /* projection operand (W log2 e, operand order)    */
+  FAVOR_KERNEL_COUNT = 7
 } favor_kernel;
 
 favor_status favor_timing_start(favor_kernel k, int capacity);

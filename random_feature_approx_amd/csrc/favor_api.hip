@@ -55,16 +55,17 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   len = (len + 63) / 64 * 64;
   p.split_len = len;
   p.splits = (L + len - 1) / len;
-  // apply: groups of 4 waves x TB x 32 tokens of one head
+  // apply: one workgroup of 8 waves per compute unit, walking groups of
+  // 8 waves x TB x 32 tokens of one head
   const int tb = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
   p.apply_tile = tb * 32;
-  const int gph = (L + 4 * p.apply_tile - 1) / (4 * p.apply_tile);
+  const int gph = (L + 8 * p.apply_tile - 1) / (8 * p.apply_tile);
   const int total = p.BH * gph;
-  p.apply_steps = (total + target - 1) / target;
+  p.apply_steps = (total + num_cus - 1) / num_cus;
   if (p.apply_steps < 1) p.apply_steps = 1;
   p.apply_groups = (total + p.apply_steps - 1) / p.apply_steps;
-  const int rs = d * p.esize + 16;
-  int fch = 81920 / (2 * rs + p.esize);
+  const int wes = dt == FAVOR_BF16 ? 2 : 4;         // projection operand bytes
+  int fch = 98304 / (d * wes + d * p.esize + p.esize);   // projection operand, M and z per feature
   fch = fch / 32 * 32;
   p.fch = fch < m ? fch : m;
   // workspace
@@ -73,6 +74,10 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   off += align256((size_t)p.BH * p.splits * m * d * sizeof(float));
   p.off_partz = off;
   off += align256((size_t)p.BH * p.splits * m * sizeof(float));
+  // projection operand, sized for one projection per head (Hw = H) so that
+  // the size does not depend on Hw
+  p.off_wprep = off;
+  off += align256((size_t)H * m * d * (dt == FAVOR_BF16 ? 2 : 4));
   p.off_mstate = off;
   off += align256((size_t)p.BH * m * d * p.esize);
   p.off_zstate = off;
@@ -232,6 +237,7 @@ const char* favor_kernel_name(favor_kernel k) {
     case FAVOR_KERNEL_APPLY: return "k_apply";
     case FAVOR_KERNEL_SPAN_SCAN: return "k_span_scan";
     case FAVOR_KERNEL_CAUSAL: return "k_causal";
+    case FAVOR_KERNEL_WPREP: return "k_wprep";
     default: return "unknown";
   }
 }

@@ -8,7 +8,7 @@
 //   1. k_reduce (shared with the non-causal path) computes every span's
 //      aggregate [sum phi(k) v^T | sum phi(k)] in float32.
 //   2. k_span_scan turns the aggregates into exclusive prefixes in place, in
-//      span order (deterministic).
+//      a fixed order of additions (deterministic).
 //   3. k_causal walks the chunks of a span starting from its prefix.  For a
 //      chunk c with queries Q_c, keys K_c and values V_c:
 //        num = tril(phi(Q_c) phi(K_c)^T) V_c + phi(Q_c) S      (masked tile
@@ -28,26 +28,60 @@ namespace favor {
 
 // ---------------------------------------------------------------------------
 // exclusive prefix of the span aggregates, in place:  a[s] <- sum_{s'<s} a[s']
+// The m*d + m values of a head are handled in quads of 4 floats.  A block is
+// kScanGroups groups of threads; group g owns spans [g*per, (g+1)*per) of its
+// quad: it first sums them, the groups' sums give each group its starting
+// offset (added in group order), and a second pass writes the running
+// prefixes.  The order of additions depends only on the span count.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, int spans, int MD, int M) {
+constexpr int kScanGroups = 8;
+constexpr int kScanQuads = 256 / kScanGroups;
+
+__global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, int spans, int M, int D) {
+  __shared__ f32x4 tot[kScanGroups][kScanQuads];
   const int bh = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  float* p;
-  int stride;
-  if (idx < MD) {
-    p = part + (size_t)bh * spans * MD + idx;
-    stride = MD;
-  } else if (idx < MD + M) {
-    p = partz + (size_t)bh * spans * M + (idx - MD);
-    stride = M;
+  const int g = threadIdx.x / kScanQuads, qi = threadIdx.x % kScanQuads;
+  const int quad = blockIdx.x * kScanQuads + qi;
+  const int md4 = M * D / 4, nq = md4 + M / 4;
+  const bool active = quad < nq;
+  f32x4* p;
+  size_t stride;
+  if (quad < md4) {
+    p = (f32x4*)(part + (size_t)bh * spans * M * D) + quad;
+    stride = md4;
   } else {
-    return;
+    p = (f32x4*)(partz + (size_t)bh * spans * M) + (active ? quad - md4 : 0);
+    stride = M / 4;
   }
-  float run = 0.f;
-  for (int s = 0; s < spans; ++s) {
-    const float t = p[(size_t)s * stride];
-    p[(size_t)s * stride] = run;
-    run += t;
+  const int per = (spans + kScanGroups - 1) / kScanGroups;
+  const int s0 = min(spans, g * per), s1 = min(spans, s0 + per);
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 sum = zero;
+  if (active) {
+    for (int s = s0; s < s1; s += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = s + j < s1 ? p[(size_t)(s + j) * stride] : zero;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += v[j];
+    }
+  }
+  tot[g][qi] = sum;
+  __syncthreads();
+  if (!active) return;
+  f32x4 run = zero;
+  for (int gg = 0; gg < g; ++gg) run += tot[gg][qi];
+  for (int s = s0; s < s1; s += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = s + j < s1 ? p[(size_t)(s + j) * stride] : zero;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s + j < s1) {
+        p[(size_t)(s + j) * stride] = run;
+        run += v[j];
+      }
+    }
   }
 }
 
@@ -393,10 +427,10 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   float* partz = (float*)(t.ws + p.off_partz);
   hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
   if (e != hipSuccess) return e;
-  const int MD = p.M * p.D;
+  const int nq = (p.M * p.D + p.M) / 4;
   timing_begin(FAVOR_KERNEL_SPAN_SCAN, s);
-  hipLaunchKernelGGL(k_span_scan, dim3((MD + p.M + 255) / 256, p.BH), dim3(256), 0, s, part, partz, p.splits, MD,
-                     p.M);
+  hipLaunchKernelGGL(k_span_scan, dim3((nq + kScanQuads - 1) / kScanQuads, p.BH), dim3(256), 0, s, part, partz,
+                     p.splits, p.M, p.D);
   timing_end(FAVOR_KERNEL_SPAN_SCAN, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -27,10 +27,10 @@ struct Plan {
   // Q-side apply (non-causal)
   int apply_tile;       // tokens per wave per step
   int apply_groups;     // total workgroups
-  int apply_steps;      // 4-tile steps per workgroup
+  int apply_steps;      // groups per workgroup
   int fch;              // features per LDS chunk
   // workspace offsets (bytes)
-  size_t off_part, off_partz, off_mstate, off_zstate, off_num, off_den, total;
+  size_t off_part, off_partz, off_wprep, off_mstate, off_zstate, off_num, off_den, total;
 };
 
 bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus);
@@ -51,6 +51,7 @@ struct Tensors {
 void timing_begin(favor_kernel k, hipStream_t s);
 void timing_end(favor_kernel k, hipStream_t s);
 
+hipError_t launch_wprep(const Plan& p, const float* w, void* out, hipStream_t s);
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);

@@ -16,6 +16,7 @@
 #include "favor_tiles.hpp"
 
 #include <math.h>
+#include <type_traits>
 
 namespace favor {
 
@@ -311,98 +312,222 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
 }
 
 // ===========================================================================
-// Combine: sum the partial states of a head in split order (deterministic)
-// and store the operand-type state used by the apply step.
+// Combine: sum the partial states of a head in a fixed order (deterministic)
+// and store the state in the operand order of the apply step.
 // ===========================================================================
+// Position of state element (f, d) in operand order [group][half][d][slot]:
+// the features of a lane's k-slots sit next to each other, so the apply step
+// reads its state operand with one 16-byte load per lane and a wave reads
+// contiguous memory.  bf16: group of 16 features (one 32x32x16 k-step),
+// f = 16 g + 8 a + 4 h + b -> slot j = 4 a + b of lane half h;  float: group
+// of 8 features (four 32x32x2 k-steps), f = 8 g + 4 h + b -> slot b.
+template <class E>
+struct OperandOrder {
+  static constexpr int J = sizeof(E) == 2 ? 8 : 4;   // slots per lane and group
+  static constexpr int GF = 2 * J;                  // features per group
+  static __device__ __forceinline__ int slot(int f) {
+    const int q = f % GF;
+    return sizeof(E) == 2 ? (((q >> 3) << 2) | (q & 3)) : (q & 3);
+  }
+  static __device__ __forceinline__ int half(int f) { return (f >> 2) & 1; }
+  static __device__ __forceinline__ int mpos(int f, int d, int D) { return (((f / GF) * 2 + half(f)) * D + d) * J + slot(f); }
+  static __device__ __forceinline__ int zpos(int f) { return ((f / GF) * 2 + half(f)) * J + slot(f); }
+};
+
+// The m*d + m values of a head's state are handled in quads of 4 floats;
+// a block is kSplitGroups groups of threads, group g summing splits
+// [g*per, (g+1)*per) of its quad in order, and the groups' sums are added in
+// group order.
+constexpr int kSplitGroups = 8;
+constexpr int kQuadsPerBlock = 256 / kSplitGroups;
+
 template <class E>
 __global__ __launch_bounds__(256) void k_combine(const float* part, const float* partz, E* mstate, E* zstate,
-                                                 int splits, int MD, int M) {
+                                                 int splits, int M, int D) {
+  __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
   const int bh = blockIdx.y;
+  const int g = threadIdx.x / kQuadsPerBlock, qi = threadIdx.x % kQuadsPerBlock;
+  const int quad = blockIdx.x * kQuadsPerBlock + qi;
+  const int md4 = M * D / 4, nq = md4 + M / 4;
+  const bool active = quad < nq;
+  const f32x4* src;
+  size_t stride;
+  if (quad < md4) {
+    src = (const f32x4*)(part + (size_t)bh * splits * M * D) + quad;
+    stride = md4;
+  } else {
+    src = (const f32x4*)(partz + (size_t)bh * splits * M) + (active ? quad - md4 : 0);
+    stride = M / 4;
+  }
+  const int per = (splits + kSplitGroups - 1) / kSplitGroups;
+  const int s0 = min(splits, g * per), s1 = min(splits, s0 + per);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    for (int s = s0; s < s1; s += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = s + j < s1 ? src[(size_t)(s + j) * stride] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += v[j];
+    }
+  }
+  red[g][qi] = acc;
+  __syncthreads();
+  if (g != 0 || !active) return;
+#pragma unroll
+  for (int gg = 1; gg < kSplitGroups; ++gg) acc += red[gg][qi];
+  using OO = OperandOrder<E>;
+  if (quad < md4) {
+    const int f = quad * 4 / D, d0 = quad * 4 % D;
+    E* dst = mstate + (size_t)bh * M * D;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[OO::mpos(f, d0 + c, D)] = (E)acc[c];
+  } else {
+    const int f0 = (quad - md4) * 4;
+    E* dst = zstate + (size_t)bh * M;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[OO::zpos(f0 + c)] = (E)acc[c];
+  }
+}
+
+// ===========================================================================
+// Projection operand: W log2(e) in the operand type of the projection (fp16
+// for bf16 inputs, float otherwise), in operand order
+// [Hw*M/32 feature blocks][NKG][half h][feature f][16 bytes]: the 16 bytes of
+// lane (f, h) at k-group g hold d = (D/2) h + (16/WES) g + 0.. (the d-major
+// k order of the projection), so a wave reads 1 KB of contiguous memory.
+// ===========================================================================
+template <class Tr, int D>
+__global__ __launch_bounds__(256) void k_wprep(const float* w, void* out, int n16) {
+  constexpr int WES = Tr::VPS == 8 ? 2 : 4;
+  constexpr int NKG = D * WES / 32;
+  constexpr int PER = 16 / WES;                      // d values per 16 bytes
   const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx < MD) {
-    const float* p = part + (size_t)bh * splits * MD + idx;
-    float s = 0.f;
-    for (int i = 0; i < splits; ++i) s += p[(size_t)i * MD];
-    mstate[(size_t)bh * MD + idx] = (E)s;
-  } else if (idx < MD + M) {
-    const int j = idx - MD;
-    const float* p = partz + (size_t)bh * splits * M + j;
-    float s = 0.f;
-    for (int i = 0; i < splits; ++i) s += p[(size_t)i * M];
-    zstate[(size_t)bh * M + j] = (E)s;
+  if (idx >= n16) return;
+  const int f = idx & 31, h = (idx >> 5) & 1, rest = idx >> 6;
+  const int g = rest % NKG, blk = rest / NKG;
+  const float* src = w + (size_t)(blk * 32 + f) * D + (D / 2) * h + PER * g;
+  if constexpr (WES == 2) {
+    const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+    u32x4 v = {pack_f16(x0[0] * kLog2e, x0[1] * kLog2e), pack_f16(x0[2] * kLog2e, x0[3] * kLog2e),
+               pack_f16(x1[0] * kLog2e, x1[1] * kLog2e), pack_f16(x1[2] * kLog2e, x1[3] * kLog2e)};
+    ((u32x4*)out)[idx] = v;
+  } else {
+    ((f32x4*)out)[idx] = *(const f32x4*)src * kLog2e;
   }
 }
 
 // ===========================================================================
 // Q-side apply: O = phi(Q) M / (phi(Q) z + eps).
-// A workgroup walks a contiguous range of "groups" (4 waves x TB x 32 tokens
-// of one head).  W (log2 e scaled), M and z of the current head sit in LDS in
-// chunks of FCH features; with a single chunk they are loaded once per head.
+// A workgroup of 8 waves walks a contiguous range of "groups" (8 waves x TB x
+// 32 tokens of one head).  The projection operand, M and z of the current
+// head sit in LDS in chunks of FCH features, all in operand order, copied
+// with global->LDS loads; with a single chunk they are loaded once per head.
 // Output is computed transposed, O^T = M^T phi(Q)^T, so each lane owns one
-// token and divides by its own denominator.
+// token and divides by its own denominator.  The rows of Q for the next
+// group are loaded while the current group is computed.
 // ===========================================================================
 struct ApplyArgs {
   const void* q;
-  const float* w;
-  const void* mstate;   // [BH][M][D] operand type
-  const void* zstate;   // [BH][M]
+  const void* wp;       // projection operand (k_wprep)
+  const void* mstate;   // [BH] x operand-ordered M (m x d), operand type
+  const void* zstate;   // [BH] x operand-ordered z (m), operand type
   void* o;
   int L, M, H, Hw;
   float eps;
   int groups_per_head, groups_total, steps, fch;
 };
 
+constexpr int kApplyWaves = 8;
+
 template <class Tr, int D, int TB>
-__global__ __launch_bounds__(256) void k_apply(ApplyArgs a) {
+__global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
+  constexpr int NW = kApplyWaves, NT = NW * 64;
   constexpr int NKD = D / Tr::KS;
   constexpr int NDB = D / 32;
   constexpr int ES = sizeof(E);
-  constexpr int RS = Rows<D, ES>::RS;
+  constexpr int WES = Tr::VPS == 8 ? 2 : 4;
+  constexpr int NKG = D * WES / 32;
+  constexpr bool QV = Tr::VPS == 8;                  // raw Q kept as 16-byte vectors (bf16)
+  using QRaw = typename std::conditional<QV, u32x4, float>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int FCH = a.fch;
   char* sW = smem;
-  char* sM = smem + FCH * RS;
-  E* sZ = (E*)(smem + 2 * FCH * RS);
+  char* sM = sW + FCH * D * WES;
+  char* sZ = sM + FCH * D * ES;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int nch = (a.M + FCH - 1) / FCH;
   const float half_ln_m = 0.5f * logf((float)a.M);
   const int g0 = blockIdx.x * a.steps;
   const int g1 = min(a.groups_total, g0 + a.steps);
-  int cur_bh = -1;
-  for (int g = g0; g < g1; ++g) {
-    const int bh = g / a.groups_per_head;
-    const int tbase = (g % a.groups_per_head) * (4 * TB * 32) + w * TB * 32;
-    const int head = bh % a.H;
-    const bool reload = nch > 1 || bh != cur_bh;
-    cur_bh = bh;
-    const E* Q = (const E*)a.q + (size_t)bh * a.L * D;
 
-    F qf[TB][NKD];
-    float bias[TB];
+  auto load_q = [&](int g, QRaw (&raw)[TB][NKD]) {
+    const int bh = g / a.groups_per_head;
+    const int tbase = (g % a.groups_per_head) * (NW * TB * 32) + w * TB * 32;
+    const E* Q = (const E*)a.q + (size_t)bh * a.L * D;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int tok = tbase + tb * 32 + l32;
       const bool ok = tok < a.L;
       const E* qrow = Q + (size_t)(ok ? tok : 0) * D;
-      float ss = 0.f;
 #pragma unroll
       for (int s = 0; s < NKD; ++s) {
         const int d0 = (D / 2) * hh + Tr::VPS * s;
-        if constexpr (Tr::VPS == 8) {
-          u32x4 v = ok ? __builtin_nontemporal_load((const u32x4*)(qrow + d0)) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (QV)
+          raw[tb][s] = ok ? __builtin_nontemporal_load((const u32x4*)(qrow + d0)) : u32x4{0u, 0u, 0u, 0u};
+        else
+          raw[tb][s] = ok ? __builtin_nontemporal_load(qrow + d0) : 0.f;
+      }
+    }
+  };
+  // all waves finished with the previous contents; copy; copies landed everywhere
+  auto reload = [&](int bh, int f0, int nf) {
+    const int head = bh % a.H;
+    __syncthreads();
+    dma_copy<NT>(sW, (const char*)a.wp + ((size_t)(a.Hw == 1 ? 0 : head) * a.M + f0) * D * WES, nf * D * WES / 16, tid);
+    dma_copy<NT>(sM, (const char*)a.mstate + ((size_t)bh * a.M + f0) * D * ES, nf * D * ES / 16, tid);
+    dma_copy<NT>(sZ, (const char*)a.zstate + ((size_t)bh * a.M + f0) * ES, nf * ES / 16, tid);
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
+
+  QRaw qnext[TB][NKD];
+  if (g0 < g1) load_q(g0, qnext);
+  int cur_bh = -1;
+  for (int g = g0; g < g1; ++g) {
+    const int bh = g / a.groups_per_head;
+    const int tbase = (g % a.groups_per_head) * (NW * TB * 32) + w * TB * 32;
+    if (nch == 1 && bh != cur_bh) reload(bh, 0, a.M);
+    cur_bh = bh;
+
+    QRaw qraw[TB][NKD];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) qraw[tb][s] = qnext[tb][s];
+    if (g + 1 < g1) load_q(g + 1, qnext);
+
+    F qf[TB][NKD];
+    float bias[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) {
+        if constexpr (QV) {
+          const u32x4 v = qraw[tb][s];
           qf[tb][s] = Tr::to_proj(v);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            float p = bf16_lo(v[j]), q = bf16_hi(v[j]);
+            const float p = bf16_lo(v[j]), q = bf16_hi(v[j]);
             ss = fmaf(p, p, fmaf(q, q, ss));
           }
         } else {
-          float v = ok ? qrow[d0] : 0.f;
-          qf[tb][s] = v;
-          ss = fmaf(v, v, ss);
+          qf[tb][s] = qraw[tb][s];
+          ss = fmaf(qraw[tb][s], qraw[tb][s], ss);
         }
       }
       ss += __shfl_xor(ss, 32);
@@ -421,33 +546,20 @@ __global__ __launch_bounds__(256) void k_apply(ApplyArgs a) {
     for (int ch = 0; ch < nch; ++ch) {
       const int f0 = ch * FCH;
       const int nf = min(FCH, a.M - f0);
-      if (reload) {
-        __syncthreads();
-        const float* wh = a.w + ((size_t)(a.Hw == 1 ? 0 : head) * a.M + f0) * D;
-        for (int e = tid * 4; e < nf * D; e += 256 * 4) {
-          f32x4 x = *(const f32x4*)(wh + e);
-          const int row = e / D, col = e % D;
-          if constexpr (ES == 2) {
-            u32x2 pk = {pack_f16(x[0] * kLog2e, x[1] * kLog2e), pack_f16(x[2] * kLog2e, x[3] * kLog2e)};
-            *(u32x2*)(sW + row * RS + col * 2) = pk;
-          } else {
-            *(f32x4*)(sW + row * RS + col * 4) = x * kLog2e;
-          }
-        }
-        const char* ms = (const char*)a.mstate + ((size_t)bh * a.M + f0) * D * ES;
-        constexpr int CPR = Rows<D, ES>::CPR;
-        for (int c = tid; c < nf * CPR; c += 256) {
-          const int row = c / CPR, cc = c % CPR;
-          *(u32x4*)(sM + row * RS + cc * 16) = *(const u32x4*)(ms + (size_t)row * D * ES + cc * 16);
-        }
-        const E* zs = (const E*)a.zstate + (size_t)bh * a.M + f0;
-        for (int j = tid; j < nf; j += 256) sZ[j] = zs[j];
-        __syncthreads();
-      }
+      if (nch > 1) reload(bh, f0, nf);
       for (int fb = 0; fb < (nf >> 5); ++fb) {
         F wfr[NKD];
+        if constexpr (WES == 2) {
 #pragma unroll
-        for (int s = 0; s < NKD; ++s) wfr[s] = row_frag<Tr, D>(sW + (fb * 32 + l32) * RS, hh, s);
+          for (int s = 0; s < NKD; ++s) wfr[s] = *(const u32x4*)(sW + (((fb * NKG + s) * 2 + hh) * 32 + l32) * 16);
+        } else {
+#pragma unroll
+          for (int gk = 0; gk < NKG; ++gk) {
+            const f32x4 v = *(const f32x4*)(sW + (((fb * NKG + gk) * 2 + hh) * 32 + l32) * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wfr[4 * gk + j] = v[j];
+          }
+        }
         f32x16 pacc[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
@@ -458,41 +570,41 @@ __global__ __launch_bounds__(256) void k_apply(ApplyArgs a) {
           for (int r = 0; r < 16; ++r) pacc[tb][r] = exp2_fast(pacc[tb][r] + bias[tb]);
         }
         if constexpr (Tr::VPS == 8) {
-          u32x2 zf[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) zf[i] = *(const u32x2*)(sZ + fb * 32 + 8 * i + 4 * hh);
+          // group gi = 2 fb + s2 holds 16 features; lane (d, hh) reads 8 of them
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
+            const int gi = 2 * fb + s2;
+            const u32x4 zf = *(const u32x4*)(sZ + (gi * 2 + hh) * 16);
             F mf[NDB];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) mf[db] = col_frag<Tr, RS>(sM, fb * 32, db * 32, s2, lane);
+            for (int db = 0; db < NDB; ++db) mf[db] = *(const u32x4*)(sM + ((gi * 2 + hh) * D + db * 32 + l32) * 16);
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
               F pf = CFrag<Tr>::make(pacc[tb], s2);
 #pragma unroll
-              for (int k = 0; k < 4; ++k) den[tb] = dot2_bf16(pf[k], zf[2 * s2 + (k >> 1)][k & 1], den[tb]);
+              for (int k = 0; k < 4; ++k) den[tb] = dot2_bf16(pf[k], zf[k], den[tb]);
 #pragma unroll
               for (int db = 0; db < NDB; ++db) oacc[tb][db] = Tr::mma(mf[db], pf, oacc[tb][db]);
             }
           }
         } else {
-          float zf[16];
+          // group gi = 4 fb + s4 holds 8 features; lane (d, hh) reads 4 of them
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f32x4 z4 = *(const f32x4*)((const float*)sZ + fb * 32 + 8 * i + 4 * hh);
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const int gi = 4 * fb + s4;
+            const f32x4 zf = *(const f32x4*)(sZ + (gi * 2 + hh) * 16);
+            f32x4 mf[NDB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) zf[4 * i + j] = z4[j];
-          }
+            for (int db = 0; db < NDB; ++db) mf[db] = *(const f32x4*)(sM + ((gi * 2 + hh) * D + db * 32 + l32) * 16);
 #pragma unroll
-          for (int s2 = 0; s2 < 16; ++s2) {
-            F mf[NDB];
+            for (int j = 0; j < 4; ++j) {
+              const int s = 4 * s4 + j;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) mf[db] = col_frag<Tr, RS>(sM, fb * 32, db * 32, s2, lane);
+              for (int tb = 0; tb < TB; ++tb) {
+                den[tb] = fmaf(pacc[tb][s], zf[j], den[tb]);
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-              den[tb] = fmaf(pacc[tb][s2], zf[s2], den[tb]);
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) oacc[tb][db] = Tr::mma(mf[db], pacc[tb][s2], oacc[tb][db]);
+                for (int db = 0; db < NDB; ++db) oacc[tb][db] = Tr::mma(mf[db][j], pacc[tb][s], oacc[tb][db]);
+              }
             }
           }
         }
@@ -590,32 +702,63 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const floa
 }
 
 template <class Tr, int D, int TB>
-static hipError_t apply_t(const Plan& p, const Tensors& t, const void* mstate, const void* zstate, hipStream_t s) {
+static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const void* mstate, const void* zstate,
+                          hipStream_t s) {
   using E = typename Tr::elem;
-  const int gph = (p.L + 4 * TB * 32 - 1) / (4 * TB * 32);
+  constexpr int WES = Tr::VPS == 8 ? 2 : 4;
+  const int gsz = kApplyWaves * TB * 32;
+  const int gph = (p.L + gsz - 1) / gsz;
   const int total = p.BH * gph;
-  ApplyArgs a{t.q, t.w, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch};
+  ApplyArgs a{t.q, wp, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
-  const size_t lds = 2 * (size_t)p.fch * Rows<D, sizeof(E)>::RS + (size_t)p.fch * sizeof(E);
+  const size_t lds = (size_t)p.fch * D * WES + (size_t)p.fch * D * sizeof(E) + (size_t)p.fch * sizeof(E);
+  if (TB * 32 != p.apply_tile) return hipErrorInvalidValue;
   timing_begin(FAVOR_KERNEL_APPLY, s);
-  hipLaunchKernelGGL((k_apply<Tr, D, TB>), dim3(nblk), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((k_apply<Tr, D, TB>), dim3(nblk), dim3(kApplyWaves * 64), lds, s, a);
   timing_end(FAVOR_KERNEL_APPLY, s);
   return hipGetLastError();
 }
 
-static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* mstate, const void* zstate,
-                               hipStream_t s) {
+template <class Tr, int D>
+static hipError_t wprep_t(const Plan& p, const float* w, void* out, hipStream_t s) {
+  constexpr int WES = Tr::VPS == 8 ? 2 : 4;
+  const int n16 = p.Hw * p.M * D * WES / 16;
+  timing_begin(FAVOR_KERNEL_WPREP, s);
+  hipLaunchKernelGGL((k_wprep<Tr, D>), dim3((n16 + 255) / 256), dim3(256), 0, s, w, out, n16);
+  timing_end(FAVOR_KERNEL_WPREP, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_wprep(const Plan& p, const float* w, void* out, hipStream_t s) {
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
-      case 32: return apply_t<TrBF16, 32, 2>(p, t, mstate, zstate, s);
-      case 64: return apply_t<TrBF16, 64, 2>(p, t, mstate, zstate, s);
-      case 128: return apply_t<TrBF16, 128, 1>(p, t, mstate, zstate, s);
+      case 32: return wprep_t<TrBF16, 32>(p, w, out, s);
+      case 64: return wprep_t<TrBF16, 64>(p, w, out, s);
+      case 128: return wprep_t<TrBF16, 128>(p, w, out, s);
     }
   } else {
     switch (p.D) {
-      case 32: return apply_t<TrF32, 32, 1>(p, t, mstate, zstate, s);
-      case 64: return apply_t<TrF32, 64, 1>(p, t, mstate, zstate, s);
-      case 128: return apply_t<TrF32, 128, 1>(p, t, mstate, zstate, s);
+      case 32: return wprep_t<TrF32, 32>(p, w, out, s);
+      case 64: return wprep_t<TrF32, 64>(p, w, out, s);
+      case 128: return wprep_t<TrF32, 128>(p, w, out, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* wp, const void* mstate,
+                               const void* zstate, hipStream_t s) {
+  if (p.dt == FAVOR_BF16) {
+    switch (p.D) {
+      case 32: return apply_t<TrBF16, 32, 2>(p, t, wp, mstate, zstate, s);
+      case 64: return apply_t<TrBF16, 64, 2>(p, t, wp, mstate, zstate, s);
+      case 128: return apply_t<TrBF16, 128, 1>(p, t, wp, mstate, zstate, s);
+    }
+  } else {
+    switch (p.D) {
+      case 32: return apply_t<TrF32, 32, 1>(p, t, wp, mstate, zstate, s);
+      case 64: return apply_t<TrF32, 64, 1>(p, t, wp, mstate, zstate, s);
+      case 128: return apply_t<TrF32, 128, 1>(p, t, wp, mstate, zstate, s);
     }
   }
   return hipErrorInvalidValue;
@@ -624,23 +767,26 @@ static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* msta
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
   float* part = (float*)(t.ws + p.off_part);
   float* partz = (float*)(t.ws + p.off_partz);
+  void* wp = t.ws + p.off_wprep;
   void* mstate = t.ws + p.off_mstate;
   void* zstate = t.ws + p.off_zstate;
-  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
+  hipError_t e = launch_wprep(p, t.w, wp, s);
   if (e != hipSuccess) return e;
-  const int MD = p.M * p.D;
-  dim3 cgrid((MD + p.M + 255) / 256, p.BH);
+  e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
+  if (e != hipSuccess) return e;
+  const int nq = (p.M * p.D + p.M) / 4;
+  dim3 cgrid((nq + kQuadsPerBlock - 1) / kQuadsPerBlock, p.BH);
   timing_begin(FAVOR_KERNEL_COMBINE, s);
   if (p.dt == FAVOR_BF16)
     hipLaunchKernelGGL((k_combine<bf16>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate, p.splits,
-                       MD, p.M);
+                       p.M, p.D);
   else
     hipLaunchKernelGGL((k_combine<float>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
-                       p.splits, MD, p.M);
+                       p.splits, p.M, p.D);
   timing_end(FAVOR_KERNEL_COMBINE, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_apply(p, t, mstate, zstate, s);
+  return launch_apply(p, t, wp, mstate, zstate, s);
 }
 
 }  // namespace favor

@@ -165,6 +165,18 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Copy n16 16-byte chunks from global src to LDS dst with global->LDS loads
+// issued by all NT threads (chunk c lands at dst + 16 c).  Completion is
+// waited for with the vector-memory counter.
+template <int NT>
+__device__ __forceinline__ void dma_copy(char* dst, const char* src, int n16, int tid) {
+  const int w = tid >> 6, lane = tid & 63;
+  for (int c0 = w * 64; c0 < n16; c0 += NT) {
+    const int c = c0 + lane;
+    if (c < n16) __builtin_amdgcn_global_load_lds(FAVOR_GLB(src + (size_t)c * 16), LDS_PTR(void, dst + c0 * 16), 16, 0, 0);
+  }
+}
+
 template <class E, int D, int TT, int NT = 256>
 struct DmaTile {
   static constexpr int ROWB = D * (int)sizeof(E);       // bytes per dense row
