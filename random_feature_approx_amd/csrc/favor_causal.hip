@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
               st[i][db] = Tr::mma(kt, vf, st[i][db]);
             }
           }
-        zc += __shfl_xor(zc, 32);
+        zc = half_sum(zc);
         zreg[i] += zc;
       }
       // publish z for the next chunk (wave-private; read after this wave's
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
                         nacc[db][tqb][4 * g + 3]};
             *(f32x4*)(rrow + db * 32 + 8 * g + 4 * hh) = v4;
           }
-        const float dsum = dacc[tqb] + __shfl_xor(dacc[tqb], 32);
+        const float dsum = half_sum(dacc[tqb]);
         if (hh == 0) sRedDen[w * C + tqb * 32 + l32] = dsum;
       }
       __syncthreads();
@@ -409,6 +409,329 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 chunked scan for d <= 64, chunks of C = 32 or 64 tokens.  Same split
+// of the features over four waves as k_causal, with every operand read as a
+// 16-byte fragment and few enough live registers for two workgroups per
+// compute unit at C = 32:
+//  - the staged chunk buffers are double-buffered: chunk c+1 is stored while
+//    chunk c is computed, and its V tile is rearranged into operand order
+//    V^T (lane = d, k-slots = tokens in c-row order) once, after the second
+//    barrier of iteration c;
+//  - phi(K) is brought from lane = token (the projection's layout, used by
+//    the intra-chunk scores) to lane = feature (used by the state update) on
+//    the matrix cores: multiplying the fragment by the 32 x 32 identity gives
+//    the same values with rows and columns exchanged, exactly;
+//  - features past m get a bias of -inf, so their phi is exactly zero.
+// ---------------------------------------------------------------------------
+template <int D, int C>
+struct CausalLds2 {
+  static constexpr int RS = Rows<D, 2>::RS;             // padded 16-bit rows
+  static constexpr int TILE = C * RS;
+  // one chunk buffer: Q and K in the projection type, raw V, V^T, row biases
+  static constexpr int kQh = 0, kKh = TILE, kV = 2 * TILE, kVT = 3 * TILE;
+  static constexpr int kBq = kVT + C * D * 2, kBk = kBq + C * 4;
+  static constexpr int BUF = kBk + C * 4;
+  static constexpr int RSR = (D + 4) * 4;                // reduction rows (float)
+  static constexpr int kRed = 2 * BUF, kRedDen = kRed + 4 * C * RSR;
+  static constexpr int kZ = kRedDen + 4 * C * 4;
+  static constexpr int kTotal = kZ + 4 * 64 * 4;          // z of 4 waves x 64 features
+};
+
+template <int D, int FBW, int C>
+__global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
+  using Tr = TrBF16;
+  using E = bf16;
+  using F = u32x4;
+  using LY = CausalLds2<D, C>;
+  constexpr int RS = LY::RS, RSR = LY::RSR;
+  constexpr int NTB = C / 32;                  // 32-token blocks per chunk
+  constexpr int NKD = D / Tr::KS;
+  constexpr int NDB = D / 32;
+  constexpr int NVT = 2 * NTB * NDB;           // V^T fragments per chunk
+  static_assert(FBW * 32 <= 64, "z slots per wave");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* sRed = (float*)(smem + LY::kRed);
+  float* sRedDen = (float*)(smem + LY::kRedDen);
+
+  const int span = blockIdx.x, bh = blockIdx.y;
+  const int head = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  float* sZ = (float*)(smem + LY::kZ) + w * 64;           // this wave's running z
+  const int nfb = a.M >> 5;
+  const size_t hoff = (size_t)bh * a.L * D;
+  const E* Qg = (const E*)a.q + hoff;
+  const E* Kg = (const E*)a.k + hoff;
+  const E* Vg = (const E*)a.v + hoff;
+  E* Og = (E*)a.o + hoff;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
+  const float half_ln_m = 0.5f * logf((float)a.M);
+  const int t0 = span * a.span_len;
+  const int t1 = min(a.L, t0 + a.span_len);
+  if (t0 >= t1) return;                                    // whole workgroup
+
+  // identity operand: slot j of k-step s2 of lane (n, hh) is 1 where feature
+  // crow(8 s2 + j, hh) of the block equals n
+  F ident[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned lo = crow(8 * s2 + 2 * k, hh) == l32 ? 0x3f80u : 0u;
+      const unsigned hi = crow(8 * s2 + 2 * k + 1, hh) == l32 ? 0x3f80u : 0u;
+      ident[s2][k] = lo | (hi << 16);
+    }
+
+  TileLoader<E, D, C, 256> lq, lk, lv;
+  auto load_chunk = [&](int c0) {
+    lq.load(Qg + (size_t)c0 * D, t1 - c0, tid);
+    lk.load(Kg + (size_t)c0 * D, t1 - c0, tid);
+    lv.load(Vg + (size_t)c0 * D, t1 - c0, tid);
+  };
+  auto store_chunk = [&](char* buf, int nv) {
+    lq.store_proj(buf + LY::kQh, tid);
+    lk.store_proj(buf + LY::kKh, tid);
+    lv.store(buf + LY::kV, tid);
+    lq.row_bias((float*)(buf + LY::kBq), tid, nv, half_ln_m);
+    lk.row_bias((float*)(buf + LY::kBk), tid, nv, half_ln_m);
+  };
+  // V^T fragment (tb, s2, db): lane (d, hh) holds V[32 tb + crow(8 s2 + j, hh)][32 db + d]
+  auto vt_at = [&](const char* buf, int tb, int s2, int db) -> const char* {
+    return buf + LY::kVT + (((tb * 2 + s2) * 2 + hh) * D + db * 32 + l32) * 16;
+  };
+  auto transpose_v = [&](char* buf) {
+#pragma unroll
+    for (int q = w; q < NVT; q += 4) {
+      const int tb = q / (2 * NDB), s2 = (q / NDB) % 2, db = q % NDB;
+      const int row = tb * 32 + 16 * s2 + 4 * hh + ((lane & 15) >> 2);
+      const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      u32x2 r[2];
+      lds_read_tr16_1x2<0, 8 * RS>(lds_addr(buf + LY::kV + row * RS + col * 2), r);
+      *(u32x4*)vt_at(buf, tb, s2, db) = u32x4{r[0][0], r[0][1], r[1][0], r[1][1]};
+    }
+  };
+
+  for (int fg = 0; fg < a.fgroups; ++fg) {
+    const int fb0 = (fg * 4 + w) * FBW;
+    F wf[FBW][NKD];
+    f32x16 st[FBW][NDB];
+    float zreg[FBW];
+    const float* pre = a.prefix + ((size_t)bh * a.spans + span) * a.M * D;
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) {
+      const bool ok = fb0 + i < nfb;
+      const int fbase = (ok ? fb0 + i : 0) * 32;
+      const float* wrow = wh + (size_t)(fbase + l32) * D;
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D>(wrow, hh, s, ok);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st[i][db][r] = ok ? pre[(size_t)(fbase + crow(r, hh)) * D + db * 32 + l32] : 0.f;
+      zreg[i] = ok ? a.prefixz[((size_t)bh * a.spans + span) * a.M + fbase + l32] : 0.f;
+    }
+
+    // prologue: chunk 0 into buffer 0 with its V^T, chunk 1 in registers
+    load_chunk(t0);
+    __syncthreads();                                     // previous feature group fully done
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) sZ[i * 32 + l32] = zreg[i];
+    store_chunk(smem, min(C, t1 - t0));
+    if (t0 + C < t1) load_chunk(t0 + C);
+    wait_lgkm0();
+    raw_barrier();
+    transpose_v(smem);
+
+    int c = 0;
+    for (int c0 = t0; c0 < t1; c0 += C, ++c) {
+      const int nv = min(C, t1 - c0);
+      char* cur = smem + (c & 1) * LY::BUF;
+      char* nxt = smem + ((c + 1) & 1) * LY::BUF;
+      wait_lgkm0();
+      raw_barrier();                                     // chunk c staged everywhere; last reduction read
+      if (c0 + C < t1) {
+        store_chunk(nxt, min(C, t1 - c0 - C));
+        if (c0 + 2 * C < t1) load_chunk(c0 + 2 * C);
+      }
+
+      // ---- feature maps of this wave's features, lane = token -------------
+      F pq[FBW][NTB][2], pk[FBW][NTB][2];
+      const float* sBq = (const float*)(cur + LY::kBq);
+      const float* sBk = (const float*)(cur + LY::kBk);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        F qf[NKD], kf[NKD];
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) {
+          qf[s] = row_frag<Tr, D>(cur + LY::kQh + (tb * 32 + l32) * RS, hh, s);
+          kf[s] = row_frag<Tr, D>(cur + LY::kKh + (tb * 32 + l32) * RS, hh, s);
+        }
+        const float bq0 = sBq[tb * 32 + l32], bk0 = sBk[tb * 32 + l32];
+#pragma unroll
+        for (int i = 0; i < FBW; ++i) {
+          const bool fvalid = fb0 + i < nfb;
+          const float bq = fvalid ? bq0 : -INFINITY, bk = fvalid ? bk0 : -INFINITY;
+          f32x16 aq = zero16(), ak = zero16();
+#pragma unroll
+          for (int s = 0; s < NKD; ++s) {
+            aq = Tr::pmma(wf[i][s], qf[s], aq);          // P^T[f][t]
+            ak = Tr::pmma(wf[i][s], kf[s], ak);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            aq[r] = exp2_fast(aq[r] + bq);
+            ak[r] = exp2_fast(ak[r] + bk);
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            pq[i][tb][s2] = CFrag<Tr>::make(aq, s2);
+            pk[i][tb][s2] = CFrag<Tr>::make(ak, s2);
+          }
+        }
+      }
+
+      // ---- numerators per 32-query block: intra-chunk scores, then phi(Q) S
+#pragma unroll
+      for (int tqb = 0; tqb < NTB; ++tqb) {
+        f32x16 nacc[NDB];
+        float dacc = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) nacc[db] = zero16();
+#pragma unroll
+        for (int tkb = 0; tkb <= tqb; ++tkb) {
+          f32x16 at = zero16();                          // A^T[tk][tq] over this wave's features
+#pragma unroll
+          for (int i = 0; i < FBW; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) at = Tr::mma(pk[i][tkb][s2], pq[i][tqb][s2], at);
+          if (tkb == tqb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (crow(r, hh) > l32) at[r] = 0.f;        // key after query
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const F af = CFrag<Tr>::make(at, s2);        // B operand: lane = tq, k = tk (c-row)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dacc = dot2_bf16(af[j], 0x3f803f80u, dacc);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) nacc[db] = Tr::mma(*(const F*)vt_at(cur, tkb, s2, db), af, nacc[db]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FBW; ++i) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const f32x4 za = *(const f32x4*)(sZ + i * 32 + 16 * s2 + 4 * hh);
+            const f32x4 zb = *(const f32x4*)(sZ + i * 32 + 16 * s2 + 8 + 4 * hh);
+            const unsigned zz[4] = {pack_bf16(za[0], za[1]), pack_bf16(za[2], za[3]), pack_bf16(zb[0], zb[1]),
+                                    pack_bf16(zb[2], zb[3])};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              nacc[db] = Tr::mma(CFrag<Tr>::make(st[i][db], s2), pq[i][tqb][s2], nacc[db]);   // S^T phi(Q)^T
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dacc = dot2_bf16(pq[i][tqb][s2][k], zz[k], dacc);
+          }
+        }
+        // this wave's partial numerators and denominators of the block
+        float* rrow = sRed + (size_t)w * C * (RSR / 4) + (tqb * 32 + l32) * (RSR / 4);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v4 = {nacc[db][4 * g], nacc[db][4 * g + 1], nacc[db][4 * g + 2], nacc[db][4 * g + 3]};
+            *(f32x4*)(rrow + db * 32 + 8 * g + 4 * hh) = v4;
+          }
+        const float dsum = half_sum(dacc);
+        if (hh == 0) sRedDen[w * C + tqb * 32 + l32] = dsum;
+      }
+
+      // ---- state update: S += phi(K)^T V, z += phi(K)^T 1 ------------------
+#pragma unroll
+      for (int i = 0; i < FBW; ++i) {
+        float zc = 0.f;
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          f32x16 kt = zero16();                          // phi(K) block, lane = feature
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) kt = Tr::mma(pk[i][tb][s2], ident[s2], kt);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const F ktf = CFrag<Tr>::make(kt, s2);       // A operand: lane = f, k = t (c-row)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zc = dot2_bf16(ktf[j], 0x3f803f80u, zc);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) st[i][db] = Tr::mma(ktf, *(const F*)vt_at(cur, tb, s2, db), st[i][db]);
+          }
+        }
+        zc = half_sum(zc);
+        zreg[i] += zc;
+      }
+      // z for the next chunk (wave-private; LDS keeps this wave's order)
+#pragma unroll
+      for (int i = 0; i < FBW; ++i)
+        if (hh == 0) sZ[i * 32 + l32] = zreg[i];
+
+      wait_lgkm0();
+      raw_barrier();                                     // partials complete
+      {
+        constexpr int TPR = 256 / C;                     // threads per output row
+        constexpr int DP = D / TPR;                      // outputs per thread
+        const int tq = tid / TPR, d0 = (tid % TPR) * DP;
+        float acc[DP];
+#pragma unroll
+        for (int j = 0; j < DP; ++j) acc[j] = 0.f;
+        float dsum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float* rrow = sRed + (size_t)ww * C * (RSR / 4) + tq * (RSR / 4) + d0;
+#pragma unroll
+          for (int j = 0; j < DP; j += 4) {
+            f32x4 v4 = *(const f32x4*)(rrow + j);
+            acc[j] += v4[0];
+            acc[j + 1] += v4[1];
+            acc[j + 2] += v4[2];
+            acc[j + 3] += v4[3];
+          }
+          dsum += sRedDen[ww * C + tq];
+        }
+        const int tok = c0 + tq;
+        if (tq < nv) {
+          const size_t oi = (size_t)tok * D + d0;
+          if (a.fgroups > 1) {
+            if (fg > 0) {
+#pragma unroll
+              for (int j = 0; j < DP; ++j) acc[j] += a.num[hoff + oi + j];
+              dsum += a.den[(size_t)bh * a.L + tok];
+            }
+            if (fg + 1 < a.fgroups) {
+#pragma unroll
+              for (int j = 0; j < DP; ++j) a.num[hoff + oi + j] = acc[j];
+              if ((tid % TPR) == 0) a.den[(size_t)bh * a.L + tok] = dsum;
+            }
+          }
+          if (fg + 1 == a.fgroups) {
+            const float inv = 1.0f / (dsum + a.eps);
+            if constexpr (DP % 8 == 0) {
+#pragma unroll
+              for (int j = 0; j < DP; j += 8)
+                *(u32x4*)(Og + oi + j) = u32x4{pack_bf16(acc[j] * inv, acc[j + 1] * inv),
+                                               pack_bf16(acc[j + 2] * inv, acc[j + 3] * inv),
+                                               pack_bf16(acc[j + 4] * inv, acc[j + 5] * inv),
+                                               pack_bf16(acc[j + 6] * inv, acc[j + 7] * inv)};
+            } else {
+#pragma unroll
+              for (int j = 0; j < DP; ++j) Og[oi + j] = (E)(acc[j] * inv);
+            }
+          }
+        }
+      }
+      if (c0 + C < t1) transpose_v(nxt);
+    }
+  }
+}
+
 template <class Tr, int D, int FBW>
 static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
   using LY = CausalLds<Tr, D, FBW>;
@@ -418,6 +741,20 @@ static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
                p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
   hipLaunchKernelGGL((k_causal<Tr, D, FBW>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
+  timing_end(FAVOR_KERNEL_CAUSAL, s);
+  return hipGetLastError();
+}
+
+template <int D, int FBW, int C>
+static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
+  using LY = CausalLds2<D, C>;
+  float* part = (float*)(t.ws + p.off_part);
+  float* partz = (float*)(t.ws + p.off_partz);
+  if (p.fbw != FBW) return hipErrorInvalidValue;
+  CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
+               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps};
+  timing_begin(FAVOR_KERNEL_CAUSAL, s);
+  hipLaunchKernelGGL((k_causal2<D, FBW, C>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
   timing_end(FAVOR_KERNEL_CAUSAL, s);
   return hipGetLastError();
 }
@@ -436,8 +773,8 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
-      case 32: return causal_t<TrBF16, 32, 2>(p, t, s);
-      case 64: return causal_t<TrBF16, 64, 2>(p, t, s);
+      case 32: return causal2_t<32, 2, 32>(p, t, s);
+      case 64: return causal2_t<64, 2, 32>(p, t, s);
       case 128: return causal_t<TrBF16, 128, 1>(p, t, s);
     }
   } else {

@@ -138,6 +138,17 @@ __device__ __forceinline__ void lds_read_tr16_1x4(unsigned a0, u32x2 (&r)[4]) {
       : "memory");
 }
 
+template <int O0, int O1>
+__device__ __forceinline__ void lds_read_tr16_1x2(unsigned a0, u32x2 (&r)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(a0), "n"(O0), "n"(O1)
+      : "memory");
+}
+
 __device__ __forceinline__ void lds_read_tr16_x8(const void* const p[8], u32x2 (&r)[8]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8\n\t"
@@ -216,6 +227,25 @@ template <> struct CFrag<TrBF16> {
 template <> struct CFrag<TrF32> {
   static __device__ __forceinline__ float make(const f32x16& v, int s) { return v[s]; }
 };
+
+// x summed over aligned groups of G consecutive lanes (G a power of two up
+// to 32): DPP lane permutations within rows of 16, a shuffle beyond.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G >= 1 && G <= 32 && (G & (G - 1)) == 0, "group size");
+  if constexpr (G >= 2) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));   // lanes ^ 1
+  if constexpr (G >= 4) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));   // lanes ^ 2
+  if constexpr (G >= 8) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));  // mirror in 8
+  if constexpr (G >= 16) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)); // mirror in 16
+  if constexpr (G >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+// x plus its value in the lane 32 apart (both wave halves get the sum)
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  const unsigned r0 = r[0], r1 = r[1];   // by value: a bit cast of a vector element reads element 0
+  return as_f32(r0) + as_f32(r1);
+}
 
 // Zero accumulator.
 __device__ __forceinline__ f32x16 zero16() {

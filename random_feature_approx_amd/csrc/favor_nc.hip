@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_features(FeatArgs a) {
       ss = fmaf(v, v, ss);
     }
   }
-  ss += __shfl_xor(ss, 32);
+  ss = half_sum(ss);
   const float bias = -(0.5f * ss + 0.5f * logf((float)a.M)) * kLog2e;
   float* out = a.phi + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * a.M;
   for (int fb = 0; fb < (a.M >> 5); ++fb) {
@@ -222,8 +222,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
         }
       }
       *(u32x4*)(sKh + prep_dst[i]) = v;
-#pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+      ss = group_sum<CPR>(ss);
       if (prep_lead) sBias[prep_row[i]] = prep_row[i] < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
     }
     wait_lgkm0();
@@ -305,7 +304,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) P[(size_t)(f0 + crow(r, hh)) * D + db * 32 + l32] = st[i][db][r];
-      float z = zs[i] + __shfl_xor(zs[i], 32);
+      float z = half_sum(zs[i]);
       if (hh == 0) Pz[f0 + l32] = z;
     }
   }
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
           ss = fmaf(qraw[tb][s], qraw[tb][s], ss);
         }
       }
-      ss += __shfl_xor(ss, 32);
+      ss = half_sum(ss);
       bias[tb] = -(0.5f * ss + half_ln_m) * kLog2e;
     }
 
@@ -615,7 +614,7 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int tok = tbase + tb * 32 + l32;
-      const float inv = 1.0f / (den[tb] + __shfl_xor(den[tb], 32) + a.eps);
+      const float inv = 1.0f / (half_sum(den[tb]) + a.eps);
       if (tok < a.L) {
         E* orow = O + (size_t)tok * D;
 #pragma unroll

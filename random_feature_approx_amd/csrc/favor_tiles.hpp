@@ -74,8 +74,7 @@ struct TileLoader {
           ss = fmaf(a, a, ss);
         }
       }
-#pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+      ss = group_sum<CPR>(ss);
       int row = c / CPR;
       if (c < TT * CPR && (c % CPR) == 0)
         sb[row] = row < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
@@ -329,8 +328,7 @@ __device__ __forceinline__ void prep_proj_tile(const char* raw, char* out, float
       }
     }
     *(u32x4*)(out + r * RS + cc * 16) = v;
-#pragma unroll
-    for (int o = 1; o < CPR; o <<= 1) ss += __shfl_xor(ss, o);
+    ss = group_sum<CPR>(ss);
     if (cc == 0) bias[r] = r < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
   }
 }
