@@ -550,10 +550,10 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
       char* nxt = smem + ((c + 1) & 1) * LY::BUF;
       wait_lgkm0();
       raw_barrier();                                     // chunk c staged everywhere; last reduction read
-      if (c0 + C < t1) {
-        store_chunk(nxt, min(C, t1 - c0 - C));
-        if (c0 + 2 * C < t1) load_chunk(c0 + 2 * C);
-      }
+      // branch-free so that the whole chunk is one scheduling region: past
+      // the end the staged rows are zero and no row is loaded
+      store_chunk(nxt, min(C, t1 - c0 - C));
+      load_chunk(c0 + 2 * C);
 
       // ---- feature maps of this wave's features, lane = token -------------
       F pq[FBW][NTB][2], pk[FBW][NTB][2];
@@ -643,8 +643,7 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
             f32x4 v4 = {nacc[db][4 * g], nacc[db][4 * g + 1], nacc[db][4 * g + 2], nacc[db][4 * g + 3]};
             *(f32x4*)(rrow + db * 32 + 8 * g + 4 * hh) = v4;
           }
-        const float dsum = half_sum(dacc);
-        if (hh == 0) sRedDen[w * C + tqb * 32 + l32] = dsum;
+        sRedDen[w * C + tqb * 32 + l32] = half_sum(dacc);   // both halves write the same value
       }
 
       // ---- state update: S += phi(K)^T V, z += phi(K)^T 1 ------------------
@@ -668,10 +667,10 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
         zc = half_sum(zc);
         zreg[i] += zc;
       }
-      // z for the next chunk (wave-private; LDS keeps this wave's order)
+      // z for the next chunk (wave-private; LDS keeps this wave's order; both
+      // halves hold the same value)
 #pragma unroll
-      for (int i = 0; i < FBW; ++i)
-        if (hh == 0) sZ[i * 32 + l32] = zreg[i];
+      for (int i = 0; i < FBW; ++i) sZ[i * 32 + l32] = zreg[i];
 
       wait_lgkm0();
       raw_barrier();                                     // partials complete

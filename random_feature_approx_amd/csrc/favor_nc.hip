@@ -95,28 +95,36 @@ struct RedArgs {
   int L, M, H, Hw, splits, split_len;
 };
 
-// Pipeline shape of the K-side kernels: tiles of TT tokens, STAGES tiles of
-// K and V resident in LDS.
+// Pipeline shape of the K-side kernels: tiles of TT tokens copied into a
+// ring of STAGES raw K|V tiles; each tile is prepared once (K in the
+// projection type with its row biases, and for bf16 V rearranged into
+// operand order V^T) into one of two prepared buffers.
 template <class Tr, int D, int NT>
 struct RedLds {
   using E = typename Tr::elem;
+  static constexpr bool kVT = Tr::VPS == 8;
   static constexpr int ROWB = D * (int)sizeof(E);
   // 32 tokens for long rows; otherwise 64, or enough rows to give every
   // thread one 16-byte chunk
   static constexpr int TT = ROWB >= 256 ? 32 : (NT * 16 / ROWB > 64 ? NT * 16 / ROWB : 64);
   using DT = DmaTile<E, D, TT, NT>;
   static constexpr int PAIR = 2 * DT::BYTES;
-  static constexpr int STAGES = 65536 / PAIR >= 4 ? 4 : (65536 / PAIR >= 3 ? 3 : 2);
+  // tile t+2 is copied while tile t is computed: with V^T the raw slot of
+  // tile t is free by then (two slots), otherwise V is read raw (three)
+  static constexpr int STAGES = kVT ? 2 : 3;
   static constexpr int RS = Rows<D, sizeof(E)>::RS;
-  static constexpr int kRing = 0;                       // [STAGES][K tile | V tile]
-  static constexpr int kKh = STAGES * PAIR;             // converted K, padded rows
-  static constexpr int kBias = kKh + TT * RS;
-  static constexpr int kTotal = kBias + TT * 4;
+  static constexpr int kKh = 0;                          // converted K, padded rows
+  static constexpr int kV = kKh + TT * RS;               // V^T (bf16)
+  static constexpr int kBias = kV + (kVT ? TT * D * 2 : 0);
+  static constexpr int PREP = kBias + TT * 4;
+  static constexpr int kRing = 2 * PREP;                 // [STAGES][K tile | V tile]
+  static constexpr int kTotal = kRing + STAGES * PAIR;
 };
 
-// NW waves per workgroup, each owning one block of 32 features: many
-// independent waves per SIMD let the matrix cores and the exponentials of
-// different waves overlap.
+// NW waves per workgroup, each owning one block of 32 features.  One barrier
+// per tile: after it, tile t+2 is copied, tile t+1 is prepared and tile t is
+// computed from its prepared buffer, so the copies, the preparation (LDS and
+// a little VALU work) and the matrix products of different tiles overlap.
 template <class Tr, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
   constexpr int FBW = 1;
@@ -130,9 +138,10 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
   constexpr int NDB = D / 32;               // 32-wide d blocks
   constexpr int NKT = 32 / Tr::KS;          // k-steps over a 32-token block
   constexpr int RS = LY::RS;
+  constexpr int ES = (int)sizeof(E);
+  constexpr int CPR = DT::CPR;
+  constexpr int NVT = (TT / 32) * 2 * NDB;  // V^T fragments per tile (bf16)
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* sKh = smem + LY::kKh;
-  float* sBias = (float*)(smem + LY::kBias);
 
   const int split = blockIdx.x, fg = blockIdx.y, bh = blockIdx.z;
   const int head = bh % a.H;
@@ -165,49 +174,37 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
   const int t1 = min(a.L, t0 + a.split_len);
   const int ntiles = t0 < t1 ? (t1 - t0 + TT - 1) / TT : 0;
 
-  // ---- per-lane constants (tile-invariant addressing) ----------------------
-  constexpr int ES = (int)sizeof(E);
-  constexpr int ROWB = DT::ROWB, CPR = DT::CPR, SWZ = DT::SWZ;
   const typename DT::Lane dplan = DT::lane_plan(w, lane);
-  int prep_src[DT::NI], prep_dst[DT::NI], prep_row[DT::NI];
-#pragma unroll
-  for (int i = 0; i < DT::NI; ++i) {
-    const int c = tid + i * NT;
-    const int r = c / CPR, cc = c % CPR;
-    prep_src[i] = r * ROWB + ((cc ^ (r & SWZ)) << 4);
-    prep_dst[i] = r * RS + cc * 16;
-    prep_row[i] = r;
-  }
-  const bool prep_lead = (tid % CPR) == 0;
-  const int kf_base = l32 * RS + (D / 2) * hh * ES;
-  // transposed V reads: rows 4hh + i16/4 (+16 s, +8, +32 tb), column 32 db + 16 g + 4 (i16 & 3)
-  int tr_base[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    tr_base[db] = DT::at(4 * hh + ((lane & 15) >> 2), db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-
+  auto ring = [&](int tt) -> char* { return smem + LY::kRing + (tt % S) * LY::PAIR; };
+  auto prep_buf = [&](int tt) -> char* { return smem + (tt & 1) * LY::PREP; };
   auto issue = [&](int tt) {
-    char* slot = smem + LY::kRing + (tt % S) * LY::PAIR;
+    char* slot = ring(tt);
     const int r0 = t0 + tt * TT;
     DT::issue_plan(slot, (const char*)(K + (size_t)r0 * D), t1 - r0, dplan, w);
     DT::issue_plan(slot + DT::BYTES, (const char*)(V + (size_t)r0 * D), t1 - r0, dplan, w);
   };
-  for (int tt = 0; tt < S - 1 && tt < ntiles; ++tt) issue(tt);
-  // the projection rows of W (loaded before the copies) are complete once at
-  // most the copies are outstanding
-  wait_vmcnt_steps<2 * DT::NI, S - 1>(min(ntiles, S - 1));
-
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int issued = min(ntiles, tt + S - 1);
-    wait_vmcnt_steps<2 * DT::NI, S - 2>(issued - tt - 1);
-    raw_barrier();                            // tile tt landed everywhere; tile tt-1 fully consumed
-    if (tt + S - 1 < ntiles) issue(tt + S - 1);
-    const char* slot = smem + LY::kRing + (tt % S) * LY::PAIR;
-    const int nvalid = min(TT, t1 - (t0 + tt * TT));
-    // ---- stage K: projection operand type, row norms -> bias -------------
+  // preparation of a tile, in two halves around the products of the
+  // previous one: read the raw K chunks; then convert them to the projection
+  // type with row biases (-inf past the end) and rearrange V into V^T
+  u32x4 kraw[DT::NI];
+  auto prep_read = [&](int tt) {
+    const char* raw = ring(tt);
 #pragma unroll
     for (int i = 0; i < DT::NI; ++i) {
-      u32x4 v = *(const u32x4*)(slot + prep_src[i]);
+      const int c = tid + i * NT;
+      kraw[i] = DT::chunk(raw, c / CPR, c % CPR);
+    }
+  };
+  auto prep_write = [&](int tt) {
+    const char* raw = ring(tt);
+    char* pb = prep_buf(tt);
+    float* bias = (float*)(pb + LY::kBias);
+    const int nvalid = min(TT, t1 - (t0 + tt * TT));
+#pragma unroll
+    for (int i = 0; i < DT::NI; ++i) {
+      const int c = tid + i * NT;
+      const int r = c / CPR, cc = c % CPR;
+      u32x4 v = kraw[i];
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -221,65 +218,92 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
           ss = fmaf(x, x, ss);
         }
       }
-      *(u32x4*)(sKh + prep_dst[i]) = v;
+      *(u32x4*)(pb + LY::kKh + r * RS + cc * 16) = v;
       ss = group_sum<CPR>(ss);
-      if (prep_lead) sBias[prep_row[i]] = prep_row[i] < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
+      if (cc == 0) bias[r] = r < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
     }
-    wait_lgkm0();
-    raw_barrier();
-    const char* sV = slot + DT::BYTES;
+    if constexpr (LY::kVT) {
+      const char* rawv = raw + DT::BYTES;
 #pragma unroll
-    for (int tb = 0; tb < TT / 32; ++tb) {
+      for (int q = w; q < NVT; q += NW) {
+        const int tb = q / (2 * NDB), s2 = (q / NDB) % 2, db = q % NDB;
+        const int off = DT::at(tb * 32 + 16 * s2 + 4 * hh + ((lane & 15) >> 2),
+                               db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+        u32x2 r2[2];
+        lds_read_tr16_1x2<0, 8 * DT::ROWB>(lds_addr(rawv + off), r2);   // rows +8 keep the swizzle
+        *(u32x4*)(pb + LY::kV + (((tb * 2 + s2) * 2 + hh) * D + db * 32 + l32) * 16) =
+            u32x4{r2[0][0], r2[0][1], r2[1][0], r2[1][1]};
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    issue(0);
+    if (ntiles > 1) issue(1);
+    // W rows (loaded first) and tile 0 complete: at most tile 1 outstanding
+    wait_vmcnt_steps<2 * DT::NI, 1>(ntiles > 1 ? 1 : 0);
+    raw_barrier();
+    prep_read(0);
+    prep_write(0);
+  }
+  constexpr int NSUB = TT / 32;
+  for (int tt = 0; tt < ntiles; ++tt) {
+    wait_vmcnt<0>();                          // tile tt+1 landed (this wave's copies)
+    wait_lgkm0();                             // this wave's preparation of tile tt written
+    raw_barrier();                            // ... everywhere; tile tt-1 fully consumed
+    if (tt + 2 < ntiles) issue(tt + 2);
+    const bool more = tt + 1 < ntiles;
+    if (more) prep_read(tt + 1);
+    const char* pb = prep_buf(tt);
+    const float* sBias = (const float*)(pb + LY::kBias);
+    // projections of every 32-token block of the tile first, then their
+    // exponentials and contractions, so matrix and vector work interleave
+    f32x16 acc[FBW][NSUB];
+#pragma unroll
+    for (int tb = 0; tb < NSUB; ++tb) {
       F kf[NKD];
 #pragma unroll
-      for (int s = 0; s < NKD; ++s) kf[s] = *(const F*)(sKh + kf_base + tb * 32 * RS + s * Tr::VPS * ES);
-      F vf[NDB][NKT];
-      if constexpr (Tr::VPS == 8) {
-        // V shares LDS with copies still in flight: transposed reads issued
-        // from assembly, which wait only for themselves
-        const unsigned vbase = lds_addr(sV) + tb * 32 * ROWB;
-        if constexpr (NDB == 1) {
-          u32x2 r[4];
-          lds_read_tr16_1x4<0, 8 * ROWB, 16 * ROWB, 24 * ROWB>(vbase + tr_base[0], r);
-          vf[0][0] = u32x4{r[0][0], r[0][1], r[1][0], r[1][1]};
-          vf[0][1] = u32x4{r[2][0], r[2][1], r[3][0], r[3][1]};
-        } else {
+      for (int s = 0; s < NKD; ++s)
+        kf[s] = *(const F*)(pb + LY::kKh + (tb * 32 + l32) * RS + ((D / 2) * hh + Tr::VPS * s) * ES);
 #pragma unroll
-          for (int db = 0; db < NDB; db += 2) {
-            u32x2 r[8];
-            lds_read_tr16_2x4<0, 8 * ROWB, 16 * ROWB, 24 * ROWB>(vbase + tr_base[db], vbase + tr_base[db + 1], r);
+      for (int i = 0; i < FBW; ++i) {
+        // the accumulator starts at each token's bias, so the projection
+        // lands directly on the base-2 exponent
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              vf[db + j][0] = u32x4{r[4 * j][0], r[4 * j][1], r[4 * j + 1][0], r[4 * j + 1][1]};
-              vf[db + j][1] = u32x4{r[4 * j + 2][0], r[4 * j + 2][1], r[4 * j + 3][0], r[4 * j + 3][1]};
-            }
-          }
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 b4 = *(const f32x4*)(sBias + tb * 32 + 8 * g + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][tb][4 * g + j] = b4[j];
         }
-      } else {
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) acc[i][tb] = Tr::pmma(kf[s], wf[i][s], acc[i][tb]);   // P[t][f] + bias[t]
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < NSUB; ++tb) {
+      F vf[NDB][NKT];
+      if constexpr (LY::kVT) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int s2 = 0; s2 < NKT; ++s2) vf[db][s2] = col_frag_swz<Tr, DT>(sV, tb * 32, db * 32, s2, lane);
+          for (int s2 = 0; s2 < NKT; ++s2)
+            vf[db][s2] = *(const F*)(pb + LY::kV + (((tb * 2 + s2) * 2 + hh) * D + db * 32 + l32) * 16);
+      } else {
+        const char* rawv = ring(tt) + DT::BYTES;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) vf[db][s2] = col_frag_swz<Tr, DT>(rawv, tb * 32, db * 32, s2, lane);
       }
 #pragma unroll
       for (int i = 0; i < FBW; ++i) {
         if (fb0 + i < nfb) {
-          // the accumulator starts at each token's bias, so the projection
-          // lands directly on the base-2 exponent
-          f32x16 acc;
+          f32x16 e = acc[i][tb];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 b4 = *(const f32x4*)(sBias + tb * 32 + 8 * g + 4 * hh);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[4 * g + j] = b4[j];
-          }
-#pragma unroll
-          for (int s = 0; s < NKD; ++s) acc = Tr::pmma(kf[s], wf[i][s], acc);   // P[t][f] + bias[t], lane = f
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = exp2_fast(acc[r]);
+          for (int r = 0; r < 16; ++r) e[r] = exp2_fast(e[r]);
 #pragma unroll
           for (int s2 = 0; s2 < NKT; ++s2) {
-            F pf = CFrag<Tr>::make(acc, s2);
+            F pf = CFrag<Tr>::make(e, s2);
             if constexpr (Tr::VPS == 8) {
 #pragma unroll
               for (int j = 0; j < 4; ++j) zs[i] = dot2_bf16(pf[j], 0x3f803f80u, zs[i]);
@@ -292,6 +316,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
         }
       }
     }
+    if (more) prep_write(tt + 1);
   }
 
   float* P = a.part + ((size_t)bh * a.splits + split) * a.M * D;
