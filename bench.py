@@ -21,6 +21,7 @@ The JSON line also carries
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -35,6 +36,13 @@ PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks
 KERNEL_SOURCES = ["favor_device.hpp", "favor_tiles.hpp", "favor_nc.hip", "favor_causal.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def causal_chunk(wl) -> int:
+    """Tokens per chunk of the causal scan: the bf16 kernel for d <= 64 carries
+    the state every 32 tokens (its registers hold a 32-token chunk), the
+    other kernel every 64."""
+    return 32 if (wl.dtype == "bf16" and wl.d <= 64) else 64
 
 
 def log(msg: str) -> None:
@@ -147,6 +155,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long", choices=["t1", "encoder", "causal_lm", "long", "wide"])
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time budget per path (0 = skip)")
+    ap.add_argument("--paths", default="", help="comma-separated subset of the workload's paths to run "
+                                                "(default: all; used to attribute profiler counters to a path)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes 5 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -179,6 +189,13 @@ def main() -> int:
         print("no GPU visible", file=sys.stderr)
         return 1
     wl = synth.WORKLOADS[args.workload]
+    if args.paths:
+        keep = [p for p in args.paths.split(",") if p]
+        bad = [p for p in keep if p not in wl.paths]
+        if bad:
+            print(f"workload {wl.name} has no path {bad}", file=sys.stderr)
+            return 2
+        wl = dataclasses.replace(wl, paths=tuple(keep))
     log(f"workload {wl.name}: B={wl.B} H={wl.H} L={wl.L} d={wl.d} m={wl.m} {wl.dtype} paths={wl.paths}")
     x = synth.make_inputs(wl, with64=False)
     dev = torch.device("cuda", 0)
@@ -234,7 +251,7 @@ def main() -> int:
         if not durs:
             continue
         users = [p for p in wl.paths if kname in ("k_reduce",) or
-                 (kname in ("k_combine", "k_apply") and p == "noncausal") or
+                 (kname in ("k_wprep", "k_combine", "k_apply") and p == "noncausal") or
                  (kname in ("k_span_scan", "k_causal") and p == "causal")]
         for j, p in enumerate(users):
             mine = durs[j::len(users)]
@@ -274,7 +291,7 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} L={wl.L} d={wl.d} m={wl.m} {wl.dtype}, "
                                f"{' + '.join(wl.paths)} per step",
                    "B": wl.B, "H": wl.H, "L": wl.L, "d": wl.d, "m": wl.m, "paths": list(wl.paths),
-                   "chunk": wl.chunk, "eps": wl.eps},
+                   "chunk": causal_chunk(wl), "eps": wl.eps},
         "roofline": roof,
         "cpu_baseline": cpu,
         "paths": paths_report,

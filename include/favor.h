@@ -103,9 +103,10 @@ favor_status favor_attn_noncausal(const void* Q, const void* K, const void* V,
  * phi(k_j) v_j^T and z_i = sum_{j<=i} phi(k_j) (the diagonal included),
  * o_i = phi(q_i)^T S_i / (phi(q_i)^T z_i + eps).  The denominator is the
  * causal analogue of the non-causal one (the notes give the numerator
- * only).  Computed in chunks of 64 tokens: inside a chunk the masked
- * chunk-by-chunk score tile is multiplied by V; across chunks the m x d
- * state is carried as a prefix sum.  Deterministic as above.
+ * only).  Computed in chunks (32 tokens for bf16 with d <= 64, 64
+ * otherwise): inside a chunk the masked chunk-by-chunk score tile is
+ * multiplied by V; across chunks the m x d state is carried as a prefix
+ * sum.  Deterministic as above.
  */
 favor_status favor_attn_causal(const void* Q, const void* K, const void* V,
                                const float* W, int Hw, void* O,
