@@ -459,7 +459,8 @@ struct ApplyArgs {
   void* o;
   int L, M, H, Hw;
   float eps;
-  int groups_per_head, groups_total, steps, fch;
+  int groups_per_head, groups_total, steps, fch, nbuf;
+  int stage_off;        // LDS offset of the per-wave output staging areas
 };
 
 constexpr int kApplyWaves = 8;
@@ -478,6 +479,9 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
   using QRaw = typename std::conditional<QV, u32x4, float>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int FCH = a.fch;
+  // one buffer (W operand, M, z) per head in flight: with two, the next
+  // group's head is copied while the current group is computed
+  const int BUFB = FCH * D * WES + FCH * D * ES + FCH * ES;
   char* sW = smem;
   char* sM = sW + FCH * D * WES;
   char* sZ = sM + FCH * D * ES;
@@ -508,15 +512,22 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
     }
   };
   // all waves finished with the previous contents; copy; copies landed everywhere
-  auto reload = [&](int bh, int f0, int nf) {
+  auto issue_state = [&](char* buf, int bh, int f0, int nf) {
     const int head = bh % a.H;
+    char* w_ = buf;
+    char* m_ = w_ + FCH * D * WES;
+    char* z_ = m_ + FCH * D * ES;
+    dma_copy<NT>(w_, (const char*)a.wp + ((size_t)(a.Hw == 1 ? 0 : head) * a.M + f0) * D * WES, nf * D * WES / 16, tid);
+    dma_copy<NT>(m_, (const char*)a.mstate + ((size_t)bh * a.M + f0) * D * ES, nf * D * ES / 16, tid);
+    dma_copy<NT>(z_, (const char*)a.zstate + ((size_t)bh * a.M + f0) * ES, nf * ES / 16, tid);
+  };
+  auto reload = [&](int bh, int f0, int nf) {
     __syncthreads();
-    dma_copy<NT>(sW, (const char*)a.wp + ((size_t)(a.Hw == 1 ? 0 : head) * a.M + f0) * D * WES, nf * D * WES / 16, tid);
-    dma_copy<NT>(sM, (const char*)a.mstate + ((size_t)bh * a.M + f0) * D * ES, nf * D * ES / 16, tid);
-    dma_copy<NT>(sZ, (const char*)a.zstate + ((size_t)bh * a.M + f0) * ES, nf * ES / 16, tid);
+    issue_state(sW, bh, f0, nf);
     wait_vmcnt<0>();
     __syncthreads();
   };
+  int cb = 0, loaded0 = -1, loaded1 = -1;             // head held by each buffer
 
   QRaw qnext[TB][NKD];
   if (g0 < g1) load_q(g0, qnext);
@@ -524,7 +535,31 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
   for (int g = g0; g < g1; ++g) {
     const int bh = g / a.groups_per_head;
     const int tbase = (g % a.groups_per_head) * (NW * TB * 32) + w * TB * 32;
-    if (nch == 1 && bh != cur_bh) reload(bh, 0, a.M);
+    if (a.nbuf == 2) {
+      if ((cb == 0 ? loaded0 : loaded1) != bh) {
+        if ((cb == 0 ? loaded1 : loaded0) == bh) {
+          cb ^= 1;                                       // copied during the previous group
+          wait_vmcnt<0>();
+          __syncthreads();
+        } else {
+          reload(bh, 0, a.M);                            // (sW points at buffer cb)
+          if (cb == 0) loaded0 = bh; else loaded1 = bh;
+        }
+        sW = smem + cb * BUFB;
+        sM = sW + FCH * D * WES;
+        sZ = sM + FCH * D * ES;
+      }
+      if (g + 1 < g1) {
+        const int nbh = (g + 1) / a.groups_per_head;
+        if (nbh != bh && (cb == 0 ? loaded1 : loaded0) != nbh) {
+          // the other buffer was last read before a barrier every wave has passed
+          issue_state(smem + (cb ^ 1) * BUFB, nbh, 0, a.M);
+          if (cb == 0) loaded1 = nbh; else loaded0 = nbh;
+        }
+      }
+    } else if (nch == 1 && bh != cur_bh) {
+      reload(bh, 0, a.M);
+    }
     cur_bh = bh;
 
     QRaw qraw[TB][NKD];
@@ -571,7 +606,9 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
       const int f0 = ch * FCH;
       const int nf = min(FCH, a.M - f0);
       if (nch > 1) reload(bh, f0, nf);
-      for (int fb = 0; fb < (nf >> 5); ++fb) {
+      // two feature blocks per step: one scheduling region, so the projection
+      // of one block overlaps the exponentials of the other
+      auto do_fb = [&](const int fb) {
         F wfr[NKD];
         if constexpr (WES == 2) {
 #pragma unroll
@@ -632,31 +669,73 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
             }
           }
         }
+      };
+      const int nfbc = nf >> 5;
+      int fb = 0;
+      if constexpr (Tr::VPS == 8 || D <= 64) {           // registers allow it
+        for (; fb + 1 < nfbc; fb += 2) {
+          do_fb(fb);
+          do_fb(fb + 1);
+        }
       }
+      for (; fb < nfbc; ++fb) do_fb(fb);
     }
 
+    // Rows of at most 128 bytes go through this wave's LDS staging area so
+    // that every store instruction writes whole rows (8 lanes per row)
+    // instead of 16 bytes in each of 32 rows; longer rows are stored directly.
     E* O = (E*)a.o + (size_t)bh * a.L * D;
+    constexpr bool kStage = D * ES <= 128;
+    constexpr int RSO = D * ES + 16;
+    constexpr int CPRO = D * ES / 16;
+    char* stage = smem + a.stage_off + w * 32 * RSO;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const int tok = tbase + tb * 32 + l32;
-      const float inv = 1.0f / (half_sum(den[tb]) + a.eps);
-      if (tok < a.L) {
-        E* orow = O + (size_t)tok * D;
+      if constexpr (!kStage) {
+        const int tok = tbase + tb * 32 + l32;
+        const float inv = 1.0f / (half_sum(den[tb]) + a.eps);
+        if (tok < a.L) {
+          E* orow = O + (size_t)tok * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d0 = db * 32 + 8 * i + 4 * hh;
-            if constexpr (ES == 2) {
-              u32x2 pk = {pack_bf16(oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv),
-                          pack_bf16(oacc[tb][db][4 * i + 2] * inv, oacc[tb][db][4 * i + 3] * inv)};
-              *(u32x2*)(orow + d0) = pk;
-            } else {
-              f32x4 v = {oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv, oacc[tb][db][4 * i + 2] * inv,
-                         oacc[tb][db][4 * i + 3] * inv};
-              *(f32x4*)(orow + d0) = v;
+            for (int i = 0; i < 4; ++i) {
+              const int d0 = db * 32 + 8 * i + 4 * hh;
+              if constexpr (ES == 2) {
+                u32x2 pk = {pack_bf16(oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv),
+                            pack_bf16(oacc[tb][db][4 * i + 2] * inv, oacc[tb][db][4 * i + 3] * inv)};
+                *(u32x2*)(orow + d0) = pk;
+              } else {
+                f32x4 v = {oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv, oacc[tb][db][4 * i + 2] * inv,
+                           oacc[tb][db][4 * i + 3] * inv};
+                *(f32x4*)(orow + d0) = v;
+              }
             }
+        }
+        continue;
+      }
+      const float inv = 1.0f / (half_sum(den[tb]) + a.eps);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = db * 32 + 8 * i + 4 * hh;
+          if constexpr (ES == 2) {
+            u32x2 pk = {pack_bf16(oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv),
+                        pack_bf16(oacc[tb][db][4 * i + 2] * inv, oacc[tb][db][4 * i + 3] * inv)};
+            *(u32x2*)(stage + l32 * RSO + d0 * ES) = pk;
+          } else {
+            f32x4 v = {oacc[tb][db][4 * i] * inv, oacc[tb][db][4 * i + 1] * inv, oacc[tb][db][4 * i + 2] * inv,
+                       oacc[tb][db][4 * i + 3] * inv};
+            *(f32x4*)(stage + l32 * RSO + d0 * ES) = v;
           }
+        }
+#pragma unroll
+      for (int k = 0; k < 32 * CPRO / 64; ++k) {
+        const int c = k * 64 + lane, row = c / CPRO, cc = c % CPRO;
+        const u32x4 v = *(const u32x4*)(stage + row * RSO + cc * 16);
+        const int tok = tbase + tb * 32 + row;
+        if (tok < a.L) *(u32x4*)((char*)(O + (size_t)tok * D) + cc * 16) = v;
       }
     }
   }
@@ -733,9 +812,14 @@ static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const
   const int gsz = kApplyWaves * TB * 32;
   const int gph = (p.L + gsz - 1) / gsz;
   const int total = p.BH * gph;
-  ApplyArgs a{t.q, wp, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch};
+  const size_t buf = (size_t)p.fch * D * WES + (size_t)p.fch * D * sizeof(E) + (size_t)p.fch * sizeof(E);
+  const size_t stage = D * sizeof(E) <= 128 ? (size_t)kApplyWaves * 32 * (D * sizeof(E) + 16) : 0;
+  const int nbuf = (p.fch >= p.M && 2 * buf + stage <= 150 * 1024) ? 2 : 1;
+  const size_t stage_off = (nbuf * buf + 15) / 16 * 16;
+  ApplyArgs a{t.q, wp, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch, nbuf,
+              (int)stage_off};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
-  const size_t lds = (size_t)p.fch * D * WES + (size_t)p.fch * D * sizeof(E) + (size_t)p.fch * sizeof(E);
+  const size_t lds = stage_off + stage;
   if (TB * 32 != p.apply_tile) return hipErrorInvalidValue;
   timing_begin(FAVOR_KERNEL_APPLY, s);
   hipLaunchKernelGGL((k_apply<Tr, D, TB>), dim3(nblk), dim3(kApplyWaves * 64), lds, s, a);
