@@ -262,7 +262,7 @@ def main() -> int:
         if not durs:
             continue
         users = [p for p in wl.paths if kname in ("k_reduce",) or
-                 (kname in ("k_wprep", "k_combine", "k_apply") and p == "noncausal") or
+                 (kname in ("k_combine", "k_apply") and p == "noncausal") or
                  (kname in ("k_span_scan", "k_causal") and p == "causal")]
         for j, p in enumerate(users):
             mine = durs[j::len(users)]

@@ -134,12 +134,11 @@ favor_status favor_attn(const void* Q, const void* K, const void* V,
 typedef enum {
   FAVOR_KERNEL_FEATURES = 0,   /* fused feature map (favor_features)            */
   FAVOR_KERNEL_REDUCE = 1,     /* K-side state reduction / causal span totals    */
-  FAVOR_KERNEL_COMBINE = 2,    /* non-causal fixed-order combine of the partials */
+  FAVOR_KERNEL_COMBINE = 2,    /* non-causal combine of the partials + W operand */
   FAVOR_KERNEL_APPLY = 3,      /* non-causal Q-side apply                         */
   FAVOR_KERNEL_SPAN_SCAN = 4,  /* causal exclusive prefix over spans              */
   FAVOR_KERNEL_CAUSAL = 5,     /* causal chunked scan                             */
-  FAVOR_KERNEL_WPREP = 6,      /* projection operand (W log2 e, operand order)    */
-  FAVOR_KERNEL_COUNT = 7
+  FAVOR_KERNEL_COUNT = 6
 } favor_kernel;
 
 favor_status favor_timing_start(favor_kernel k, int capacity);

@@ -29,8 +29,7 @@ _lib = None
 STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid shape", 3: "unsupported d, m or dtype",
           4: "workspace missing or too small", 5: "HIP runtime error", 6: "internal error"}
 F32, BF16 = 0, 1
-KERNELS = {"k_features": 0, "k_reduce": 1, "k_combine": 2, "k_apply": 3, "k_span_scan": 4, "k_causal": 5,
-           "k_wprep": 6}
+KERNELS = {"k_features": 0, "k_reduce": 1, "k_combine": 2, "k_apply": 3, "k_span_scan": 4, "k_causal": 5}
 
 
 class FavorError(RuntimeError):

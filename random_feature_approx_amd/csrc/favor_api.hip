@@ -237,7 +237,6 @@ const char* favor_kernel_name(favor_kernel k) {
     case FAVOR_KERNEL_APPLY: return "k_apply";
     case FAVOR_KERNEL_SPAN_SCAN: return "k_span_scan";
     case FAVOR_KERNEL_CAUSAL: return "k_causal";
-    case FAVOR_KERNEL_WPREP: return "k_wprep";
     default: return "unknown";
   }
 }

@@ -51,7 +51,6 @@ struct Tensors {
 void timing_begin(favor_kernel k, hipStream_t s);
 void timing_end(favor_kernel k, hipStream_t s);
 
-hipError_t launch_wprep(const Plan& p, const float* w, void* out, hipStream_t s);
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);

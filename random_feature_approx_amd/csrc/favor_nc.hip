@@ -365,11 +365,41 @@ struct OperandOrder {
 constexpr int kSplitGroups = 8;
 constexpr int kQuadsPerBlock = 256 / kSplitGroups;
 
+// Projection operand for the apply: W log2(e) in the operand type of the
+// projection (fp16 for bf16 inputs, float otherwise), in operand order
+// [Hw*M/32 feature blocks][NKG][half h][feature f][16 bytes]: the 16 bytes of
+// lane (f, h) at k-group g hold d = (D/2) h + (16/WES) g + 0.. (the d-major
+// k order of the projection), so a wave reads 1 KB of contiguous memory.
+template <class E>
+__device__ __forceinline__ void wprep_chunk(const float* w, void* out, int idx, int D) {
+  constexpr int WES = sizeof(E);
+  constexpr int PER = 16 / WES;                      // d values per 16 bytes
+  const int nkg = D * WES / 32;
+  const int f = idx & 31, h = (idx >> 5) & 1, rest = idx >> 6;
+  const int g = rest % nkg, blk = rest / nkg;
+  const float* src = w + (size_t)(blk * 32 + f) * D + (D / 2) * h + PER * g;
+  if constexpr (WES == 2) {
+    const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+    u32x4 v = {pack_f16(x0[0] * kLog2e, x0[1] * kLog2e), pack_f16(x0[2] * kLog2e, x0[3] * kLog2e),
+               pack_f16(x1[0] * kLog2e, x1[1] * kLog2e), pack_f16(x1[2] * kLog2e, x1[3] * kLog2e)};
+    ((u32x4*)out)[idx] = v;
+  } else {
+    ((f32x4*)out)[idx] = *(const f32x4*)src * kLog2e;
+  }
+}
+
+// grid.y = BH + 1: slices 0..BH-1 combine a head's partial states, the last
+// slice prepares the projection operand from W (n16w 16-byte chunks).
 template <class E>
 __global__ __launch_bounds__(256) void k_combine(const float* part, const float* partz, E* mstate, E* zstate,
-                                                 int splits, int M, int D) {
+                                                 int splits, int M, int D, int BH, const float* w, void* wp,
+                                                 int n16w) {
   __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
   const int bh = blockIdx.y;
+  if (bh == BH) {
+    for (int idx = blockIdx.x * 256 + threadIdx.x; idx < n16w; idx += gridDim.x * 256) wprep_chunk<E>(w, wp, idx, D);
+    return;
+  }
   const int g = threadIdx.x / kQuadsPerBlock, qi = threadIdx.x % kQuadsPerBlock;
   const int quad = blockIdx.x * kQuadsPerBlock + qi;
   const int md4 = M * D / 4, nq = md4 + M / 4;
@@ -415,33 +445,6 @@ __global__ __launch_bounds__(256) void k_combine(const float* part, const float*
 }
 
 // ===========================================================================
-// Projection operand: W log2(e) in the operand type of the projection (fp16
-// for bf16 inputs, float otherwise), in operand order
-// [Hw*M/32 feature blocks][NKG][half h][feature f][16 bytes]: the 16 bytes of
-// lane (f, h) at k-group g hold d = (D/2) h + (16/WES) g + 0.. (the d-major
-// k order of the projection), so a wave reads 1 KB of contiguous memory.
-// ===========================================================================
-template <class Tr, int D>
-__global__ __launch_bounds__(256) void k_wprep(const float* w, void* out, int n16) {
-  constexpr int WES = Tr::VPS == 8 ? 2 : 4;
-  constexpr int NKG = D * WES / 32;
-  constexpr int PER = 16 / WES;                      // d values per 16 bytes
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n16) return;
-  const int f = idx & 31, h = (idx >> 5) & 1, rest = idx >> 6;
-  const int g = rest % NKG, blk = rest / NKG;
-  const float* src = w + (size_t)(blk * 32 + f) * D + (D / 2) * h + PER * g;
-  if constexpr (WES == 2) {
-    const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
-    u32x4 v = {pack_f16(x0[0] * kLog2e, x0[1] * kLog2e), pack_f16(x0[2] * kLog2e, x0[3] * kLog2e),
-               pack_f16(x1[0] * kLog2e, x1[1] * kLog2e), pack_f16(x1[2] * kLog2e, x1[3] * kLog2e)};
-    ((u32x4*)out)[idx] = v;
-  } else {
-    ((f32x4*)out)[idx] = *(const f32x4*)src * kLog2e;
-  }
-}
-
-// ===========================================================================
 // Q-side apply: O = phi(Q) M / (phi(Q) z + eps).
 // A workgroup of 8 waves walks a contiguous range of "groups" (8 waves x TB x
 // 32 tokens of one head).  The projection operand, M and z of the current
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(256) void k_wprep(const float* w, void* out, int n1
 // ===========================================================================
 struct ApplyArgs {
   const void* q;
-  const void* wp;       // projection operand (k_wprep)
+  const void* wp;       // projection operand (prepared by k_combine)
   const void* mstate;   // [BH] x operand-ordered M (m x d), operand type
   const void* zstate;   // [BH] x operand-ordered z (m), operand type
   void* o;
@@ -827,33 +830,6 @@ static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const
   return hipGetLastError();
 }
 
-template <class Tr, int D>
-static hipError_t wprep_t(const Plan& p, const float* w, void* out, hipStream_t s) {
-  constexpr int WES = Tr::VPS == 8 ? 2 : 4;
-  const int n16 = p.Hw * p.M * D * WES / 16;
-  timing_begin(FAVOR_KERNEL_WPREP, s);
-  hipLaunchKernelGGL((k_wprep<Tr, D>), dim3((n16 + 255) / 256), dim3(256), 0, s, w, out, n16);
-  timing_end(FAVOR_KERNEL_WPREP, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_wprep(const Plan& p, const float* w, void* out, hipStream_t s) {
-  if (p.dt == FAVOR_BF16) {
-    switch (p.D) {
-      case 32: return wprep_t<TrBF16, 32>(p, w, out, s);
-      case 64: return wprep_t<TrBF16, 64>(p, w, out, s);
-      case 128: return wprep_t<TrBF16, 128>(p, w, out, s);
-    }
-  } else {
-    switch (p.D) {
-      case 32: return wprep_t<TrF32, 32>(p, w, out, s);
-      case 64: return wprep_t<TrF32, 64>(p, w, out, s);
-      case 128: return wprep_t<TrF32, 128>(p, w, out, s);
-    }
-  }
-  return hipErrorInvalidValue;
-}
-
 static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* wp, const void* mstate,
                                const void* zstate, hipStream_t s) {
   if (p.dt == FAVOR_BF16) {
@@ -878,19 +854,18 @@ hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
   void* wp = t.ws + p.off_wprep;
   void* mstate = t.ws + p.off_mstate;
   void* zstate = t.ws + p.off_zstate;
-  hipError_t e = launch_wprep(p, t.w, wp, s);
-  if (e != hipSuccess) return e;
-  e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
+  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
   if (e != hipSuccess) return e;
   const int nq = (p.M * p.D + p.M) / 4;
-  dim3 cgrid((nq + kQuadsPerBlock - 1) / kQuadsPerBlock, p.BH);
+  const int n16w = p.Hw * p.M * p.D * (p.dt == FAVOR_BF16 ? 2 : 4) / 16;
+  dim3 cgrid((nq + kQuadsPerBlock - 1) / kQuadsPerBlock, p.BH + 1);
   timing_begin(FAVOR_KERNEL_COMBINE, s);
   if (p.dt == FAVOR_BF16)
     hipLaunchKernelGGL((k_combine<bf16>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate, p.splits,
-                       p.M, p.D);
+                       p.M, p.D, p.BH, t.w, wp, n16w);
   else
     hipLaunchKernelGGL((k_combine<float>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
-                       p.splits, p.M, p.D);
+                       p.splits, p.M, p.D, p.BH, t.w, wp, n16w);
   timing_end(FAVOR_KERNEL_COMBINE, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

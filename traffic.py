@@ -37,7 +37,7 @@ COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
 
 
 def short_name(kernel_name: str) -> str:
-    for k in ("k_reduce", "k_combine", "k_apply", "k_span_scan", "k_causal", "k_wprep", "k_features"):
+    for k in ("k_reduce", "k_combine", "k_apply", "k_span_scan", "k_causal", "k_features"):
         if k in kernel_name:
             return k
     return kernel_name
