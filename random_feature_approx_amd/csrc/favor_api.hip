@@ -40,8 +40,9 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.fbw = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
   const int nfb = m / 32;
   p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
+  p.rfbw = 1;   // two blocks per wave (4 waves) measured slower: fewer waves to hide latency
   p.rnw = (dt == FAVOR_F32 && d == 128) ? 4 : 8;
-  p.rfgroups = (nfb + p.rnw - 1) / p.rnw;
+  p.rfgroups = (nfb + p.rnw * p.rfbw - 1) / (p.rnw * p.rfbw);
   const int target = 2 * num_cus;
   // non-causal: reduction workgroups = BH * splits * rfgroups; causal: the
   // chunk scan runs one workgroup per (span, head) and walks feature groups

@@ -19,7 +19,8 @@ struct Plan {
   // K-side reduction (non-causal state, or causal span aggregates)
   int splits;           // token ranges per head
   int split_len;        // tokens per range (multiple of 64)
-  int rnw;              // waves per reduction workgroup (one 32-feature block each)
+  int rnw;              // waves per reduction workgroup
+  int rfbw;             // 32-feature blocks per reduction wave
   int rfgroups;         // reduction feature groups per head (workgroups sharing K, V tiles)
   // causal chunk scan
   int fgroups;          // feature groups walked in turn by one workgroup

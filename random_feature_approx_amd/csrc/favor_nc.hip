@@ -121,13 +121,12 @@ struct RedLds {
   static constexpr int kTotal = kRing + STAGES * PAIR;
 };
 
-// NW waves per workgroup, each owning one block of 32 features.  One barrier
+// NW waves per workgroup, each owning FBW blocks of 32 features.  One barrier
 // per tile: after it, tile t+2 is copied, tile t+1 is prepared and tile t is
 // computed from its prepared buffer, so the copies, the preparation (LDS and
 // a little VALU work) and the matrix products of different tiles overlap.
-template <class Tr, int D, int NW>
+template <class Tr, int D, int NW, int FBW>
 __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
-  constexpr int FBW = 1;
   constexpr int NT = NW * 64;
   using E = typename Tr::elem;
   using F = typename Tr::frag;
@@ -778,13 +777,16 @@ template <class Tr, int D>
 hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
                            hipStream_t s) {
   RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len};
-  // waves per workgroup: 8, or 4 where a wave's registers exceed half a SIMD's
+  // 8 waves of one feature block each, or 4 where a wave's registers exceed
+  // half a SIMD's (two blocks per wave, sharing each K/V fragment read, ran
+  // slower: half as many waves to hide the latency of each block's chain)
+  constexpr int FBW = 1;
   constexpr int NW = (Tr::VPS == 1 && D == 128) ? 4 : 8;
-  if (p.rnw != NW) return hipErrorInvalidValue;
+  if (p.rnw != NW || p.rfbw != FBW) return hipErrorInvalidValue;
   dim3 grid(p.splits, p.rfgroups, p.BH);
   const size_t lds = RedLds<Tr, D, NW * 64>::kTotal;
   timing_begin(FAVOR_KERNEL_REDUCE, s);
-  hipLaunchKernelGGL((k_reduce<Tr, D, NW>), grid, dim3(NW * 64), lds, s, a);
+  hipLaunchKernelGGL((k_reduce<Tr, D, NW, FBW>), grid, dim3(NW * 64), lds, s, a);
   timing_end(FAVOR_KERNEL_REDUCE, s);
   return hipGetLastError();
 }
