@@ -56,11 +56,14 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   len = (len + 63) / 64 * 64;
   p.split_len = len;
   p.splits = (L + len - 1) / len;
-  // apply: one workgroup of 8 waves per compute unit, walking groups of
-  // 8 waves x TB x 32 tokens of one head
-  const int tb = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
-  p.apply_tile = tb * 32;
-  const int gph = (L + 8 * p.apply_tile - 1) / (8 * p.apply_tile);
+  // apply: one workgroup per compute unit walking groups of NW waves x TB x
+  // 32 tokens of one head (bf16, d <= 64: 16 waves of one block each, four
+  // per SIMD; otherwise 8 waves)
+  const bool lean = dt == FAVOR_BF16 && d <= 64;
+  p.apply_nw = lean ? 16 : 8;
+  p.apply_tile = 32;
+  const int gsz = p.apply_nw * p.apply_tile;
+  const int gph = (L + gsz - 1) / gsz;
   const int total = p.BH * gph;
   p.apply_steps = (total + num_cus - 1) / num_cus;
   if (p.apply_steps < 1) p.apply_steps = 1;

@@ -27,6 +27,7 @@ struct Plan {
   int fbw;              // 32-feature blocks per wave
   // Q-side apply (non-causal)
   int apply_tile;       // tokens per wave per step
+  int apply_nw;         // waves per apply workgroup
   int apply_groups;     // total workgroups
   int apply_steps;      // groups per workgroup
   int fch;              // features per LDS chunk

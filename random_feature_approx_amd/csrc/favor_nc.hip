@@ -465,13 +465,14 @@ struct ApplyArgs {
   int stage_off;        // LDS offset of the per-wave output staging areas
 };
 
-constexpr int kApplyWaves = 8;
-
-template <class Tr, int D, int TB>
-__global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
+// NW waves per workgroup, TB 32-token blocks per wave.  LEAN: no Q prefetch,
+// one feature block per scheduling region and no output staging, so that a
+// wave fits 128 registers (four waves per SIMD).
+template <class Tr, int D, int TB, int NW, bool LEAN>
+__global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
-  constexpr int NW = kApplyWaves, NT = NW * 64;
+  constexpr int NT = NW * 64;
   constexpr int NKD = D / Tr::KS;
   constexpr int NDB = D / 32;
   constexpr int ES = sizeof(E);
@@ -532,7 +533,22 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
   int cb = 0, loaded0 = -1, loaded1 = -1;             // head held by each buffer
 
   QRaw qnext[TB][NKD];
-  if (g0 < g1) load_q(g0, qnext);
+  if (!LEAN && g0 < g1) load_q(g0, qnext);
+  // LEAN: each wave copies its next 32 Q rows into its own LDS slot with
+  // global->LDS loads while the current group is computed (no registers held)
+  using QT = DmaTile<E, D, 32, 64>;
+  char* qslot = smem + a.stage_off + w * QT::BYTES;
+  const typename QT::Lane qplan = QT::lane_plan(0, lane);
+  auto issue_q = [&](int g) {
+    const int bh = g / a.groups_per_head;
+    const int tbase = (g % a.groups_per_head) * (NW * TB * 32) + w * TB * 32;
+    const E* Q = (const E*)a.q + (size_t)bh * a.L * D;
+    const bool any = tbase < a.L;                        // rows past the end re-read row 0
+    QT::issue_plan(qslot, (const char*)(Q + (size_t)(any ? tbase : 0) * D), any ? a.L - tbase : 1, qplan, 0);
+  };
+  if constexpr (LEAN) {
+    if (g0 < g1) issue_q(g0);
+  }
   int cur_bh = -1;
   for (int g = g0; g < g1; ++g) {
     const int bh = g / a.groups_per_head;
@@ -565,11 +581,22 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
     cur_bh = bh;
 
     QRaw qraw[TB][NKD];
+    if constexpr (LEAN) {
+      static_assert(TB == 1 && QV, "one 32-row block per wave");
+      // this wave's rows of group g landed (for later groups the wait before
+      // the previous group's output stores covered it)
+      if (g == g0) wait_vmcnt<0>();
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+      for (int s = 0; s < NKD; ++s) qraw[0][s] = QT::chunk(qslot, l32, ((D / 2) * hh + Tr::VPS * s) * ES / 16);
+      wait_lgkm0();                                      // read before the slot is refilled
+      if (g + 1 < g1) issue_q(g + 1);
+    } else {
 #pragma unroll
-      for (int s = 0; s < NKD; ++s) qraw[tb][s] = qnext[tb][s];
-    if (g + 1 < g1) load_q(g + 1, qnext);
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) qraw[tb][s] = qnext[tb][s];
+      if (g + 1 < g1) load_q(g + 1, qnext);
+    }
 
     F qf[TB][NKD];
     float bias[TB];
@@ -674,7 +701,7 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
       };
       const int nfbc = nf >> 5;
       int fb = 0;
-      if constexpr (Tr::VPS == 8 || D <= 64) {           // registers allow it
+      if constexpr (!LEAN && (Tr::VPS == 8 || D <= 64)) {   // registers allow it
         for (; fb + 1 < nfbc; fb += 2) {
           do_fb(fb);
           do_fb(fb + 1);
@@ -687,7 +714,10 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply(ApplyArgs a) {
     // that every store instruction writes whole rows (8 lanes per row)
     // instead of 16 bytes in each of 32 rows; longer rows are stored directly.
     E* O = (E*)a.o + (size_t)bh * a.L * D;
-    constexpr bool kStage = D * ES <= 128;
+    constexpr bool kStage = !LEAN && D * ES <= 128;
+    // LEAN: the next group's rows (copy issued at this group's start) are
+    // waited for here, before this group's stores join the queue
+    if constexpr (LEAN) wait_vmcnt<0>();
     constexpr int RSO = D * ES + 16;
     constexpr int CPRO = D * ES / 16;
     char* stage = smem + a.stage_off + w * 32 * RSO;
@@ -809,25 +839,27 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const floa
   return hipErrorInvalidValue;
 }
 
-template <class Tr, int D, int TB>
+template <class Tr, int D, int TB, int NW, bool LEAN>
 static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const void* mstate, const void* zstate,
                           hipStream_t s) {
   using E = typename Tr::elem;
   constexpr int WES = Tr::VPS == 8 ? 2 : 4;
-  const int gsz = kApplyWaves * TB * 32;
+  const int gsz = NW * TB * 32;
   const int gph = (p.L + gsz - 1) / gsz;
   const int total = p.BH * gph;
   const size_t buf = (size_t)p.fch * D * WES + (size_t)p.fch * D * sizeof(E) + (size_t)p.fch * sizeof(E);
-  const size_t stage = D * sizeof(E) <= 128 ? (size_t)kApplyWaves * 32 * (D * sizeof(E) + 16) : 0;
+  // output staging rows (non-LEAN, rows up to 128 bytes) or the LEAN Q slots
+  const size_t stage = LEAN ? (size_t)NW * 32 * D * sizeof(E)
+                            : (D * sizeof(E) <= 128 ? (size_t)NW * 32 * (D * sizeof(E) + 16) : 0);
   const int nbuf = (p.fch >= p.M && 2 * buf + stage <= 150 * 1024) ? 2 : 1;
   const size_t stage_off = (nbuf * buf + 15) / 16 * 16;
   ApplyArgs a{t.q, wp, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch, nbuf,
               (int)stage_off};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
   const size_t lds = stage_off + stage;
-  if (TB * 32 != p.apply_tile) return hipErrorInvalidValue;
+  if (TB * 32 != p.apply_tile || NW != p.apply_nw) return hipErrorInvalidValue;
   timing_begin(FAVOR_KERNEL_APPLY, s);
-  hipLaunchKernelGGL((k_apply<Tr, D, TB>), dim3(nblk), dim3(kApplyWaves * 64), lds, s, a);
+  hipLaunchKernelGGL((k_apply<Tr, D, TB, NW, LEAN>), dim3(nblk), dim3(NW * 64), lds, s, a);
   timing_end(FAVOR_KERNEL_APPLY, s);
   return hipGetLastError();
 }
@@ -836,15 +868,15 @@ static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* wp, 
                                const void* zstate, hipStream_t s) {
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
-      case 32: return apply_t<TrBF16, 32, 2>(p, t, wp, mstate, zstate, s);
-      case 64: return apply_t<TrBF16, 64, 2>(p, t, wp, mstate, zstate, s);
-      case 128: return apply_t<TrBF16, 128, 1>(p, t, wp, mstate, zstate, s);
+      case 32: return apply_t<TrBF16, 32, 1, 16, true>(p, t, wp, mstate, zstate, s);
+      case 64: return apply_t<TrBF16, 64, 1, 16, true>(p, t, wp, mstate, zstate, s);
+      case 128: return apply_t<TrBF16, 128, 1, 8, false>(p, t, wp, mstate, zstate, s);
     }
   } else {
     switch (p.D) {
-      case 32: return apply_t<TrF32, 32, 1>(p, t, wp, mstate, zstate, s);
-      case 64: return apply_t<TrF32, 64, 1>(p, t, wp, mstate, zstate, s);
-      case 128: return apply_t<TrF32, 128, 1>(p, t, wp, mstate, zstate, s);
+      case 32: return apply_t<TrF32, 32, 1, 8, false>(p, t, wp, mstate, zstate, s);
+      case 64: return apply_t<TrF32, 64, 1, 8, false>(p, t, wp, mstate, zstate, s);
+      case 128: return apply_t<TrF32, 128, 1, 8, false>(p, t, wp, mstate, zstate, s);
     }
   }
   return hipErrorInvalidValue;
