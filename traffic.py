@@ -1,6 +1,7 @@
 """Measure HBM traffic per kernel launch with rocprofv3 counters for bench.py.
 
     python traffic.py [--workload long] [--out gpurun_out/traffic]
+    python traffic.py --workload long --resummarise STAMP   (re-read the runs of STAMP)
 
 Every counter is collected in a rocprofv3 run of its own (FETCH_SIZE, then
 WRITE_SIZE), once per path of the workload (bench.py --paths P, so that a
@@ -12,7 +13,7 @@ per-dispatch readings are multiplied by it.
 
 Writes profiles/hbm_traffic.json (read by bench.py, valid while the kernel
 sources hash the same) and profiles/hbm_traffic_<workload>.txt (the summary
-with the commands that produced it).  Needs a GPU; the script itself does
+with the commands that produced it), and copies both into the --out folder.  Needs a GPU; the script itself does
 not touch it, each rocprofv3 run is a child process.
 """
 from __future__ import annotations
@@ -22,6 +23,7 @@ import csv
 import glob
 import json
 import os
+import shutil
 import subprocess
 import sys
 import time
@@ -43,39 +45,46 @@ def short_name(kernel_name: str) -> str:
     return kernel_name
 
 
-def run_pass(counter: str, out_dir: str, prog: list) -> tuple:
-    """One rocprofv3 counter run; returns its counter rows and the command."""
+def run_pass(counter: str, out_dir: str, prog: list, run: bool = True) -> tuple:
+    """One rocprofv3 counter run (or, with run=False, the rows an earlier run
+    left in out_dir); returns its counter rows and the command, with the
+    repository's own path written as $REPO."""
     cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", counter, "--output-format", "csv",
            "-d", out_dir, "-o", "run", "--", sys.executable, *prog]
-    print("[traffic] " + " ".join(cmd), flush=True)
-    env = dict(os.environ, TMPDIR="/tmp")
-    r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if r.returncode != 0:
-        print(r.stdout[-3000:], flush=True)
-        raise SystemExit(f"rocprofv3 pass failed ({r.returncode}): {' '.join(cmd)}")
+    shown = " ".join(["python3" if c == sys.executable else c.replace(ROOT, "$REPO") for c in cmd[4:]])
+    if run:
+        print("[traffic] " + " ".join(cmd), flush=True)
+        env = dict(os.environ, TMPDIR="/tmp")
+        r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            print(r.stdout[-3000:], flush=True)
+            raise SystemExit(f"rocprofv3 pass failed ({r.returncode}): {' '.join(cmd)}")
     rows = []
     for f in glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             rows += [row for row in csv.DictReader(fh) if row.get("Counter_Name") == counter]
     if not rows:
         raise SystemExit(f"no {counter} rows under {out_dir}")
-    return rows, " ".join(cmd[4:])
+    return rows, shown
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="long", choices=list(synth.WORKLOADS))
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "traffic"))
+    ap.add_argument("--resummarise", metavar="STAMP", default=None,
+                    help="rebuild the summary from the runs an earlier call left under --out")
     args = ap.parse_args()
     wl = synth.WORKLOADS[args.workload]
     bench_py = os.path.join(ROOT, "bench.py")
-    stamp = time.strftime("%Y%m%d-%H%M%S")
+    stamp = args.resummarise or time.strftime("%Y%m%d-%H%M%S")
+    run = args.resummarise is None
 
     # scale factors from the plain copy (bytes read = bytes written = COPY_MIB MiB)
     scale, commands = {}, []
     for c in COUNTERS:
         rows, cmd = run_pass(c, os.path.join(args.out, f"copy_{c}_{stamp}"),
-                             [bench_py, "--copy-calibration", str(COPY_MIB)])
+                             [bench_py, "--copy-calibration", str(COPY_MIB)], run)
         commands.append(cmd)
         vals = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         if not vals:
@@ -88,7 +97,7 @@ def main() -> int:
         for c in COUNTERS:
             rows, cmd = run_pass(c, os.path.join(args.out, f"{wl.name}_{path}_{c}_{stamp}"),
                                  [bench_py, "--workload", wl.name, "--paths", path, "--steps", "3", "--warmup", "1",
-                                  "--cpu-seconds", "0"])
+                                  "--cpu-seconds", "0"], run)
             commands.append(cmd)
             acc = {}
             for r in rows:
@@ -128,11 +137,15 @@ def main() -> int:
             continue
         lines.append(f"{key[len(wl.name) + 1:]:32s} {v['fetch_bytes'] / 1e6:10.2f} {v['write_bytes'] / 1e6:10.2f} "
                      f"{v['bytes_per_launch'] / 1e6:10.2f}")
-    lines += ["", "commands (run from /tmp with TMPDIR=/tmp):"] + ["  " + c for c in commands]
+    lines += ["", "made by: python3 traffic.py --workload {} ($REPO = the repository root), which runs,".format(wl.name),
+              "from /tmp with TMPDIR=/tmp:"] + ["  " + c for c in commands]
     txt = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl.name}.txt")
     with open(txt, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
+    os.makedirs(args.out, exist_ok=True)
+    for src in (bench.TRAFFIC_FILE, txt):
+        shutil.copy(src, os.path.join(args.out, os.path.basename(src)))
     return 0
 
 
