@@ -121,6 +121,34 @@ favor_status favor_attn(const void* Q, const void* K, const void* V,
                         favor_dtype dtype, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Backward pass of non-causal attention: the gradients dQ, dK, dV of
+ * sum(dO * O) for the O that favor_attn_noncausal computes from the same
+ * Q, K, V, W, eps (upstream gradient dO, all [B, H, L, d] in dtype; W gets
+ * no gradient: it is a fixed random projection).  The pages give no
+ * formulas for it; this is the chain rule through the reassociated form
+ * (Performer page, In[25]) and the feature-map equation, where
+ * d phi_f / dx = phi_f (omega_f - x).  Nothing from the forward call is
+ * reused: the state M, z is recomputed from K and V.
+ * Precision: with bf16 inputs the state M, its gradient, the features of Q
+ * divided by their denominators and the projection W log2(e) enter their
+ * products as pairs of bf16 (fp16 for W) values, hi + lo, about 16
+ * significant bits, because the gradient takes differences of nearly equal
+ * sums; gradients are returned rounded to bf16.
+ * Workspace: favor_bwd_workspace_bytes(B, H, L, d, m, 0, dtype) bytes,
+ * 256-byte aligned, no initialisation; it also covers Hw = H.  The causal
+ * backward is not available yet (favor_bwd_workspace_bytes returns 0 for
+ * causal = 1).  Same shape support and error behaviour as the forward.
+ */
+size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype);
+
+favor_status favor_attn_noncausal_bwd(const void* Q, const void* K, const void* V,
+                                      const float* W, int Hw, const void* dO,
+                                      void* dQ, void* dK, void* dV,
+                                      int B, int H, int L, int d, int m, float eps,
+                                      favor_dtype dtype, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/*
  * Kernel timing (for benchmarks and profiling; host-side only, allocates no
  * device memory).  favor_timing_start(k, capacity) creates `capacity` pairs
  * of HIP timing events; every later launch of kernel k by this library
@@ -138,7 +166,12 @@ typedef enum {
   FAVOR_KERNEL_APPLY = 3,      /* non-causal Q-side apply                         */
   FAVOR_KERNEL_SPAN_SCAN = 4,  /* causal exclusive prefix over spans              */
   FAVOR_KERNEL_CAUSAL = 5,     /* causal chunked scan                             */
-  FAVOR_KERNEL_COUNT = 6
+  FAVOR_KERNEL_BWD_PREP = 6,   /* backward: W operands                            */
+  FAVOR_KERNEL_BWD_REDUCE = 7, /* backward: state and state-gradient reductions   */
+  FAVOR_KERNEL_BWD_COMBINE = 8,/* backward: combine of their partials             */
+  FAVOR_KERNEL_BWD_Q = 9,      /* backward: query side (dQ)                       */
+  FAVOR_KERNEL_BWD_K = 10,     /* backward: key side (dK, dV)                     */
+  FAVOR_KERNEL_COUNT = 11
 } favor_kernel;
 
 favor_status favor_timing_start(favor_kernel k, int capacity);

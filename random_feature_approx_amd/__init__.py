@@ -10,6 +10,9 @@ Functions
     attn(q, k, v, w, causal=False, eps=1e-6) FAVOR+ attention, output like q
     attn_noncausal(...), attn_causal(...)    the two paths explicitly
     workspace_bytes(B, H, L, d, m, causal, dtype)
+    attn_backward(q, k, v, w, g, causal=False, eps=1e-6)
+                                            gradients (dq, dk, dv) of sum(g * O)
+    bwd_workspace_bytes(B, H, L, d, m, causal, dtype)
 
 Shapes: q, k, v are [B, H, L, d] (bfloat16 or float32, same dtype, contiguous);
 w is float32 [m, d] (shared by all heads) or [H, m, d] (one per head).
@@ -20,7 +23,8 @@ import ctypes
 import os
 
 __all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal",
-           "workspace_bytes", "FavorError", "STATUS", "KERNELS", "timing_start", "timing_stop"]
+           "workspace_bytes", "attn_backward", "bwd_workspace_bytes", "FavorError", "STATUS", "KERNELS",
+           "timing_start", "timing_stop"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBNAME = "libfavor.so"
@@ -29,7 +33,8 @@ _lib = None
 STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid shape", 3: "unsupported d, m or dtype",
           4: "workspace missing or too small", 5: "HIP runtime error", 6: "internal error"}
 F32, BF16 = 0, 1
-KERNELS = {"k_features": 0, "k_reduce": 1, "k_combine": 2, "k_apply": 3, "k_span_scan": 4, "k_causal": 5}
+KERNELS = {"k_features": 0, "k_reduce": 1, "k_combine": 2, "k_apply": 3, "k_span_scan": 4, "k_causal": 5,
+           "k_bprep": 6, "k_bred": 7, "k_bcombine": 8, "k_bside_q": 9, "k_bside_k": 10}
 
 
 class FavorError(RuntimeError):
@@ -67,6 +72,10 @@ def load():
         getattr(lib, name).argtypes = attn_args
     lib.favor_attn.restype = i
     lib.favor_attn.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.favor_bwd_workspace_bytes.restype = sz
+    lib.favor_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.favor_attn_noncausal_bwd.restype = i
+    lib.favor_attn_noncausal_bwd.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.favor_timing_start.restype = i
     lib.favor_timing_start.argtypes = [i, i]
     lib.favor_timing_stop.restype = i
@@ -175,6 +184,41 @@ def attn_noncausal(q, k, v, w, eps: float = 1e-6, **kw):
 
 def attn_causal(q, k, v, w, eps: float = 1e-6, **kw):
     return attn(q, k, v, w, causal=True, eps=eps, **kw)
+
+
+def bwd_workspace_bytes(B: int, H: int, L: int, d: int, m: int, causal: bool, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(load().favor_bwd_workspace_bytes(B, H, L, d, m, int(bool(causal)), code))
+
+
+def attn_backward(q, k, v, w, g, causal: bool = False, eps: float = 1e-6, workspace=None):
+    """Gradients (dq, dk, dv) of sum(g * attn(q, k, v, w, causal, eps)),
+    each with the shape and dtype of q.  W gets no gradient."""
+    lib = load()
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or g.shape != q.shape:
+        raise ValueError("q, k, v, g must share one [B, H, L, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype or g.dtype != q.dtype:
+        raise TypeError("q, k, v, g must share one dtype")
+    if causal:
+        raise NotImplementedError("the causal backward is not available yet")
+    B, H, L, d = q.shape
+    w, hw = _proj(w, H, (w.shape[-2], d))
+    m = int(w.shape[1])
+    _check_device(q, k, v, g, w)
+    code = _dtype_code(q)
+    need = int(lib.favor_bwd_workspace_bytes(B, H, L, d, m, 0, code))
+    if need == 0:
+        raise FavorError("favor_bwd_workspace_bytes", 2)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = lib.favor_attn_noncausal_bwd(ptr(q), ptr(k), ptr(v), ptr(w), hw, ptr(g), ptr(dq), ptr(dk), ptr(dv),
+                                      B, H, L, d, m, float(eps), code, ptr(workspace), workspace.numel(), _stream())
+    if st != 0:
+        raise FavorError("favor_attn_noncausal_bwd", st)
+    return dq, dk, dv
 
 
 def timing_start(kernel: str, capacity: int) -> None:

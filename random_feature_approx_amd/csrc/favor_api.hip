@@ -93,6 +93,43 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.off_den = off;
   if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * sizeof(float));
   p.total = off;
+  // backward: 4 feature blocks per reduction workgroup, about two
+  // workgroups per compute unit
+  p.bfgroups = (nfb + 3) / 4;
+  {
+    const int per = p.BH * p.bfgroups;
+    int bs = (target + per - 1) / per;
+    if (bs > max_splits) bs = max_splits;
+    if (bs < 1) bs = 1;
+    int bl = (L + bs - 1) / bs;
+    bl = (bl + 63) / 64 * 64;
+    p.bsplit_len = bl;
+    p.bsplits = (L + bl - 1) / bl;
+  }
+  size_t bo = 0;
+  p.boff_part = bo;
+  bo += align256((size_t)p.BH * p.bsplits * m * d * sizeof(float));
+  p.boff_partz = bo;
+  bo += align256((size_t)p.BH * p.bsplits * m * sizeof(float));
+  p.boff_zf = bo;
+  bo += align256((size_t)p.BH * m * sizeof(float));
+  p.boff_lg = bo;
+  bo += align256((size_t)p.BH * L * sizeof(float));
+  p.boff_cw = bo;
+  bo += align256((size_t)p.BH * L * sizeof(float));
+  p.boff_wph = bo;                                   // sized for Hw = H
+  bo += align256((size_t)H * m * d * (size_t)wes);
+  p.boff_wpl = bo;
+  bo += align256((size_t)H * m * d * (size_t)wes);
+  p.boff_wt = bo;
+  bo += align256((size_t)H * m * d * p.esize);
+  p.boff_rows_hi = bo;
+  bo += align256((size_t)p.BH * m * d * p.esize);
+  p.boff_rows_lo = bo;
+  bo += align256((size_t)p.BH * m * d * p.esize);
+  p.boff_op = bo;
+  bo += align256((size_t)p.BH * m * d * p.esize);
+  p.btotal = bo;
   return true;
 }
 
@@ -197,6 +234,26 @@ static void timer_free(Timer& t) {
   t = Timer();
 }
 
+size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype) {
+  Plan p;
+  if (causal) return 0;
+  if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count())) return 0;
+  return p.btotal;
+}
+
+favor_status favor_attn_noncausal_bwd(const void* Q, const void* K, const void* V, const float* W, int Hw,
+                                      const void* dO, void* dQ, void* dK, void* dV, int B, int H, int L, int d,
+                                      int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV) return FAVOR_ERR_NULL;
+  favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
+  if (st != FAVOR_OK) return st;
+  Plan p;
+  if (!make_plan(p, B, H, L, d, m, Hw, 0, dtype, device_cu_count())) return FAVOR_ERR_HIP;
+  if (!ws || ws_bytes < p.btotal || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
+  BwdTensors t{Q, K, V, W, dO, dQ, dK, dV, eps, (char*)ws};
+  return launch_noncausal_bwd(p, t, (hipStream_t)stream) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
 favor_status favor_timing_start(favor_kernel k, int capacity) {
   if ((int)k < 0 || k >= FAVOR_KERNEL_COUNT || capacity < 1) return FAVOR_ERR_SHAPE;
   Timer& t = g_timers[k];
@@ -241,6 +298,11 @@ const char* favor_kernel_name(favor_kernel k) {
     case FAVOR_KERNEL_APPLY: return "k_apply";
     case FAVOR_KERNEL_SPAN_SCAN: return "k_span_scan";
     case FAVOR_KERNEL_CAUSAL: return "k_causal";
+    case FAVOR_KERNEL_BWD_PREP: return "k_bprep";
+    case FAVOR_KERNEL_BWD_REDUCE: return "k_bred";
+    case FAVOR_KERNEL_BWD_COMBINE: return "k_bcombine";
+    case FAVOR_KERNEL_BWD_Q: return "k_bside_q";
+    case FAVOR_KERNEL_BWD_K: return "k_bside_k";
     default: return "unknown";
   }
 }

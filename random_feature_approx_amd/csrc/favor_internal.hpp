@@ -33,6 +33,11 @@ struct Plan {
   int fch;              // features per LDS chunk
   // workspace offsets (bytes)
   size_t off_part, off_partz, off_wprep, off_mstate, off_zstate, off_num, off_den, total;
+  // backward pass: its reductions (4 waves of one feature block each) and
+  // its workspace (a separate layout, sized by favor_bwd_workspace_bytes)
+  int bsplits, bsplit_len, bfgroups;
+  size_t boff_part, boff_partz, boff_zf, boff_lg, boff_cw, boff_wph, boff_wpl, boff_wt, boff_rows_hi,
+      boff_rows_lo, boff_op, btotal;
 };
 
 bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus);
@@ -48,6 +53,19 @@ struct Tensors {
   char* ws;
 };
 
+struct BwdTensors {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* w;
+  const void* g;        // upstream gradient dLoss/dO
+  void* dq;
+  void* dk;
+  void* dv;
+  float eps;
+  char* ws;
+};
+
 // Kernel timing hooks (see favor_timing_start): record the next free event
 // pair of kernel k around a launch on stream s.
 void timing_begin(favor_kernel k, hipStream_t s);
@@ -56,6 +74,7 @@ void timing_end(favor_kernel k, hipStream_t s);
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
                          hipStream_t s);
 

@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "bf16_round", "bf16_bits_to_f32",
     "t1_qkv", "t1_projection", "iid_projection", "orthogonal_projection",
-    "make_inputs", "random_case", "as_f64",
+    "make_inputs", "random_case", "as_f64", "upstream_gradient",
 ]
 
 
@@ -227,3 +227,12 @@ def random_case(seed: int, B: int, H: int, L: int, d: int, m: int, dtype: str,
         out[name + "64"] = as_f64(out[name], dtype)
     return out
 
+
+
+def upstream_gradient(seed: int, shape, dtype: str):
+    """A seeded upstream gradient dLoss/dO for the backward pass: N(0, 1)
+    entries in device format (bf16 bits or float32) and their exact float64
+    values."""
+    g = _draw(np.random.default_rng(seed), tuple(shape), 1.0)
+    dev = bf16_round(g) if dtype == "bf16" else np.ascontiguousarray(g, dtype=np.float32)
+    return dev, as_f64(dev, dtype)
