@@ -16,7 +16,10 @@ The JSON line also carries
     the library records on the launch stream during the timed steps;
   * "cpu_baseline": the float64 NumPy oracle timed on the host cores on a
     bounded sample of the same workload (a reported baseline, not a target);
-  * "paths" and "kernels": per-path and per-kernel timings.
+  * "paths" and "kernels": per-path and per-kernel timings;
+  * "backward": the backward pass (gradients of sum(G * O) for a seeded
+    upstream gradient G) of each path that has one, timed the same way after
+    the forward measurement; it is reported beside `value`, never in it.
 """
 from __future__ import annotations
 
@@ -34,7 +37,8 @@ sys.path.insert(0, ROOT)
 METRIC = "FAVOR+ fwd tokens/sec (B·H·L/s) causal & non-causal; % of MFMA/HBM roofline"
 PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks
-KERNEL_SOURCES = ["favor_device.hpp", "favor_tiles.hpp", "favor_nc.hip", "favor_causal.hip"]
+KERNEL_SOURCES = ["favor_device.hpp", "favor_tiles.hpp", "favor_nc.hip", "favor_causal.hip"]   # forward kernels
+BWD_KERNELS = ["k_bprep", "k_bred", "k_bcombine", "k_bside_q", "k_bside_k"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -71,6 +75,25 @@ def algorithmic(kernel: str, path: str, wl) -> dict:
         return {"bytes": 2 * d * s * T, "flops": 4 * m * d * T}
     if kernel in ("k_combine", "k_span_scan"):
         return {"bytes": 0, "flops": 0}
+    # backward (the features of each side are computed by two kernels each;
+    # per launch of the reduction: read X and Y (2ds), projection and
+    # phi^T Y (4md); non-causal query side: read Q, G, write dQ (3ds),
+    # projection, y = M g and W^T (phi * dphi) (6md); key side: read K, V,
+    # write dK, dV (4ds), projection, dM^T phi, dM v and W^T (phi * dphi)
+    # (8md).  Causal: the query side also reads K, V for the state (5ds,
+    # plus the state update 2md: 8md); the key side also reads Q, G (6ds,
+    # plus the projection of Q and the update 4md: 12md).  The timed "launch"
+    # of a side is every kernel launch of that side in one call.)
+    if kernel == "k_bred":
+        return {"bytes": 2 * d * s * T, "flops": 4 * m * d * T}
+    if kernel == "k_bside_q":
+        if path == "causal":
+            return {"bytes": 5 * d * s * T, "flops": 8 * m * d * T}
+        return {"bytes": 3 * d * s * T, "flops": 6 * m * d * T}
+    if kernel == "k_bside_k":
+        if path == "causal":
+            return {"bytes": 6 * d * s * T, "flops": 12 * m * d * T}
+        return {"bytes": 4 * d * s * T, "flops": 8 * m * d * T}
     return {"bytes": 0, "flops": 0}
 
 
@@ -148,6 +171,57 @@ def cpu_baseline(wl, x, seconds: float) -> dict:
             "sample": "float64 NumPy oracle on whole heads of the same workload; " + "; ".join(sample)}
 
 
+def backward_leg(favor, torch, wl, q, k, v, w, to_dev, K: int, warmup: int) -> dict:
+    """Time the backward pass of every path that has one: K untimed warmup
+    calls, K calls bracketed by two events, then K more with the library's
+    per-launch kernel events (outside the timed region)."""
+    import synth
+    g_np, _ = synth.upstream_gradient(wl.seed_data + 6000, (wl.B, wl.H, wl.L, wl.d), wl.dtype)
+    g = to_dev(g_np)
+    out = {}
+    for path in wl.paths:
+        causal = path == "causal"
+        code = favor.BF16 if wl.dtype == "bf16" else favor.F32
+        ws = torch.empty(favor.bwd_workspace_bytes(wl.B, wl.H, wl.L, wl.d, wl.m, causal, code),
+                         dtype=torch.uint8, device=q.device)
+
+        def run():
+            return favor.attn_backward(q, k, v, w, g, causal=causal, eps=wl.eps, workspace=ws)
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / K
+        log(f"backward {path}: {ms:.4f} ms per call")
+        for kname in BWD_KERNELS:
+            favor.timing_start(kname, 2 * K + 4)
+        for _ in range(K):
+            run()
+        torch.cuda.synchronize()
+        kern = {}
+        for kname in BWD_KERNELS:
+            durs = favor.timing_stop(kname, 2 * K + 4)
+            if not durs:
+                continue
+            n_per = len(durs) // K if len(durs) >= K else 1
+            avg = sum(durs) / len(durs)
+            entry = {"avg_ms": round(avg, 5), "launches_per_call": n_per}
+            if algorithmic(kname, path, wl)["bytes"]:
+                r = roofline_entry(kname, path, wl, avg, None)
+                entry.update(hbm_frac_alg=r["hbm_frac_alg"], mfma_frac_alg=r["mfma_frac_alg"])
+            kern[kname] = entry
+        dom = max((kn for kn in kern if algorithmic(kn, path, wl)["bytes"]), key=lambda kn: kern[kn]["avg_ms"])
+        out[path] = {"ms": round(ms, 5), "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1), "kernels": kern,
+                     "roofline": roofline_entry(dom, path, wl, kern[dom]["avg_ms"], None)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +231,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time budget per path (0 = skip)")
     ap.add_argument("--paths", default="", help="comma-separated subset of the workload's paths to run "
                                                 "(default: all; used to attribute profiler counters to a path)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes 5 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -278,6 +353,8 @@ def main() -> int:
         kern_report[key] = {"avg_ms": round(val["avg_ms"], 5), "launches": val["launches"],
                             "hbm_frac_alg": r.get("hbm_frac_alg"), "mfma_frac_alg": r.get("mfma_frac_alg")}
 
+    bwd = None if args.no_backward else backward_leg(favor, torch, wl, q, k, v, w, to_dev, K, args.warmup)
+
     tokens = wl.tokens
     value = tokens / (ms_step * 1e-3)
     paths_report = {p: {"ms": round(path_ms[p], 5), "tokens_per_s": round(tokens / (path_ms[p] * 1e-3), 1)}
@@ -307,6 +384,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "paths": paths_report,
         "kernels": kern_report,
+        "backward": bwd,
     }
     print(json.dumps(line), flush=True)
     return 0

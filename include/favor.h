@@ -135,9 +135,8 @@ favor_status favor_attn(const void* Q, const void* K, const void* V,
  * significant bits, because the gradient takes differences of nearly equal
  * sums; gradients are returned rounded to bf16.
  * Workspace: favor_bwd_workspace_bytes(B, H, L, d, m, 0, dtype) bytes,
- * 256-byte aligned, no initialisation; it also covers Hw = H.  The causal
- * backward is not available yet (favor_bwd_workspace_bytes returns 0 for
- * causal = 1).  Same shape support and error behaviour as the forward.
+ * 256-byte aligned, no initialisation; it also covers Hw = H.  Same shape
+ * support and error behaviour as the forward.
  */
 size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype);
 
@@ -147,6 +146,24 @@ favor_status favor_attn_noncausal_bwd(const void* Q, const void* K, const void* 
                                       int B, int H, int L, int d, int m, float eps,
                                       favor_dtype dtype, void* ws, size_t ws_bytes,
                                       void* stream);
+
+/*
+ * Backward pass of causal attention: dQ, dK, dV of sum(dO * O) for the O of
+ * favor_attn_causal (study notes, case 2, with the causal denominator).  The
+ * query side uses the prefix sums S_i, z_i; the key side the suffix sums
+ * R_j = sum_{i>=j} phi(q_i) g_i^T / D_i and r_j = sum_{i>=j} phi(q_i) c_i / D_i
+ * (c_i = -phi(q_i).S_i g_i / D_i), accumulated in reverse as the study notes'
+ * pitfalls section says the causal backward must be.  Computed in 32-token
+ * chunks over spans of the sequence; precision as favor_attn_noncausal_bwd,
+ * with the query side's two feature sums formed from split (hi + lo)
+ * operands.  Workspace: favor_bwd_workspace_bytes(B, H, L, d, m, 1, dtype).
+ */
+favor_status favor_attn_causal_bwd(const void* Q, const void* K, const void* V,
+                                   const float* W, int Hw, const void* dO,
+                                   void* dQ, void* dK, void* dV,
+                                   int B, int H, int L, int d, int m, float eps,
+                                   favor_dtype dtype, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /*
  * Kernel timing (for benchmarks and profiling; host-side only, allocates no

@@ -74,8 +74,9 @@ def load():
     lib.favor_attn.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.favor_bwd_workspace_bytes.restype = sz
     lib.favor_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
-    lib.favor_attn_noncausal_bwd.restype = i
-    lib.favor_attn_noncausal_bwd.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    for name in ("favor_attn_noncausal_bwd", "favor_attn_causal_bwd"):
+        getattr(lib, name).restype = i
+        getattr(lib, name).argtypes = [vp, vp, vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.favor_timing_start.restype = i
     lib.favor_timing_start.argtypes = [i, i]
     lib.favor_timing_stop.restype = i
@@ -200,24 +201,23 @@ def attn_backward(q, k, v, w, g, causal: bool = False, eps: float = 1e-6, worksp
         raise ValueError("q, k, v, g must share one [B, H, L, d] shape")
     if k.dtype != q.dtype or v.dtype != q.dtype or g.dtype != q.dtype:
         raise TypeError("q, k, v, g must share one dtype")
-    if causal:
-        raise NotImplementedError("the causal backward is not available yet")
     B, H, L, d = q.shape
     w, hw = _proj(w, H, (w.shape[-2], d))
     m = int(w.shape[1])
     _check_device(q, k, v, g, w)
     code = _dtype_code(q)
-    need = int(lib.favor_bwd_workspace_bytes(B, H, L, d, m, 0, code))
+    need = int(lib.favor_bwd_workspace_bytes(B, H, L, d, m, int(bool(causal)), code))
     if need == 0:
         raise FavorError("favor_bwd_workspace_bytes", 2)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    st = lib.favor_attn_noncausal_bwd(ptr(q), ptr(k), ptr(v), ptr(w), hw, ptr(g), ptr(dq), ptr(dk), ptr(dv),
-                                      B, H, L, d, m, float(eps), code, ptr(workspace), workspace.numel(), _stream())
+    name = "favor_attn_causal_bwd" if causal else "favor_attn_noncausal_bwd"
+    st = getattr(lib, name)(ptr(q), ptr(k), ptr(v), ptr(w), hw, ptr(g), ptr(dq), ptr(dk), ptr(dv),
+                            B, H, L, d, m, float(eps), code, ptr(workspace), workspace.numel(), _stream())
     if st != 0:
-        raise FavorError("favor_attn_noncausal_bwd", st)
+        raise FavorError(name, st)
     return dq, dk, dv
 
 

@@ -94,9 +94,13 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * sizeof(float));
   p.total = off;
   // backward: 4 feature blocks per reduction workgroup, about two
-  // workgroups per compute unit
+  // workgroups per compute unit; the causal backward reduces over the spans
+  // of the forward's chunk scan
   p.bfgroups = (nfb + 3) / 4;
-  {
+  if (causal) {
+    p.bsplits = p.splits;
+    p.bsplit_len = p.split_len;
+  } else {
     const int per = p.BH * p.bfgroups;
     int bs = (target + per - 1) / per;
     if (bs > max_splits) bs = max_splits;
@@ -123,12 +127,18 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   bo += align256((size_t)H * m * d * (size_t)wes);
   p.boff_wt = bo;
   bo += align256((size_t)H * m * d * p.esize);
+  p.boff_wtl = bo;
+  bo += align256((size_t)H * m * d * p.esize);
   p.boff_rows_hi = bo;
   bo += align256((size_t)p.BH * m * d * p.esize);
   p.boff_rows_lo = bo;
   bo += align256((size_t)p.BH * m * d * p.esize);
   p.boff_op = bo;
   bo += align256((size_t)p.BH * m * d * p.esize);
+  // causal with more than one feature group: float32 per-token sums carried
+  // from one group to the next (2 d + 2 per token)
+  p.boff_acc = bo;
+  if (causal && p.bfgroups > 1) bo += align256((size_t)p.BH * L * (2 * d + 2) * sizeof(float));
   p.btotal = bo;
   return true;
 }
@@ -236,22 +246,34 @@ static void timer_free(Timer& t) {
 
 size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype) {
   Plan p;
-  if (causal) return 0;
   if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count())) return 0;
   return p.btotal;
+}
+
+static favor_status bwd_common(const void* Q, const void* K, const void* V, const float* W, int Hw, const void* dO,
+                               void* dQ, void* dK, void* dV, int B, int H, int L, int d, int m, float eps, int causal,
+                               favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV) return FAVOR_ERR_NULL;
+  favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
+  if (st != FAVOR_OK) return st;
+  Plan p;
+  if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count())) return FAVOR_ERR_HIP;
+  if (!ws || ws_bytes < p.btotal || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
+  BwdTensors t{Q, K, V, W, dO, dQ, dK, dV, eps, (char*)ws};
+  const hipError_t e = causal ? launch_causal_bwd(p, t, (hipStream_t)stream) : launch_noncausal_bwd(p, t, (hipStream_t)stream);
+  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
 favor_status favor_attn_noncausal_bwd(const void* Q, const void* K, const void* V, const float* W, int Hw,
                                       const void* dO, void* dQ, void* dK, void* dV, int B, int H, int L, int d,
                                       int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
-  if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV) return FAVOR_ERR_NULL;
-  favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
-  if (st != FAVOR_OK) return st;
-  Plan p;
-  if (!make_plan(p, B, H, L, d, m, Hw, 0, dtype, device_cu_count())) return FAVOR_ERR_HIP;
-  if (!ws || ws_bytes < p.btotal || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
-  BwdTensors t{Q, K, V, W, dO, dQ, dK, dV, eps, (char*)ws};
-  return launch_noncausal_bwd(p, t, (hipStream_t)stream) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  return bwd_common(Q, K, V, W, Hw, dO, dQ, dK, dV, B, H, L, d, m, eps, 0, dtype, ws, ws_bytes, stream);
+}
+
+favor_status favor_attn_causal_bwd(const void* Q, const void* K, const void* V, const float* W, int Hw,
+                                   const void* dO, void* dQ, void* dK, void* dV, int B, int H, int L, int d, int m,
+                                   float eps, favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_common(Q, K, V, W, Hw, dO, dQ, dK, dV, B, H, L, d, m, eps, 1, dtype, ws, ws_bytes, stream);
 }
 
 favor_status favor_timing_start(favor_kernel k, int capacity) {

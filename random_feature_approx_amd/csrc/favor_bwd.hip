@@ -27,9 +27,9 @@
 // for some rows, and so does dM v_j + dz on the key side; every operand that
 // feeds those differences is carried as a pair of bf16 values (hi + lo,
 // two matrix products) -- the projection (fp16 pair), M, dM and phi(Q)/D --
-// so they hold about 16 significant bits.  The last products (W^T against
-// the feature gradients, dM^T phi(K)) use single bf16 operands; accumulation
-// is float32 throughout.
+// so they hold about 16 significant bits, and the products of W^T with the
+// feature gradients take three products (hi hi, hi lo, lo hi).  dM^T phi(K)
+// uses single bf16 operands; accumulation is float32 throughout.
 #include "favor_device.hpp"
 #include "favor_internal.hpp"
 #include "favor_tiles.hpp"
@@ -70,7 +70,8 @@ template <> struct Bw<TrF32> {
 // feature order of a feature accumulator used as the other operand.
 // ---------------------------------------------------------------------------
 template <class Tr>
-__global__ __launch_bounds__(256) void k_bprep(const float* w, void* wph, void* wpl, void* wt, int nrows, int D) {
+__global__ __launch_bounds__(256) void k_bprep(const float* w, void* wph, void* wpl, void* wt, void* wtl, int nrows,
+                                               int D) {
   using E = typename Tr::elem;
   constexpr int WES = Tr::VPS == 8 ? 2 : 4;
   constexpr int PER = 16 / WES;
@@ -106,12 +107,15 @@ __global__ __launch_bounds__(256) void k_bprep(const float* w, void* wph, void* 
       const int db = rest % NDB;
       rest /= NDB;
       const int s = rest % NKT, fbg = rest / NKT;      // fbg: feature block over all Hw heads
-      E vals[VPS];
-#pragma unroll
-      for (int j = 0; j < VPS; ++j) vals[j] = (E)w[(size_t)(fbg * 32 + crow(VPS * s + j, h)) * D + db * 32 + c];
       E* dst = (E*)wt + (size_t)i * VPS;
+      E* dstl = (E*)wtl + (size_t)i * VPS;
 #pragma unroll
-      for (int j = 0; j < VPS; ++j) dst[j] = vals[j];
+      for (int j = 0; j < VPS; ++j) {
+        const float x = w[(size_t)(fbg * 32 + crow(VPS * s + j, h)) * D + db * 32 + c];
+        const E hi = (E)x;
+        dst[j] = hi;
+        if (wtl) dstl[j] = (E)(x - (float)hi);         // lo part (bf16)
+      }
     }
   }
 }
@@ -398,7 +402,8 @@ struct BSideArgs {
   const float* zf;        // z or dz [BH][M]
   const void* wph;
   const void* wpl;
-  const void* wt;         // W^T operand
+  const void* wt;         // W^T operand (hi)
+  const void* wtl;        // W^T operand (lo, bf16)
   void* dx;               // dQ or dK
   void* dy;               // dV (K side)
   float* lg;              // [BH][L] (Q side)
@@ -459,6 +464,7 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
   const char* wph = (const char*)a.wph + (size_t)hw * nfb * NKG * 2 * 32 * 16;
   const char* wpl = (const char*)a.wpl + (size_t)hw * nfb * NKG * 2 * 32 * 16;
   const E* wt = (const E*)a.wt + (size_t)hw * a.M * D;
+  const E* wtlo = (const E*)a.wtl + (size_t)hw * a.M * D;
   const E* rhi = (const E*)a.rows_hi + (size_t)bh * a.M * D;
   const E* rlo = (const E*)a.rows_lo + (size_t)bh * a.M * D;
   const float* zf = a.zf + (size_t)bh * a.M;
@@ -514,18 +520,28 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
     }
     return zr;
   };
-  // acc[db] += W^T gacc (the c-row feature order of gacc)
+  // acc[db] += W^T gacc (the c-row feature order of gacc), both operands
+  // split into hi + lo (three products: hi hi, hi lo, lo hi)
   auto wt_times = [&](int fb, const f32x16& gacc, f32x16 (&acc)[NDB]) {
 #pragma unroll
     for (int s2 = 0; s2 < NKT; ++s2) {
-      const F gfr = CFrag<Tr>::make(gacc, s2);
+      F gfr[SP::NS];
+      SP::split(gacc, s2, gfr);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const size_t e = (((((size_t)fb * NKT + s2) * NDB + db) * 2 + hh) * 32 + l32) * VPS;
-        F wfr;
-        if constexpr (VPS == 8) wfr = *(const u32x4*)(wt + e);
-        else wfr = wt[e];
-        acc[db] = Tr::mma(wfr, gfr, acc[db]);
+        F wfr[SP::NS];
+        if constexpr (VPS == 8) {
+          wfr[0] = *(const u32x4*)(wt + e);
+          if constexpr (SP::NS == 2) wfr[1] = *(const u32x4*)(wtlo + e);
+        } else {
+          wfr[0] = wt[e];
+        }
+        acc[db] = Tr::mma(wfr[0], gfr[0], acc[db]);
+        if constexpr (SP::NS == 2) {
+          acc[db] = Tr::mma(wfr[0], gfr[1], acc[db]);
+          acc[db] = Tr::mma(wfr[1], gfr[0], acc[db]);
+        }
       }
     }
   };
@@ -648,8 +664,8 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
 // host side
 // ===========================================================================
 struct BwdBuffers {
-  float *part, *partz, *zf, *lg, *cw;
-  void *wph, *wpl, *wt, *rows_hi, *rows_lo, *op;
+  float *part, *partz, *zf, *lg, *cw, *acc;
+  void *wph, *wpl, *wt, *wtl, *rows_hi, *rows_lo, *op;
 };
 
 static BwdBuffers bwd_buffers(const Plan& p, char* ws) {
@@ -662,6 +678,8 @@ static BwdBuffers bwd_buffers(const Plan& p, char* ws) {
   b.wph = ws + p.boff_wph;
   b.wpl = ws + p.boff_wpl;
   b.wt = ws + p.boff_wt;
+  b.wtl = ws + p.boff_wtl;
+  b.acc = (float*)(ws + p.boff_acc);
   b.rows_hi = ws + p.boff_rows_hi;
   b.rows_lo = ws + p.boff_rows_lo;
   b.op = ws + p.boff_op;
@@ -679,7 +697,8 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     const int n = nrows * D / (16 / WES) + nrows * D / Tr::VPS;
     const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
     timing_begin(FAVOR_KERNEL_BWD_PREP, s);
-    hipLaunchKernelGGL((k_bprep<Tr>), dim3(blocks), dim3(256), 0, s, t.w, b.wph, b.wpl, b.wt, nrows, D);
+    hipLaunchKernelGGL((k_bprep<Tr>), dim3(blocks), dim3(256), 0, s, t.w, b.wph, b.wpl, b.wt,
+                       Tr::VPS == 8 ? b.wtl : nullptr, nrows, D);
     timing_end(FAVOR_KERNEL_BWD_PREP, s);
   }
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
@@ -703,7 +722,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   }
   // query side: dQ, and the per-token scale and weight of the next reduction
   {
-    BSideArgs a{t.q, t.g, b.rows_hi, b.rows_lo, nullptr, b.zf, b.wph, b.wpl, b.wt, t.dq, nullptr, b.lg, b.cw,
+    BSideArgs a{t.q, t.g, b.rows_hi, b.rows_lo, nullptr, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dq, nullptr, b.lg, b.cw,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps};
     timing_begin(FAVOR_KERNEL_BWD_Q, s);
     hipLaunchKernelGGL((k_bside<Tr, D, true>), sgrid, dim3(256), 0, s, a);
@@ -722,7 +741,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   }
   // key side: dK, dV
   {
-    BSideArgs a{t.k, t.v, b.rows_hi, b.rows_lo, b.op, b.zf, b.wph, b.wpl, b.wt, t.dk, t.dv, nullptr, nullptr,
+    BSideArgs a{t.k, t.v, b.rows_hi, b.rows_lo, b.op, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dk, t.dv, nullptr, nullptr,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps};
     timing_begin(FAVOR_KERNEL_BWD_K, s);
     hipLaunchKernelGGL((k_bside<Tr, D, false>), sgrid, dim3(256), 0, s, a);
@@ -743,6 +762,672 @@ hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t 
       case 32: return bwd_noncausal_t<TrF32, 32>(p, t, s);
       case 64: return bwd_noncausal_t<TrF32, 64>(p, t, s);
       case 128: return bwd_noncausal_t<TrF32, 128>(p, t, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// ===========================================================================
+// Causal backward.
+//
+// With S_i = sum_{j<=i} phi(k_j) v_j^T and z_i = sum_{j<=i} phi(k_j) (the
+// prefix sums of case 2 of the performer-2020 study notes), the query side is
+// the non-causal one with M, z replaced by S_i, z_i:
+//   y_i = S_i g_i,  s_i = phi(q_i).y_i,  D_i = phi(q_i).z_i + eps,
+//   dq_i = (A1_i - (s_i/D_i) A2_i - (s_i eps/D_i) q_i) / D_i,
+//   A1_i = W^T (phi(q_i) * y_i),  A2_i = W^T (phi(q_i) * z_i);
+// the key side uses the suffix sums that the notes' pitfalls section says the
+// backward must accumulate in reverse:
+//   R_j = sum_{i>=j} phi(q_i) g_i^T / D_i,  r_j = sum_{i>=j} phi(q_i) c_i / D_i,
+//   c_i = -s_i/D_i,  dv_j = R_j^T phi(k_j),  dphi(k_j) = R_j v_j + r_j.
+// Both sides walk 32-token chunks of a span (one workgroup per span and
+// head, four waves, one 32-feature block per wave, feature groups in turn),
+// starting from the span's exclusive prefix (query side) or suffix (key side)
+// of the span aggregates.  Inside a chunk the masked token-by-token terms are
+// matrix products with the chunk's 32 x 32 score-like tiles.  The query side
+// forms A1 and A2 separately (one pass over the features) with three-term
+// split products (hi*hi + hi*lo + lo*hi), which keeps the difference
+// A1 - (s/D) A2 accurate; the contributions of the waves and feature groups
+// are summed in a fixed order.
+// ===========================================================================
+
+// exclusive scan over the spans of a head, in place, one thread per quad of
+// floats walking the spans in order: forward a[s] <- sum_{s'<s} a[s'], or
+// reverse a[s] <- sum_{s'>s} a[s']
+__global__ __launch_bounds__(256) void k_bscan(float* part, float* partz, int spans, int M, int D, int reverse) {
+  const int bh = blockIdx.y;
+  const int quad = blockIdx.x * 256 + threadIdx.x;
+  const int md4 = M * D / 4, nq = md4 + M / 4;
+  if (quad >= nq) return;
+  f32x4* p;
+  size_t stride;
+  if (quad < md4) {
+    p = (f32x4*)(part + (size_t)bh * spans * M * D) + quad;
+    stride = md4;
+  } else {
+    p = (f32x4*)(partz + (size_t)bh * spans * M) + (quad - md4);
+    stride = M / 4;
+  }
+  f32x4 run = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < spans; ++k) {
+    const int sp = reverse ? spans - 1 - k : k;
+    const f32x4 v = p[(size_t)sp * stride];
+    p[(size_t)sp * stride] = run;
+    run += v;
+  }
+}
+
+struct BCausalArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* wph;       // projection operand (hi; or the float operand)
+  const void* wpl;       // lo (bf16)
+  const void* wth;       // W^T operand (hi)
+  const void* wtl;       // W^T operand (lo, bf16)
+  const float* pre;      // [BH][spans][M][D] exclusive span prefix (query side) or suffix (key side)
+  const float* prez;     // [BH][spans][M]
+  const float* lg;       // key side: log2 D_i [BH][L]
+  const float* cw;       // key side: c_i [BH][L]
+  float* lg_out;         // query side outputs
+  float* cw_out;
+  void* dx;              // dQ (query side) or dK (key side)
+  void* dy;              // dV (key side)
+  float* acc;            // [BH][L][2D+2] sums carried between feature groups
+  int L, M, H, Hw, spans, span_len, fgroups;
+  float eps;
+};
+
+template <class Tr, int D>
+struct BCLds {
+  using E = typename Tr::elem;
+  static constexpr int C = 32;
+  static constexpr int RS = Rows<D, sizeof(E)>::RS;
+  static constexpr int RSR = D + 4;                     // reduction rows (floats)
+  static constexpr int kQ = 0, kK = C * RS, kV = 2 * C * RS, kG = 3 * C * RS;
+  static constexpr int kBq = 4 * C * RS, kBk = kBq + C * 4, kC = kBk + C * 4;
+  static constexpr int kZ = kC + C * 4;                 // per wave: 32 floats (z or r of its features)
+  static constexpr int kRed = kZ + 4 * 32 * 4;          // per wave: C x RSR floats
+  static constexpr int kRedS = kRed + 4 * C * RSR * 4;  // per wave: C x 2 floats
+  static constexpr int kTotal = kRedS + 4 * C * 2 * 4;
+};
+
+// B operand over d in c-row order (k-step s2 of d block db) from one row of
+// a staged [token][d] tile: d = 32 db + crow(VPS s2 + j, h)
+template <class Tr>
+__device__ __forceinline__ typename Tr::frag crow_frag(const char* row, int db, int s2, int hh) {
+  if constexpr (Tr::VPS == 8) {
+    const char* p = row + (32 * db + 16 * s2 + 4 * hh) * 2;
+    const u32x2 a = *(const u32x2*)p, b = *(const u32x2*)(p + 16);
+    return u32x4{a[0], a[1], b[0], b[1]};
+  } else {
+    return *(const float*)(row + (32 * db + crow(s2, hh)) * 4);
+  }
+}
+
+// constant operand [k][n] of k-step s: 1 where pred(k = crow(VPS s + j, h), n = lane) holds
+template <class Tr, class P>
+__device__ __forceinline__ typename Tr::frag const_frag(int s, int lane, P pred) {
+  const int hh = lane >> 5, n = lane & 31;
+  if constexpr (Tr::VPS == 8) {
+    u32x4 f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned lo = pred(crow(8 * s + 2 * k, hh), n) ? 0x3f80u : 0u;
+      const unsigned hi = pred(crow(8 * s + 2 * k + 1, hh), n) ? 0x3f800000u : 0u;
+      f[k] = lo | hi;
+    }
+    return f;
+  } else {
+    return pred(crow(s, hh), n) ? 1.f : 0.f;
+  }
+}
+
+// products with split operands: a (split) x b, a x b (split), a x b (both split)
+template <class Tr>
+__device__ __forceinline__ f32x16 mma_sa(const typename Tr::frag (&a)[Bw<Tr>::NS], typename Tr::frag b, f32x16 c) {
+#pragma unroll
+  for (int p = 0; p < Bw<Tr>::NS; ++p) c = Tr::mma(a[p], b, c);
+  return c;
+}
+template <class Tr>
+__device__ __forceinline__ f32x16 mma_sb(typename Tr::frag a, const typename Tr::frag (&b)[Bw<Tr>::NS], f32x16 c) {
+#pragma unroll
+  for (int p = 0; p < Bw<Tr>::NS; ++p) c = Tr::mma(a, b[p], c);
+  return c;
+}
+template <class Tr>
+__device__ __forceinline__ f32x16 mma_ss(const typename Tr::frag (&a)[Bw<Tr>::NS],
+                                         const typename Tr::frag (&b)[Bw<Tr>::NS], f32x16 c) {
+  c = Tr::mma(a[0], b[0], c);
+  if constexpr (Bw<Tr>::NS == 2) {
+    c = Tr::mma(a[0], b[1], c);
+    c = Tr::mma(a[1], b[0], c);
+  }
+  return c;
+}
+
+// values of a per-feature array at the accumulator rows crow(r, h)
+__device__ __forceinline__ f32x16 rows_of(const float* v, int hh) {
+  f32x16 out;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 x = *(const f32x4*)(v + 8 * g + 4 * hh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * g + j] = x[j];
+  }
+  return out;
+}
+
+// MODE kQ1: the query side's first walk -- D_i = phi(q_i).z_i + eps and
+//            s_i = phi(q_i).y_i, written as log2 D_i and c_i = -s_i/D_i;
+// MODE kQ2: its second walk -- per feature u = y - z s_i/D_i (float32, where
+//            the difference cancels), dq_i = (W^T (phi(q_i) * u) - (s_i eps/D_i) q_i)/D_i;
+// MODE kK:  the key side, walking the chunks of a span in reverse.
+constexpr int kQ1 = 0, kQ2 = 1, kK = 2;
+
+template <class Tr, int D, int MODE>
+__global__ __launch_bounds__(256) void k_bcausal(BCausalArgs a) {
+  using E = typename Tr::elem;
+  using F = typename Tr::frag;
+  using SP = Bw<Tr>;
+  using LY = BCLds<Tr, D>;
+  constexpr bool QSIDE = MODE != kK;
+  constexpr int C = LY::C;
+  constexpr int NKD = D / Tr::KS;
+  constexpr int NDB = D / 32;
+  constexpr int NKT = 32 / Tr::KS;
+  constexpr int VPS = Tr::VPS;
+  constexpr int RS = LY::RS, RSR = LY::RSR;
+  constexpr int WES = VPS == 8 ? 2 : 4;
+  constexpr int NKG = D * WES / 32;
+  constexpr int DP = D / 8;                              // outputs per thread in the reductions
+  constexpr int AW = 2 * D + 2;                          // floats per token of the carried sums
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* sQ = smem + LY::kQ;
+  char* sK = smem + LY::kK;
+  char* sV = smem + LY::kV;
+  char* sG = smem + LY::kG;
+  float* sBq = (float*)(smem + LY::kBq);
+  float* sBk = (float*)(smem + LY::kBk);
+  float* sC = (float*)(smem + LY::kC);
+  float* sRed = (float*)(smem + LY::kRed);
+  float* sRedS = (float*)(smem + LY::kRedS);
+
+  const int span = blockIdx.x, bh = blockIdx.y;
+  const int head = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  float* sZ = (float*)(smem + LY::kZ) + w * 32;
+  const int nfb = a.M >> 5;
+  const size_t hoff = (size_t)bh * a.L * D;
+  const E* Qg = (const E*)a.q + hoff;
+  const E* Kg = (const E*)a.k + hoff;
+  const E* Vg = (const E*)a.v + hoff;
+  const E* Gg = (const E*)a.g + hoff;
+  const int hw = a.Hw == 1 ? 0 : head;
+  const float half_ln_m = 0.5f * logf((float)a.M);
+  const int t0 = span * a.span_len;
+  const int t1 = min(a.L, t0 + a.span_len);
+  const int nch = t0 < t1 ? (t1 - t0 + C - 1) / C : 0;
+  const E* wth = (const E*)a.wth + (size_t)hw * a.M * D;
+  const E* wtl = (const E*)a.wtl + (size_t)hw * a.M * D;
+
+  F ident[NKT], tri[NKT];
+#pragma unroll
+  for (int s2 = 0; s2 < NKT; ++s2) {
+    ident[s2] = const_frag<Tr>(s2, lane, [](int k, int n) { return k == n; });
+    tri[s2] = const_frag<Tr>(s2, lane, [](int k, int n) { return k <= n; });   // key k <= query n
+  }
+  // W^T operand (hi, lo) of block fb, k-step s2, d block db (lane = d)
+  auto wt_frag = [&](int fb, int s2, int db, F (&wt)[SP::NS]) {
+    const size_t e = (((((size_t)fb * NKT + s2) * NDB + db) * 2 + hh) * 32 + l32) * VPS;
+    if constexpr (VPS == 8) {
+      wt[0] = *(const u32x4*)(wth + e);
+      if constexpr (SP::NS == 2) wt[1] = *(const u32x4*)(wtl + e);
+    } else {
+      wt[0] = wth[e];
+    }
+  };
+
+  for (int fg = 0; fg < a.fgroups; ++fg) {
+    const int fb = fg * 4 + w;
+    const bool valid = fb < nfb;
+    const int fbs = valid ? fb : 0;
+    // projection operand of this wave's block (lane = feature)
+    F wf[SP::NS][NKD];
+#pragma unroll
+    for (int p = 0; p < SP::NS; ++p) {
+      const char* base = (const char*)(p == 0 ? a.wph : a.wpl) + ((size_t)hw * nfb + fbs) * NKG * 2 * 32 * 16;
+      if constexpr (WES == 2) {
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) wf[p][s] = *(const u32x4*)(base + ((s * 2 + hh) * 32 + l32) * 16);
+      } else {
+#pragma unroll
+        for (int gk = 0; gk < NKG; ++gk) {
+          const f32x4 v = *(const f32x4*)(base + ((gk * 2 + hh) * 32 + l32) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wf[p][4 * gk + j] = v[j];
+        }
+      }
+    }
+    // state of this block from the span prefix (query side: S^T, rows d, lane f;
+    // key side: R^T (rows d, lane f) and R (rows f, lane d)) and z or r
+    const float* pre = a.pre + ((size_t)bh * a.spans + span) * a.M * D;
+    f32x16 st[NDB], st2[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st[db][r] = valid ? pre[(size_t)(fbs * 32 + l32) * D + db * 32 + crow(r, hh)] : 0.f;
+        if constexpr (!QSIDE) st2[db][r] = valid ? pre[(size_t)(fbs * 32 + crow(r, hh)) * D + db * 32 + l32] : 0.f;
+      }
+    float zreg = valid ? a.prez[((size_t)bh * a.spans + span) * a.M + fbs * 32 + l32] : 0.f;
+    sZ[l32] = zreg;
+
+    TileLoader<E, D, C, 256> lq, lk, lv, lg_;
+    auto chunk0 = [&](int ci) { return t0 + ci * C; };
+    auto prefetch = [&](int ci) {
+      const int c0 = chunk0(ci);
+      lq.load(Qg + (size_t)c0 * D, t1 - c0, tid);
+      lk.load(Kg + (size_t)c0 * D, t1 - c0, tid);
+      lv.load(Vg + (size_t)c0 * D, t1 - c0, tid);
+      lg_.load(Gg + (size_t)c0 * D, t1 - c0, tid);
+    };
+    if (nch > 0) prefetch(QSIDE ? 0 : nch - 1);
+    for (int it = 0; it < nch; ++it) {
+      const int ci = QSIDE ? it : nch - 1 - it;
+      const int c0 = chunk0(ci);
+      const int nv = min(C, t1 - c0);
+      __syncthreads();                                   // the previous chunk's reductions are done
+      lq.store_proj(sQ, tid);
+      lk.store_proj(sK, tid);
+      lv.store(sV, tid);
+      lg_.store(sG, tid);
+      lk.row_bias(sBk, tid, nv, half_ln_m);
+      lq.row_bias(sBq, tid, nv, half_ln_m);
+      if constexpr (MODE != kQ1) {
+        // per-token log2 D_i and c_i of the first walk: the key side divides
+        // the query features by D_i (bias - log2 D_i) and weights them by c_i;
+        // the second query walk uses s_i/D_i = -c_i
+        if (tid >= 64 && tid < 64 + C) {
+          const int r = tid - 64;
+          const bool ok = r < nv;
+          sC[r] = ok ? a.cw[(size_t)bh * a.L + c0 + r] : 0.f;
+          if constexpr (MODE == kK) sRedS[r] = ok ? a.lg[(size_t)bh * a.L + c0 + r] : 0.f;
+        }
+      }
+      __syncthreads();
+      if constexpr (MODE == kK) {
+        if (tid < C) sBq[tid] -= sRedS[tid];             // rows past nv stay -inf
+        __syncthreads();
+      }
+      if (it + 1 < nch) prefetch(QSIDE ? ci + 1 : ci - 1);
+
+      f32x16 r1[NDB], r2[NDB];                          // per-token partial outputs (rows d, lane token)
+      float ps1 = 0.f, ps2 = 0.f;                       // per-token partial scalars
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        r1[db] = zero16();
+        r2[db] = zero16();
+      }
+      if (valid) {
+        if constexpr (QSIDE) {
+          // phi(Q)^T (rows f, lane i) and phi(K) (rows j, lane f)
+          f32x16 pq = zero16(), pk;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 b4 = *(const f32x4*)(sBk + 8 * g + 4 * hh);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pk[4 * g + j] = b4[j];
+          }
+#pragma unroll
+          for (int s = 0; s < NKD; ++s) {
+            const F qf = row_frag<Tr, D>(sQ + l32 * RS, hh, s);
+            const F kf = row_frag<Tr, D>(sK + l32 * RS, hh, s);
+#pragma unroll
+            for (int p = 0; p < SP::NS; ++p) {
+              pq = Tr::pmma(wf[p][s], qf, pq);
+              pk = Tr::pmma(kf, wf[p][s], pk);
+            }
+          }
+          const float bq = sBq[l32];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pq[r] = exp2_fast(pq[r] + bq);
+            pk[r] = exp2_fast(pk[r]);
+          }
+          // B[j][i] = v_j . g_i for j <= i (rows j, lane i)
+          f32x16 bm = zero16();
+#pragma unroll
+          for (int s = 0; s < NKD; ++s)
+            bm = Tr::mma(row_frag<Tr, D>(sV + l32 * RS, hh, s), row_frag<Tr, D>(sG + l32 * RS, hh, s), bm);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (crow(r, hh) > l32) bm[r] = 0.f;
+          // Y^T = S^T-operand x G + phi(K)^T B;  Z^T = z + phi(K)^T T (rows f, lane i)
+          f32x16 y = zero16(), z = rows_of(sZ, hh);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < NKT; ++s2) {
+              F sf[SP::NS];
+              SP::split(st[db], s2, sf);
+              y = mma_sa<Tr>(sf, crow_frag<Tr>(sG + l32 * RS, db, s2, hh), y);
+            }
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F kf[SP::NS], bf[SP::NS];
+            SP::split(pk, s2, kf);
+            SP::split(bm, s2, bf);
+            y = mma_ss<Tr>(kf, bf, y);
+            z = mma_sa<Tr>(kf, tri[s2], z);
+          }
+          if constexpr (MODE == kQ1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              ps1 = fmaf(pq[r], z[r], ps1);
+              ps2 = fmaf(pq[r], y[r], ps2);
+            }
+          } else {
+            // u = y - z s/D in float32, then dq^T += W^T (phi * u) (rows d, lane i)
+            const float ratio = -sC[l32];
+            f32x16 gq;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) gq[r] = pq[r] * (y[r] - z[r] * ratio);
+#pragma unroll
+            for (int s2 = 0; s2 < NKT; ++s2) {
+              F gf[SP::NS];
+              SP::split(gq, s2, gf);
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                F wt[SP::NS];
+                wt_frag(fbs, s2, db, wt);
+                r1[db] = mma_ss<Tr>(wt, gf, r1[db]);
+              }
+            }
+          }
+          // state update: S^T += V^T phi(K), z += phi(K)^T 1
+          float zc = 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F kf[SP::NS];
+            SP::split(pk, s2, kf);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) st[db] = mma_sb<Tr>(col_frag<Tr, RS>(sV, 0, db * 32, s2, lane), kf, st[db]);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) zc += pk[r];
+          zreg += half_sum(zc);
+          sZ[l32] = zreg;                                // read by this wave's next chunk
+        } else {
+          // phi(K)^T, phi'(Q)^T (rows f, lane token); phi'(Q) (rows i, lane f)
+          f32x16 pk = zero16(), pqt = zero16();
+#pragma unroll
+          for (int s = 0; s < NKD; ++s) {
+            const F qf = row_frag<Tr, D>(sQ + l32 * RS, hh, s);
+            const F kf = row_frag<Tr, D>(sK + l32 * RS, hh, s);
+#pragma unroll
+            for (int p = 0; p < SP::NS; ++p) {
+              pqt = Tr::pmma(wf[p][s], qf, pqt);
+              pk = Tr::pmma(wf[p][s], kf, pk);
+            }
+          }
+          const float bq = sBq[l32], bk = sBk[l32];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pqt[r] = exp2_fast(pqt[r] + bq);
+            pk[r] = exp2_fast(pk[r] + bk);
+          }
+          f32x16 pq = zero16();
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F qf[SP::NS];
+            SP::split(pqt, s2, qf);
+            pq = mma_sa<Tr>(qf, ident[s2], pq);
+          }
+          // E[i][j] = g_i . v_j + c_i for i >= j (rows i, lane j)
+          f32x16 em = rows_of(sC, hh);
+#pragma unroll
+          for (int s = 0; s < NKD; ++s)
+            em = Tr::mma(row_frag<Tr, D>(sG + l32 * RS, hh, s), row_frag<Tr, D>(sV + l32 * RS, hh, s), em);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (crow(r, hh) < l32) em[r] = 0.f;
+          // dphi(K)^T = r + R V^T + phi'(Q)^T E (rows f, lane j)
+          f32x16 u = rows_of(sZ, hh);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int s2 = 0; s2 < NKT; ++s2) {
+              F rf[SP::NS];
+              SP::split(st[db], s2, rf);
+              u = mma_sa<Tr>(rf, crow_frag<Tr>(sV + l32 * RS, db, s2, hh), u);
+            }
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F qf[SP::NS], ef[SP::NS];
+            SP::split(pq, s2, qf);
+            SP::split(em, s2, ef);
+            u = mma_ss<Tr>(qf, ef, u);
+          }
+          // scores A2[i][j] = phi'(q_i) . phi(k_j) over this block, i >= j
+          f32x16 a2 = zero16();
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) a2 = Tr::mma(CFrag<Tr>::make(pqt, s2), CFrag<Tr>::make(pk, s2), a2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (crow(r, hh) < l32) a2[r] = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            u[r] *= pk[r];
+            ps1 += u[r];
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F gf[SP::NS];
+            SP::split(u, s2, gf);
+            const F kf = CFrag<Tr>::make(pk, s2);
+            const F af = CFrag<Tr>::make(a2, s2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              F wt[SP::NS];
+              wt_frag(fbs, s2, db, wt);
+              r1[db] = mma_ss<Tr>(wt, gf, r1[db]);                                       // dk^T
+              r2[db] = Tr::mma(CFrag<Tr>::make(st2[db], s2), kf, r2[db]);               // R^T phi(K)
+              r2[db] = Tr::mma(col_frag<Tr, RS>(sG, 0, db * 32, s2, lane), af, r2[db]); // G^T A2
+            }
+          }
+          // state update: R^T += G^T phi'(Q), R += phi'(Q)^T G, r += phi'(Q)^T c
+#pragma unroll
+          for (int s2 = 0; s2 < NKT; ++s2) {
+            F qf[SP::NS];
+            SP::split(pq, s2, qf);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const F gcol = col_frag<Tr, RS>(sG, 0, db * 32, s2, lane);
+              st[db] = mma_sb<Tr>(gcol, qf, st[db]);
+              st2[db] = mma_sa<Tr>(qf, gcol, st2[db]);
+            }
+          }
+          const f32x16 cr = rows_of(sC, hh);
+          float rc = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) rc = fmaf(pq[r], cr[r], rc);
+          zreg += half_sum(rc);
+          sZ[l32] = zreg;
+        }
+      }
+
+      // ---- sums over the waves (fixed order) and the feature groups --------
+      // carried sums per token: [0, D) first output, [D, 2D) second, 2D and
+      // 2D+1 the two scalars
+      float* accrow = a.acc + ((size_t)bh * a.L + c0) * AW;
+      const int tq = tid >> 3, d0 = (tid & 7) * DP;
+      constexpr int NROUND = MODE == kQ1 ? 0 : (MODE == kQ2 ? 1 : 2);
+      float v1[DP], v2[DP], sc1 = 0.f, sc2 = 0.f;
+      {
+        const float a1 = half_sum(ps1), a2s = half_sum(ps2);
+        if (hh == 0) {
+          sRedS[(w * C + l32) * 2] = a1;
+          sRedS[(w * C + l32) * 2 + 1] = a2s;
+        }
+      }
+#pragma unroll
+      for (int round = 0; round < NROUND; ++round) {
+        f32x16 (&rr)[NDB] = round == 0 ? r1 : r2;
+        float* rrow = sRed + (size_t)w * C * RSR + l32 * RSR;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(rrow + db * 32 + 8 * g + 4 * hh) =
+                f32x4{rr[db][4 * g], rr[db][4 * g + 1], rr[db][4 * g + 2], rr[db][4 * g + 3]};
+        __syncthreads();
+        float* vv = round == 0 ? v1 : v2;
+#pragma unroll
+        for (int j = 0; j < DP; ++j) vv[j] = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float* src = sRed + (size_t)ww * C * RSR + tq * RSR + d0;
+#pragma unroll
+          for (int j = 0; j < DP; j += 4) {
+            const f32x4 x = *(const f32x4*)(src + j);
+            vv[j] += x[0];
+            vv[j + 1] += x[1];
+            vv[j + 2] += x[2];
+            vv[j + 3] += x[3];
+          }
+        }
+        if (a.fgroups > 1 && tq < nv) {
+          float* ar = accrow + (size_t)tq * AW + round * D + d0;
+          if (fg > 0) {
+#pragma unroll
+            for (int j = 0; j < DP; ++j) vv[j] += ar[j];
+          }
+          if (fg + 1 < a.fgroups) {
+#pragma unroll
+            for (int j = 0; j < DP; ++j) ar[j] = vv[j];
+          }
+        }
+        if (round + 1 < NROUND) __syncthreads();         // before the next round overwrites sRed
+      }
+      if constexpr (NROUND == 0) __syncthreads();        // the scalars are in LDS
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        sc1 += sRedS[(ww * C + tq) * 2];
+        sc2 += sRedS[(ww * C + tq) * 2 + 1];
+      }
+      if (a.fgroups > 1 && tq < nv && MODE != kQ2) {
+        float* as = accrow + (size_t)tq * AW + 2 * D;
+        if (fg > 0) {
+          sc1 += as[0];
+          sc2 += as[1];
+        }
+        if (fg + 1 < a.fgroups && (tid & 7) == 0) {
+          as[0] = sc1;
+          as[1] = sc2;
+        }
+      }
+      if (fg + 1 == a.fgroups && tq < nv) {
+        const size_t tok = (size_t)c0 + tq;
+        if constexpr (MODE == kQ1) {
+          if ((tid & 7) == 0) {
+            const float den = sc1 + a.eps;
+            a.lg_out[(size_t)bh * a.L + tok] = log2f(den);
+            a.cw_out[(size_t)bh * a.L + tok] = -(sc2 / den);
+          }
+        } else if constexpr (MODE == kQ2) {
+          E* out = (E*)a.dx + hoff + tok * D + d0;
+          const E* xr = Qg + tok * D + d0;
+          const float inv = exp2f(-a.lg[(size_t)bh * a.L + tok]);
+          const float ratio = -a.cw[(size_t)bh * a.L + tok];
+#pragma unroll
+          for (int j = 0; j < DP; ++j) out[j] = (E)((v1[j] - ratio * a.eps * (float)xr[j]) * inv);
+        } else {
+          E* out = (E*)a.dx + hoff + tok * D + d0;
+          const E* xr = Kg + tok * D + d0;
+          E* outv = (E*)a.dy + hoff + tok * D + d0;
+#pragma unroll
+          for (int j = 0; j < DP; ++j) {
+            out[j] = (E)(v1[j] - sc1 * (float)xr[j]);
+            outv[j] = (E)v2[j];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class Tr, int D>
+static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s) {
+  using E = typename Tr::elem;
+  const BwdBuffers b = bwd_buffers(p, t.ws);
+  const int nrows = p.Hw * p.M;
+  {
+    constexpr int WES = Tr::VPS == 8 ? 2 : 4;
+    const int n = nrows * D / (16 / WES) + nrows * D / Tr::VPS;
+    const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    timing_begin(FAVOR_KERNEL_BWD_PREP, s);
+    hipLaunchKernelGGL((k_bprep<Tr>), dim3(blocks), dim3(256), 0, s, t.w, b.wph, b.wpl, b.wt,
+                       Tr::VPS == 8 ? b.wtl : nullptr, nrows, D);
+    timing_end(FAVOR_KERNEL_BWD_PREP, s);
+  }
+  const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
+  const size_t rlds = BRedLds<Tr, D>::kTotal;
+  const int nq = (p.M * D + p.M) / 4;
+  const dim3 sgrid((nq + 255) / 256, p.BH);
+  const size_t clds = BCLds<Tr, D>::kTotal;
+  const int fgroups = (p.M / 32 + 3) / 4;
+  if (fgroups > 1 && p.boff_acc == p.btotal) return hipErrorInvalidValue;   // no room for the sums
+  BCausalArgs ca{t.q, t.k, t.v, t.g, b.wph, b.wpl, b.wt, b.wtl, b.part, b.partz, b.lg, b.cw, b.lg, b.cw,
+                 t.dq, nullptr, b.acc, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, fgroups, t.eps};
+  // span aggregates of phi(K) V^T, phi(K) -> exclusive prefixes
+  {
+    BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len};
+    timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
+    hipLaunchKernelGGL((k_bred<Tr, D, false>), rgrid, dim3(256), rlds, s, a);
+    timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
+    timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
+    hipLaunchKernelGGL(k_bscan, sgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, 0);
+    timing_end(FAVOR_KERNEL_BWD_COMBINE, s);
+  }
+  // query side: log2 D_i and c_i (the lg and cw arrays), then dQ
+  timing_begin(FAVOR_KERNEL_BWD_Q, s);
+  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ1>), dim3(p.bsplits, p.BH), dim3(256), clds, s, ca);
+  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ2>), dim3(p.bsplits, p.BH), dim3(256), clds, s, ca);
+  timing_end(FAVOR_KERNEL_BWD_Q, s);
+  // span aggregates of phi'(Q) G^T, phi'(Q) c -> exclusive suffixes
+  {
+    BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len};
+    timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
+    hipLaunchKernelGGL((k_bred<Tr, D, true>), rgrid, dim3(256), rlds, s, a);
+    timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
+    timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
+    hipLaunchKernelGGL(k_bscan, sgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, 1);
+    timing_end(FAVOR_KERNEL_BWD_COMBINE, s);
+  }
+  // key side
+  ca.dx = t.dk;
+  ca.dy = t.dv;
+  timing_begin(FAVOR_KERNEL_BWD_K, s);
+  hipLaunchKernelGGL((k_bcausal<Tr, D, kK>), dim3(p.bsplits, p.BH), dim3(256), clds, s, ca);
+  timing_end(FAVOR_KERNEL_BWD_K, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_causal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s) {
+  if (p.dt == FAVOR_BF16) {
+    switch (p.D) {
+      case 32: return bwd_causal_t<TrBF16, 32>(p, t, s);
+      case 64: return bwd_causal_t<TrBF16, 64>(p, t, s);
+      case 128: return bwd_causal_t<TrBF16, 128>(p, t, s);
+    }
+  } else {
+    switch (p.D) {
+      case 32: return bwd_causal_t<TrF32, 32>(p, t, s);
+      case 64: return bwd_causal_t<TrF32, 64>(p, t, s);
+      case 128: return bwd_causal_t<TrF32, 128>(p, t, s);
     }
   }
   return hipErrorInvalidValue;

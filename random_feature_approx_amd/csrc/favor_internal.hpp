@@ -36,8 +36,8 @@ struct Plan {
   // backward pass: its reductions (4 waves of one feature block each) and
   // its workspace (a separate layout, sized by favor_bwd_workspace_bytes)
   int bsplits, bsplit_len, bfgroups;
-  size_t boff_part, boff_partz, boff_zf, boff_lg, boff_cw, boff_wph, boff_wpl, boff_wt, boff_rows_hi,
-      boff_rows_lo, boff_op, btotal;
+  size_t boff_part, boff_partz, boff_zf, boff_lg, boff_cw, boff_wph, boff_wpl, boff_wt, boff_wtl, boff_rows_hi,
+      boff_rows_lo, boff_op, boff_acc, btotal;
 };
 
 bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus);
@@ -75,6 +75,7 @@ hipError_t launch_features(const Plan& p, const void* x, const float* w, float* 
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
+hipError_t launch_causal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
                          hipStream_t s);
 
