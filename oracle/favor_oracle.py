@@ -13,7 +13,8 @@ Everything here is plain NumPy in float64, written from the three source pages:
   performer-2020): section 核心要点 (key points: kernel view, reordering,
   linearised denominator), the 换顺序 diagram and 案例 2 (causal prefix sum).
 * "Linear Attention > Kernel Feature Maps" (P3): the softmax-kernel equation
-  and section 4, positive random features.
+  and section 4, positive random features; sections 1-3 (ELU + 1, ReLU,
+  random Fourier features) for the feature-map variants.
 
 Conventions: X is (L, d) per head, the projection W is (m, d) with rows
 omega_i, and every function takes the values actually handed to the device,
@@ -35,7 +36,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "favor_features", "attn_quadratic", "attn_noncausal", "attn_causal",
+    "favor_features", "feature_map", "FEATURE_MAPS", "attn_quadratic", "attn_noncausal", "attn_causal",
     "attn_rows", "softmax_attention", "per_head", "head_projection",
     "favor_features_vjp", "attn_noncausal_grad", "attn_causal_grad", "per_head_grad",
 ]
@@ -57,16 +58,50 @@ def favor_features(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     return np.exp(proj - half_sq_norm) / np.sqrt(m)
 
 
-def attn_quadratic(q, k, v, w, eps: float = 1e-6, causal: bool = False) -> np.ndarray:
+FEATURE_MAPS = ("positive", "elu1", "relu", "trig")
+
+
+def feature_map(x: np.ndarray, w: np.ndarray, kind: str = "positive") -> np.ndarray:
+    """The feature maps of P3 (sections 1-4), each applied to the projection
+    p = x W^T (rows omega_i of W; with W the identity, m = d, the first two
+    act on x itself as the page writes them):
+
+    * "positive": FAVOR+ positive random features (favor_features);
+    * "elu1": ELU(p) + 1, i.e. p + 1 where p > 0 and exp(p) where p <= 0;
+    * "relu": max(0, p);
+    * "trig": random Fourier features, 2m outputs
+      (1/sqrt(m)) [sin(omega_1.x), cos(omega_1.x), ..., sin(omega_m.x), cos(omega_m.x)].
+
+    x: (..., d), w: (m, d).  Returns (..., m) or, for "trig", (..., 2m) float64.
+    """
+    if kind == "positive":
+        return favor_features(x, w)
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    p = x @ w.T
+    if kind == "elu1":
+        return np.where(p > 0, p + 1.0, np.exp(np.minimum(p, 0.0)))
+    if kind == "relu":
+        return np.maximum(p, 0.0)
+    if kind == "trig":
+        out = np.empty(p.shape[:-1] + (2 * p.shape[-1],))
+        out[..., 0::2] = np.sin(p)
+        out[..., 1::2] = np.cos(p)
+        return out / np.sqrt(w.shape[0])
+    raise ValueError(f"unknown feature map {kind!r}")
+
+
+def attn_quadratic(q, k, v, w, eps: float = 1e-6, causal: bool = False, kind: str = "positive") -> np.ndarray:
     """The definition: A = phi(Q) phi(K)^T (an L x L matrix of kernel
     estimates), optionally masked to keys j <= query i, then
     O = (A V) / (A 1 + eps) row by row.
 
     This is the left-to-right product order of the 换顺序 diagram in P2 (the
-    order FAVOR+ avoids), with the normaliser of P2's key points.
+    order FAVOR+ avoids), with the normaliser of P2's key points; `kind`
+    selects the feature map (feature_map).
     """
-    fq = favor_features(q, w)
-    fk = favor_features(k, w)
+    fq = feature_map(q, w, kind)
+    fk = feature_map(k, w, kind)
     a = fq @ fk.T
     if causal:
         a = np.tril(a)
@@ -75,13 +110,13 @@ def attn_quadratic(q, k, v, w, eps: float = 1e-6, causal: bool = False) -> np.nd
     return num / den[:, None]
 
 
-def attn_noncausal(q, k, v, w, eps: float = 1e-6) -> np.ndarray:
+def attn_noncausal(q, k, v, w, eps: float = 1e-6, kind: str = "positive") -> np.ndarray:
     """Reassociated non-causal attention, in the order of P1 In[25] and the
     right-hand side of P2's 换顺序 diagram: first the m x d state
     M = phi(K)^T V and the key sum z = phi(K)^T 1, then
     O = (phi(Q) M) / (phi(Q) z + eps)."""
-    fq = favor_features(q, w)
-    fk = favor_features(k, w)
+    fq = feature_map(q, w, kind)
+    fk = feature_map(k, w, kind)
     v = np.asarray(v, dtype=np.float64)
     state = fk.T @ v
     key_sum = fk.sum(axis=0)
@@ -90,7 +125,7 @@ def attn_noncausal(q, k, v, w, eps: float = 1e-6) -> np.ndarray:
     return num / den[:, None]
 
 
-def attn_causal(q, k, v, w, eps: float = 1e-6) -> np.ndarray:
+def attn_causal(q, k, v, w, eps: float = 1e-6, kind: str = "positive") -> np.ndarray:
     """Causal attention by the running prefix sum of P2 案例 2: walking the
     tokens in order, S_i = S_{i-1} + phi(k_i) v_i^T (an m x d matrix) and
     z_i = z_{i-1} + phi(k_i); the output is
@@ -98,8 +133,8 @@ def attn_causal(q, k, v, w, eps: float = 1e-6) -> np.ndarray:
 
     One Python step per token; O(L m d) time and O(m d) state.
     """
-    fq = favor_features(q, w)
-    fk = favor_features(k, w)
+    fq = feature_map(q, w, kind)
+    fk = feature_map(k, w, kind)
     v = np.asarray(v, dtype=np.float64)
     L, d = v.shape
     m = fq.shape[1]
@@ -113,7 +148,7 @@ def attn_causal(q, k, v, w, eps: float = 1e-6) -> np.ndarray:
     return out
 
 
-def attn_rows(q, k, v, w, rows, eps: float = 1e-6, causal: bool = False) -> np.ndarray:
+def attn_rows(q, k, v, w, rows, eps: float = 1e-6, causal: bool = False, kind: str = "positive") -> np.ndarray:
     """Selected output rows by the definition: for each query i,
     a_j = phi(q_i) . phi(k_j) over the keys it sees (all keys, or j <= i when
     causal), o_i = sum_j a_j v_j / (sum_j a_j + eps).
@@ -121,8 +156,8 @@ def attn_rows(q, k, v, w, rows, eps: float = 1e-6, causal: bool = False) -> np.n
     Used for sampled-row checks at sizes where the full output is too big.
     """
     rows = np.asarray(rows, dtype=np.int64)
-    fq = favor_features(np.asarray(q)[rows], w)
-    fk = favor_features(k, w)
+    fq = feature_map(np.asarray(q)[rows], w, kind)
+    fk = feature_map(k, w, kind)
     v = np.asarray(v, dtype=np.float64)
     out = np.empty((len(rows), v.shape[1]))
     for r, i in enumerate(rows):
