@@ -114,6 +114,52 @@ favor_status favor_attn_causal(const void* Q, const void* K, const void* V,
                                favor_dtype dtype, void* ws, size_t ws_bytes,
                                void* stream);
 
+/*
+ * Feature maps ("Linear Attention > Kernel Feature Maps", sections 1-4), all
+ * applied to the projection p = W x (with W the d x d identity, m = d, the
+ * first two act on x itself as the page writes them):
+ *   FAVOR_FMAP_POSITIVE  FAVOR+: exp(p - |x|^2/2)/sqrt(m)         (section 4)
+ *   FAVOR_FMAP_ELU1      ELU(p) + 1: p + 1 for p > 0, exp(p) else  (section 1)
+ *   FAVOR_FMAP_RELU      max(0, p)                                 (section 2)
+ *   FAVOR_FMAP_TRIG      random Fourier features, 2m of them:
+ *                        (1/sqrt(m)) [sin p_1, cos p_1, ..., sin p_m, cos p_m]
+ *                        (section 3; they estimate exp(-|q-k|^2/2))
+ * The trig features are not positive: the denominator phi(q).sum phi(k) + eps
+ * can come near zero (the performer-2020 notes' pitfalls); results are then
+ * ill-conditioned but computed as defined.  bf16 inputs: W's scaled copy is
+ * rounded to fp16 for the projection as for FAVOR+ (scale 1, or 1/(2 pi)
+ * for the trig map, whose sine and cosine take revolutions).
+ */
+typedef enum {
+  FAVOR_FMAP_POSITIVE = 0,
+  FAVOR_FMAP_ELU1 = 1,
+  FAVOR_FMAP_RELU = 2,
+  FAVOR_FMAP_TRIG = 3
+} favor_feature_map;
+
+/* Workspace of favor_attn_fmap for these shapes (m = rows of W). */
+size_t favor_workspace_bytes_fmap(int B, int H, int L, int d, int m, int causal,
+                                  favor_feature_map fmap, favor_dtype dtype);
+
+/* Phi = phi(X) for the chosen map, float32 [B, H, L, m] or, for the trig
+ * map, [B, H, L, 2m] in the page's interleaved order. */
+favor_status favor_features_fmap(const void* X, const float* W, int Hw, float* Phi,
+                                 int B, int H, int L, int d, int m,
+                                 favor_feature_map fmap, favor_dtype dtype, void* stream);
+
+/*
+ * Attention (non-causal or causal, as favor_attn) with the chosen feature
+ * map: O = phi(Q) (phi(K)^T V) / (phi(Q) (phi(K)^T 1) + eps), causally with
+ * prefix sums.  Same arguments, shapes, errors and workspace rules as
+ * favor_attn, workspace from favor_workspace_bytes_fmap; m counts the rows
+ * of W (the trig map uses 2m features).
+ */
+favor_status favor_attn_fmap(const void* Q, const void* K, const void* V,
+                             const float* W, int Hw, void* O,
+                             int B, int H, int L, int d, int m, float eps, int causal,
+                             favor_feature_map fmap, favor_dtype dtype, void* ws,
+                             size_t ws_bytes, void* stream);
+
 /* Dispatcher: favor_attn_causal when causal != 0, else favor_attn_noncausal. */
 favor_status favor_attn(const void* Q, const void* K, const void* V,
                         const float* W, int Hw, void* O,

@@ -6,8 +6,10 @@ memory and the current stream.  There is no CPU fallback: if the library is
 missing, or the tensors are not on a HIP device, calls raise.
 
 Functions
-    features(x, w)                          phi(x) as float32 [B, H, L, m]
-    attn(q, k, v, w, causal=False, eps=1e-6) FAVOR+ attention, output like q
+    features(x, w, fmap="positive")         phi(x) as float32 [B, H, L, m] (2m for "trig")
+    attn(q, k, v, w, causal=False, eps=1e-6, fmap="positive")
+                                            attention, output like q; fmap is one of
+                                            FMAPS (FAVOR+ "positive", "elu1", "relu", "trig")
     attn_noncausal(...), attn_causal(...)    the two paths explicitly
     workspace_bytes(B, H, L, d, m, causal, dtype)
     attn_backward(q, k, v, w, g, causal=False, eps=1e-6)
@@ -22,7 +24,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal",
+__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS",
            "workspace_bytes", "attn_backward", "bwd_workspace_bytes", "FavorError", "STATUS", "KERNELS",
            "timing_start", "timing_stop"]
 
@@ -30,6 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBNAME = "libfavor.so"
 _lib = None
 
+FMAPS = {"positive": 0, "elu1": 1, "relu": 2, "trig": 3}
 STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid shape", 3: "unsupported d, m or dtype",
           4: "workspace missing or too small", 5: "HIP runtime error", 6: "internal error"}
 F32, BF16 = 0, 1
@@ -72,6 +75,12 @@ def load():
         getattr(lib, name).argtypes = attn_args
     lib.favor_attn.restype = i
     lib.favor_attn.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.favor_workspace_bytes_fmap.restype = sz
+    lib.favor_workspace_bytes_fmap.argtypes = [i, i, i, i, i, i, i, i]
+    lib.favor_features_fmap.restype = i
+    lib.favor_features_fmap.argtypes = [vp, vp, i, vp, i, i, i, i, i, i, i, vp]
+    lib.favor_attn_fmap.restype = i
+    lib.favor_attn_fmap.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.favor_bwd_workspace_bytes.restype = sz
     lib.favor_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     for name in ("favor_attn_noncausal_bwd", "favor_attn_causal_bwd"):
@@ -127,13 +136,20 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def workspace_bytes(B: int, H: int, L: int, d: int, m: int, causal: bool, dtype) -> int:
+def _fmap_code(fmap) -> int:
+    if fmap not in FMAPS:
+        raise ValueError(f"unknown feature map {fmap!r}; use one of {sorted(FMAPS)}")
+    return FMAPS[fmap]
+
+
+def workspace_bytes(B: int, H: int, L: int, d: int, m: int, causal: bool, dtype, fmap: str = "positive") -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
-    return int(load().favor_workspace_bytes(B, H, L, d, m, int(bool(causal)), code))
+    return int(load().favor_workspace_bytes_fmap(B, H, L, d, m, int(bool(causal)), _fmap_code(fmap), code))
 
 
-def features(x, w):
-    """phi(x) = exp(W x - |x|^2/2)/sqrt(m) as float32 [B, H, L, m]."""
+def features(x, w, fmap: str = "positive"):
+    """phi(x) as float32 [B, H, L, m] (FAVOR+: exp(W x - |x|^2/2)/sqrt(m));
+    [B, H, L, 2m] for the trig map, sines and cosines interleaved."""
     lib = load()
     torch = _torch()
     if x.dim() != 4:
@@ -142,16 +158,18 @@ def features(x, w):
     w, hw = _proj(w, H, (w.shape[-2], d))
     m = int(w.shape[1])
     _check_device(x, w)
-    phi = torch.empty((B, H, L, m), dtype=torch.float32, device=x.device)
-    st = lib.favor_features(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), hw,
-                            ctypes.c_void_p(phi.data_ptr()), B, H, L, d, m, _dtype_code(x), _stream())
+    code = _fmap_code(fmap)
+    phi = torch.empty((B, H, L, 2 * m if fmap == "trig" else m), dtype=torch.float32, device=x.device)
+    st = lib.favor_features_fmap(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), hw,
+                                 ctypes.c_void_p(phi.data_ptr()), B, H, L, d, m, code, _dtype_code(x), _stream())
     if st != 0:
-        raise FavorError("favor_features", st)
+        raise FavorError("favor_features_fmap", st)
     return phi
 
 
-def attn(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, workspace=None):
-    """FAVOR+ attention; returns O with the shape and dtype of q."""
+def attn(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, workspace=None, fmap: str = "positive"):
+    """Linear attention with the given feature map (FAVOR+ by default);
+    returns O with the shape and dtype of q."""
     lib = load()
     torch = _torch()
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -165,17 +183,23 @@ def attn(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, workspac
     code = _dtype_code(q)
     o = torch.empty_like(q) if out is None else out
     _check_device(o)
-    need = int(lib.favor_workspace_bytes(B, H, L, d, m, int(bool(causal)), code))
+    fcode = _fmap_code(fmap)
+    need = int(lib.favor_workspace_bytes_fmap(B, H, L, d, m, int(bool(causal)), fcode, code))
     if need == 0:
-        raise FavorError("favor_workspace_bytes", 2)
+        raise FavorError("favor_workspace_bytes_fmap", 2)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    fn = lib.favor_attn_causal if causal else lib.favor_attn_noncausal
-    st = fn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-            ctypes.c_void_p(w.data_ptr()), hw, ctypes.c_void_p(o.data_ptr()), B, H, L, d, m,
-            float(eps), code, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream())
+    ptrs = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(w.data_ptr()), hw, ctypes.c_void_p(o.data_ptr()), B, H, L, d, m, float(eps))
+    tail = (ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream())
+    if fcode == 0:
+        name = "favor_attn_causal" if causal else "favor_attn_noncausal"
+        st = getattr(lib, name)(*ptrs, code, *tail)
+    else:
+        name = "favor_attn_fmap"
+        st = lib.favor_attn_fmap(*ptrs, int(bool(causal)), fcode, code, *tail)
     if st != 0:
-        raise FavorError("favor_attn_causal" if causal else "favor_attn_noncausal", st)
+        raise FavorError(name, st)
     return o
 
 

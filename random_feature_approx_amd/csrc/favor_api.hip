@@ -30,14 +30,21 @@ static favor_status check_shapes(int B, int H, int L, int d, int m, int Hw, favo
   return FAVOR_OK;
 }
 
-bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus) {
+bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus,
+               int fmap) {
   if (check_shapes(B, H, L, d, m, Hw, dt) != FAVOR_OK || num_cus <= 0) return false;
+  if (fmap < FAVOR_FMAP_POSITIVE || fmap > FAVOR_FMAP_TRIG) return false;
+  p.fmap = fmap;
+  p.Mw = m;
+  if (fmap == FAVOR_FMAP_TRIG) m *= 2;      // a sine and a cosine per row of W
   p.B = B; p.H = H; p.L = L; p.D = d; p.M = m; p.Hw = Hw; p.causal = causal ? 1 : 0; p.dt = dt;
   p.BH = B * H;
   p.esize = dt == FAVOR_BF16 ? 2 : 4;
   // reduction split: about two workgroups per compute unit, ranges of at
   // least 256 tokens, whole 64-token chunks.
-  p.fbw = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
+  // the bf16 FAVOR+ scan for d <= 64 owns two feature blocks per wave; the
+  // generic scan (other maps, widths and float32) one
+  p.fbw = (dt == FAVOR_BF16 && d <= 64 && fmap == FAVOR_FMAP_POSITIVE) ? 2 : 1;
   const int nfb = m / 32;
   p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
   p.rfbw = 1;   // two blocks per wave (4 waves) measured slower: fewer waves to hide latency
@@ -199,24 +206,38 @@ size_t favor_workspace_bytes(int B, int H, int L, int d, int m, int causal, favo
   return p.total;
 }
 
-favor_status favor_features(const void* X, const float* W, int Hw, float* Phi, int B, int H, int L, int d, int m,
-                            favor_dtype dtype, void* stream) {
+size_t favor_workspace_bytes_fmap(int B, int H, int L, int d, int m, int causal, favor_feature_map fmap,
+                                  favor_dtype dtype) {
+  Plan p;
+  if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count(), (int)fmap)) return 0;
+  return p.total;
+}
+
+favor_status favor_features_fmap(const void* X, const float* W, int Hw, float* Phi, int B, int H, int L, int d,
+                                 int m, favor_feature_map fmap, favor_dtype dtype, void* stream) {
   if (!X || !W || !Phi) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
   if (st != FAVOR_OK) return st;
+  if ((int)fmap < FAVOR_FMAP_POSITIVE || (int)fmap > FAVOR_FMAP_TRIG) return FAVOR_ERR_UNSUPPORTED;
   Plan p;
-  if (!make_plan(p, B, H, L, d, m, Hw, 0, dtype, device_cu_count())) return FAVOR_ERR_HIP;
+  if (!make_plan(p, B, H, L, d, m, Hw, 0, dtype, device_cu_count(), (int)fmap)) return FAVOR_ERR_HIP;
   return launch_features(p, X, W, Phi, (hipStream_t)stream) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+favor_status favor_features(const void* X, const float* W, int Hw, float* Phi, int B, int H, int L, int d, int m,
+                            favor_dtype dtype, void* stream) {
+  return favor_features_fmap(X, W, Hw, Phi, B, H, L, d, m, FAVOR_FMAP_POSITIVE, dtype, stream);
 }
 
 static favor_status attn_common(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
                                 int H, int L, int d, int m, float eps, int causal, favor_dtype dtype, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                size_t ws_bytes, void* stream, int fmap = FAVOR_FMAP_POSITIVE) {
   if (!Q || !K || !V || !W || !O) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
   if (st != FAVOR_OK) return st;
+  if (fmap < FAVOR_FMAP_POSITIVE || fmap > FAVOR_FMAP_TRIG) return FAVOR_ERR_UNSUPPORTED;
   Plan p;
-  if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count())) return FAVOR_ERR_HIP;
+  if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count(), fmap)) return FAVOR_ERR_HIP;
   if (!ws || ws_bytes < p.total || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
   Tensors t{Q, K, V, W, O, eps, (char*)ws};
   hipError_t e = causal ? launch_causal(p, t, (hipStream_t)stream) : launch_noncausal(p, t, (hipStream_t)stream);
@@ -333,6 +354,12 @@ favor_status favor_attn(const void* Q, const void* K, const void* V, const float
                         int L, int d, int m, float eps, int causal, favor_dtype dtype, void* ws, size_t ws_bytes,
                         void* stream) {
   return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, causal, dtype, ws, ws_bytes, stream);
+}
+
+favor_status favor_attn_fmap(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
+                             int H, int L, int d, int m, float eps, int causal, favor_feature_map fmap,
+                             favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, causal, dtype, ws, ws_bytes, stream, (int)fmap);
 }
 
 }  // extern "C"

@@ -97,6 +97,7 @@ struct CausalArgs {
   float* den;             // [BH][L]
   int L, M, H, Hw, spans, span_len, fgroups;
   float eps;
+  int Mw;                 // rows of W per head (M, or M/2 for the trig map)
 };
 
 // LDS layout (bytes), computed identically on host and device.
@@ -117,7 +118,7 @@ struct CausalLds {
   static constexpr int kTotal = kZ + 4 * FW * 4;
 };
 
-template <class Tr, int D, int FBW>
+template <class Tr, int D, int FBW, int FM>
 __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
@@ -147,8 +148,9 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
   const E* Kg = (const E*)a.k + hoff;
   const E* Vg = (const E*)a.v + hoff;
   E* Og = (E*)a.o + hoff;
-  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.Mw * D;
   const float half_ln_m = 0.5f * logf((float)a.M);
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
   const int t0 = span * a.span_len;
   const int t1 = min(a.L, t0 + a.span_len);
 
@@ -161,9 +163,9 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
     for (int i = 0; i < FBW; ++i) {
       const bool ok = fb0 + i < nfb;
       const int fbase = (ok ? fb0 + i : 0) * 32;
-      const float* wrow = wh + (size_t)(fbase + l32) * D;
+      const float* wrow = wh + (size_t)((FM == FM_TRIG ? fbase % a.Mw : fbase) + l32) * D;
 #pragma unroll
-      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D>(wrow, hh, s, ok);
+      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, ok);
       const float* pre = a.prefix + ((size_t)bh * a.spans + span) * a.M * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -186,8 +188,8 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
       lq.store_proj(sQ, tid);
       lk.store_proj(sK, tid);
       lv.store(sV, tid);
-      lq.row_bias(sBq, tid, nv, half_ln_m);
-      lk.row_bias(sBk, tid, nv, half_ln_m);
+      lq.template row_bias<FM>(sBq, tid, nv, half_ln_m);
+      lk.template row_bias<FM>(sBk, tid, nv, half_ln_m);
       __syncthreads();
       if (c0 + C < t1) {
         lq.load(Qg + (size_t)(c0 + C) * D, t1 - c0 - C, tid);
@@ -216,10 +218,11 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
           }
           // features past m (a partly filled last group) are exactly zero
           const bool fvalid = fb0 + i < nfb;
+          const bool cosine = (fb0 + i) * 32 >= a.Mw;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            aq[r] = fvalid ? exp2_fast(aq[r] + bq) : 0.f;
-            ak[r] = fvalid ? exp2_fast(ak[r] + bk) : 0.f;
+            aq[r] = fvalid ? FMap<FM>::phi(aq[r] + bq, cosine, tscale) : 0.f;
+            ak[r] = fvalid ? FMap<FM>::phi(ak[r] + bk, cosine, tscale) : 0.f;
           }
 #pragma unroll
           for (int s2 = 0; s2 < NKT; ++s2) {
@@ -731,17 +734,37 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
   }
 }
 
-template <class Tr, int D, int FBW>
+template <class Tr, int D, int FBW, int FM>
 static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
   using LY = CausalLds<Tr, D, FBW>;
   float* part = (float*)(t.ws + p.off_part);
   float* partz = (float*)(t.ws + p.off_partz);
+  if (p.fbw != FBW) return hipErrorInvalidValue;
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
-               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps};
+               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
-  hipLaunchKernelGGL((k_causal<Tr, D, FBW>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
+  hipLaunchKernelGGL((k_causal<Tr, D, FBW, FM>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
   timing_end(FAVOR_KERNEL_CAUSAL, s);
   return hipGetLastError();
+}
+
+// the other feature maps run the generic scan (one feature block per wave)
+template <int FM>
+static hipError_t causal_fmap(const Plan& p, const Tensors& t, hipStream_t s) {
+  if (p.dt == FAVOR_BF16) {
+    switch (p.D) {
+      case 32: return causal_t<TrBF16, 32, 1, FM>(p, t, s);
+      case 64: return causal_t<TrBF16, 64, 1, FM>(p, t, s);
+      case 128: return causal_t<TrBF16, 128, 1, FM>(p, t, s);
+    }
+  } else {
+    switch (p.D) {
+      case 32: return causal_t<TrF32, 32, 1, FM>(p, t, s);
+      case 64: return causal_t<TrF32, 64, 1, FM>(p, t, s);
+      case 128: return causal_t<TrF32, 128, 1, FM>(p, t, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D, int FBW, int C>
@@ -751,7 +774,7 @@ static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
   float* partz = (float*)(t.ws + p.off_partz);
   if (p.fbw != FBW) return hipErrorInvalidValue;
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
-               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps};
+               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
   hipLaunchKernelGGL((k_causal2<D, FBW, C>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
   timing_end(FAVOR_KERNEL_CAUSAL, s);
@@ -770,17 +793,24 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   timing_end(FAVOR_KERNEL_SPAN_SCAN, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  switch (p.fmap) {
+    case FM_POS: break;
+    case FM_ELU1: return causal_fmap<FM_ELU1>(p, t, s);
+    case FM_RELU: return causal_fmap<FM_RELU>(p, t, s);
+    case FM_TRIG: return causal_fmap<FM_TRIG>(p, t, s);
+    default: return hipErrorInvalidValue;
+  }
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
       case 32: return causal2_t<32, 2, 32>(p, t, s);
       case 64: return causal2_t<64, 2, 32>(p, t, s);
-      case 128: return causal_t<TrBF16, 128, 1>(p, t, s);
+      case 128: return causal_t<TrBF16, 128, 1, FM_POS>(p, t, s);
     }
   } else {
     switch (p.D) {
-      case 32: return causal_t<TrF32, 32, 1>(p, t, s);
-      case 64: return causal_t<TrF32, 64, 1>(p, t, s);
-      case 128: return causal_t<TrF32, 128, 1>(p, t, s);
+      case 32: return causal_t<TrF32, 32, 1, FM_POS>(p, t, s);
+      case 64: return causal_t<TrF32, 64, 1, FM_POS>(p, t, s);
+      case 128: return causal_t<TrF32, 128, 1, FM_POS>(p, t, s);
     }
   }
   return hipErrorInvalidValue;

@@ -14,6 +14,8 @@ namespace favor {
 struct Plan {
   int B, H, L, D, M, Hw, causal;
   favor_dtype dt;
+  int fmap;             // feature map (FM_POS, FM_ELU1, FM_RELU, FM_TRIG)
+  int Mw;               // rows of W per head; M (features) is 2 Mw for the trig map
   int BH;
   int esize;            // bytes per element of Q, K, V, O
   // K-side reduction (non-causal state, or causal span aggregates)
@@ -40,7 +42,8 @@ struct Plan {
       boff_rows_lo, boff_op, boff_acc, btotal;
 };
 
-bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus);
+bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus,
+               int fmap = 0);
 int device_cu_count();
 
 struct Tensors {

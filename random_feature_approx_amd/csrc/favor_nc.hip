@@ -28,9 +28,10 @@ struct FeatArgs {
   const float* w;
   float* phi;
   int L, M, H, Hw;
+  int Mw;               // rows of W per head (M, or M/2 for the trig map)
 };
 
-template <class Tr, int D>
+template <class Tr, int D, int FM>
 __global__ __launch_bounds__(256) void k_features(FeatArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void k_features(FeatArgs a) {
   const int tok = blockIdx.x * 128 + w * 32 + l32;
   const bool tok_ok = tok < a.L;
   const E* xrow = (const E*)a.x + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * D;
-  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.Mw * D;
   F xf[NKD];
   float ss = 0.f;
 #pragma unroll
@@ -61,20 +62,32 @@ __global__ __launch_bounds__(256) void k_features(FeatArgs a) {
     }
   }
   ss = half_sum(ss);
-  const float bias = -(0.5f * ss + 0.5f * logf((float)a.M)) * kLog2e;
+  const float bias = FMap<FM>::row_bias(ss, 0.5f * logf((float)a.M));
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
+  const int nfbw = a.Mw >> 5;
   float* out = a.phi + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * a.M;
   for (int fb = 0; fb < (a.M >> 5); ++fb) {
-    const float* wrow = wh + (size_t)(fb * 32 + l32) * D;
+    const float* wrow = wh + (size_t)((FM == FM_TRIG ? fb % nfbw : fb) * 32 + l32) * D;
+    const bool cosine = fb >= nfbw;
     f32x16 acc = zero16();
 #pragma unroll
-    for (int s = 0; s < NKD; ++s) acc = Tr::pmma(w_frag<Tr, D>(wrow, hh, s, true), xf[s], acc);
+    for (int s = 0; s < NKD; ++s) acc = Tr::pmma(w_frag<Tr, D, FM>(wrow, hh, s, true), xf[s], acc);
     if (tok_ok) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = exp2_fast(acc[4 * i + j] + bias);
-        *(f32x4*)(out + fb * 32 + 8 * i + 4 * hh) = v;
+        for (int j = 0; j < 4; ++j) v[j] = FMap<FM>::phi(acc[4 * i + j] + bias, cosine, tscale);
+        if constexpr (FM == FM_TRIG) {
+          // the page's order: feature 2i is the sine of omega_i, 2i+1 its cosine
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int f = fb * 32 + 8 * i + 4 * hh + j;
+            out[cosine ? 2 * (f - a.Mw) + 1 : 2 * f] = v[j];
+          }
+        } else {
+          *(f32x4*)(out + fb * 32 + 8 * i + 4 * hh) = v;
+        }
       }
     }
   }
@@ -93,6 +106,7 @@ struct RedArgs {
   float* part;   // [BH][splits][M][D]
   float* partz;  // [BH][splits][M]
   int L, M, H, Hw, splits, split_len;
+  int Mw;        // rows of W per head (M, or M/2 for the trig map)
 };
 
 // Pipeline shape of the K-side kernels: tiles of TT tokens copied into a
@@ -125,7 +139,7 @@ struct RedLds {
 // per tile: after it, tile t+2 is copied, tile t+1 is prepared and tile t is
 // computed from its prepared buffer, so the copies, the preparation (LDS and
 // a little VALU work) and the matrix products of different tiles overlap.
-template <class Tr, int D, int NW, int FBW>
+template <class Tr, int D, int NW, int FBW, int FM>
 __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
   constexpr int NT = NW * 64;
   using E = typename Tr::elem;
@@ -149,16 +163,19 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
   const int fb0 = (fg * NW + w) * FBW;
   const E* K = (const E*)a.k + (size_t)bh * a.L * D;
   const E* V = (const E*)a.v + (size_t)bh * a.L * D;
-  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.Mw * D;
   const float half_ln_m = 0.5f * logf((float)a.M);
+  const int nfbw = a.Mw >> 5;
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
 
   F wf[FBW][NKD];
 #pragma unroll
   for (int i = 0; i < FBW; ++i) {
     const bool ok = fb0 + i < nfb;
-    const float* wrow = wh + (size_t)((ok ? fb0 + i : 0) * 32 + l32) * D;
+    const int fbw_ = ok ? fb0 + i : 0;
+    const float* wrow = wh + (size_t)((FM == FM_TRIG ? fbw_ % nfbw : fbw_) * 32 + l32) * D;
 #pragma unroll
-    for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D>(wrow, hh, s, ok);
+    for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, ok);
   }
   f32x16 st[FBW][NDB];
   float zs[FBW];
@@ -219,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
       }
       *(u32x4*)(pb + LY::kKh + r * RS + cc * 16) = v;
       ss = group_sum<CPR>(ss);
-      if (cc == 0) bias[r] = r < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
+      if (cc == 0) bias[r] = r < nvalid ? FMap<FM>::row_bias(ss, half_ln_m) : -INFINITY;
     }
     if constexpr (LY::kVT) {
       const char* rawv = raw + DT::BYTES;
@@ -298,8 +315,9 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
       for (int i = 0; i < FBW; ++i) {
         if (fb0 + i < nfb) {
           f32x16 e = acc[i][tb];
+          const bool cosine = fb0 + i >= nfbw;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e[r] = exp2_fast(e[r]);
+          for (int r = 0; r < 16; ++r) e[r] = FMap<FM>::phi(e[r], cosine, tscale);
 #pragma unroll
           for (int s2 = 0; s2 < NKT; ++s2) {
             F pf = CFrag<Tr>::make(e, s2);
@@ -369,34 +387,43 @@ constexpr int kQuadsPerBlock = 256 / kSplitGroups;
 // [Hw*M/32 feature blocks][NKG][half h][feature f][16 bytes]: the 16 bytes of
 // lane (f, h) at k-group g hold d = (D/2) h + (16/WES) g + 0.. (the d-major
 // k order of the projection), so a wave reads 1 KB of contiguous memory.
-template <class E>
-__device__ __forceinline__ void wprep_chunk(const float* w, void* out, int idx, int D) {
+// The operand covers M features per head; for the trig map feature f uses
+// W row f mod Mw (its sine and its cosine share a row).
+template <class E, int FM>
+__device__ __forceinline__ void wprep_chunk(const float* w, void* out, int idx, int D, int M, int Mw) {
   constexpr int WES = sizeof(E);
   constexpr int PER = 16 / WES;                      // d values per 16 bytes
+  constexpr float sc = FMap<FM>::kWScale;
   const int nkg = D * WES / 32;
   const int f = idx & 31, h = (idx >> 5) & 1, rest = idx >> 6;
   const int g = rest % nkg, blk = rest / nkg;
-  const float* src = w + (size_t)(blk * 32 + f) * D + (D / 2) * h + PER * g;
+  int row = blk * 32 + f;
+  if constexpr (FM == FM_TRIG) {
+    const int nb = M >> 5;                           // feature blocks per head
+    row = (blk / nb) * Mw + ((blk % nb) * 32 + f) % Mw;
+  }
+  const float* src = w + (size_t)row * D + (D / 2) * h + PER * g;
   if constexpr (WES == 2) {
     const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
-    u32x4 v = {pack_f16(x0[0] * kLog2e, x0[1] * kLog2e), pack_f16(x0[2] * kLog2e, x0[3] * kLog2e),
-               pack_f16(x1[0] * kLog2e, x1[1] * kLog2e), pack_f16(x1[2] * kLog2e, x1[3] * kLog2e)};
+    u32x4 v = {pack_f16(x0[0] * sc, x0[1] * sc), pack_f16(x0[2] * sc, x0[3] * sc),
+               pack_f16(x1[0] * sc, x1[1] * sc), pack_f16(x1[2] * sc, x1[3] * sc)};
     ((u32x4*)out)[idx] = v;
   } else {
-    ((f32x4*)out)[idx] = *(const f32x4*)src * kLog2e;
+    ((f32x4*)out)[idx] = *(const f32x4*)src * sc;
   }
 }
 
 // grid.y = BH + 1: slices 0..BH-1 combine a head's partial states, the last
 // slice prepares the projection operand from W (n16w 16-byte chunks).
-template <class E>
+template <class E, int FM>
 __global__ __launch_bounds__(256) void k_combine(const float* part, const float* partz, E* mstate, E* zstate,
                                                  int splits, int M, int D, int BH, const float* w, void* wp,
-                                                 int n16w) {
+                                                 int n16w, int Mw) {
   __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
   const int bh = blockIdx.y;
   if (bh == BH) {
-    for (int idx = blockIdx.x * 256 + threadIdx.x; idx < n16w; idx += gridDim.x * 256) wprep_chunk<E>(w, wp, idx, D);
+    for (int idx = blockIdx.x * 256 + threadIdx.x; idx < n16w; idx += gridDim.x * 256)
+      wprep_chunk<E, FM>(w, wp, idx, D, M, Mw);
     return;
   }
   const int g = threadIdx.x / kQuadsPerBlock, qi = threadIdx.x % kQuadsPerBlock;
@@ -463,12 +490,13 @@ struct ApplyArgs {
   float eps;
   int groups_per_head, groups_total, steps, fch, nbuf;
   int stage_off;        // LDS offset of the per-wave output staging areas
+  int Mw;               // rows of W per head (M, or M/2 for the trig map)
 };
 
 // NW waves per workgroup, TB 32-token blocks per wave.  LEAN: no Q prefetch,
 // one feature block per scheduling region and no output staging, so that a
 // wave fits 128 registers (four waves per SIMD).
-template <class Tr, int D, int TB, int NW, bool LEAN>
+template <class Tr, int D, int TB, int NW, bool LEAN, int FM>
 __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
@@ -492,6 +520,7 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int nch = (a.M + FCH - 1) / FCH;
   const float half_ln_m = 0.5f * logf((float)a.M);
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
   const int g0 = blockIdx.x * a.steps;
   const int g1 = min(a.groups_total, g0 + a.steps);
 
@@ -619,7 +648,7 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
         }
       }
       ss = half_sum(ss);
-      bias[tb] = -(0.5f * ss + half_ln_m) * kLog2e;
+      bias[tb] = FMap<FM>::row_bias(ss, half_ln_m);
     }
 
     f32x16 oacc[TB][NDB];
@@ -651,13 +680,14 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
           }
         }
         f32x16 pacc[TB];
+        const bool cosine = f0 + fb * 32 >= a.Mw;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
           pacc[tb] = zero16();
 #pragma unroll
           for (int s = 0; s < NKD; ++s) pacc[tb] = Tr::pmma(wfr[s], qf[tb][s], pacc[tb]);   // P^T[f][t], lane = t
 #pragma unroll
-          for (int r = 0; r < 16; ++r) pacc[tb][r] = exp2_fast(pacc[tb][r] + bias[tb]);
+          for (int r = 0; r < 16; ++r) pacc[tb][r] = FMap<FM>::phi(pacc[tb][r] + bias[tb], cosine, tscale);
         }
         if constexpr (Tr::VPS == 8) {
           // group gi = 2 fb + s2 holds 16 features; lane (d, hh) reads 8 of them
@@ -776,14 +806,28 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
 // ===========================================================================
 // host launchers
 // ===========================================================================
+// Call f.template operator()<FM>() for the plan's feature map.
+template <class Fn>
+static hipError_t with_fmap(int fmap, Fn&& f) {
+  switch (fmap) {
+    case FM_POS: return f.template operator()<FM_POS>();
+    case FM_ELU1: return f.template operator()<FM_ELU1>();
+    case FM_RELU: return f.template operator()<FM_RELU>();
+    case FM_TRIG: return f.template operator()<FM_TRIG>();
+  }
+  return hipErrorInvalidValue;
+}
+
 template <class Tr, int D>
 static hipError_t features_t(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s) {
-  FeatArgs a{x, w, phi, p.L, p.M, p.H, p.Hw};
+  FeatArgs a{x, w, phi, p.L, p.M, p.H, p.Hw, p.Mw};
   dim3 grid((p.L + 127) / 128, p.BH);
-  timing_begin(FAVOR_KERNEL_FEATURES, s);
-  hipLaunchKernelGGL((k_features<Tr, D>), grid, dim3(256), 0, s, a);
-  timing_end(FAVOR_KERNEL_FEATURES, s);
-  return hipGetLastError();
+  return with_fmap(p.fmap, [&]<int FM>() {
+    timing_begin(FAVOR_KERNEL_FEATURES, s);
+    hipLaunchKernelGGL((k_features<Tr, D, FM>), grid, dim3(256), 0, s, a);
+    timing_end(FAVOR_KERNEL_FEATURES, s);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s) {
@@ -806,7 +850,7 @@ hipError_t launch_features(const Plan& p, const void* x, const float* w, float* 
 template <class Tr, int D>
 hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
                            hipStream_t s) {
-  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len};
+  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw};
   // 8 waves of one feature block each, or 4 where a wave's registers exceed
   // half a SIMD's (two blocks per wave, sharing each K/V fragment read, ran
   // slower: half as many waves to hide the latency of each block's chain)
@@ -815,10 +859,12 @@ hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const fl
   if (p.rnw != NW || p.rfbw != FBW) return hipErrorInvalidValue;
   dim3 grid(p.splits, p.rfgroups, p.BH);
   const size_t lds = RedLds<Tr, D, NW * 64>::kTotal;
-  timing_begin(FAVOR_KERNEL_REDUCE, s);
-  hipLaunchKernelGGL((k_reduce<Tr, D, NW, FBW>), grid, dim3(NW * 64), lds, s, a);
-  timing_end(FAVOR_KERNEL_REDUCE, s);
-  return hipGetLastError();
+  return with_fmap(p.fmap, [&]<int FM>() {
+    timing_begin(FAVOR_KERNEL_REDUCE, s);
+    hipLaunchKernelGGL((k_reduce<Tr, D, NW, FBW, FM>), grid, dim3(NW * 64), lds, s, a);
+    timing_end(FAVOR_KERNEL_REDUCE, s);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
@@ -854,14 +900,16 @@ static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const
   const int nbuf = (p.fch >= p.M && 2 * buf + stage <= 150 * 1024) ? 2 : 1;
   const size_t stage_off = (nbuf * buf + 15) / 16 * 16;
   ApplyArgs a{t.q, wp, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch, nbuf,
-              (int)stage_off};
+              (int)stage_off, p.Mw};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
   const size_t lds = stage_off + stage;
   if (TB * 32 != p.apply_tile || NW != p.apply_nw) return hipErrorInvalidValue;
-  timing_begin(FAVOR_KERNEL_APPLY, s);
-  hipLaunchKernelGGL((k_apply<Tr, D, TB, NW, LEAN>), dim3(nblk), dim3(NW * 64), lds, s, a);
-  timing_end(FAVOR_KERNEL_APPLY, s);
-  return hipGetLastError();
+  return with_fmap(p.fmap, [&]<int FM>() {
+    timing_begin(FAVOR_KERNEL_APPLY, s);
+    hipLaunchKernelGGL((k_apply<Tr, D, TB, NW, LEAN, FM>), dim3(nblk), dim3(NW * 64), lds, s, a);
+    timing_end(FAVOR_KERNEL_APPLY, s);
+    return hipGetLastError();
+  });
 }
 
 static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* wp, const void* mstate,
@@ -893,15 +941,17 @@ hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
   const int nq = (p.M * p.D + p.M) / 4;
   const int n16w = p.Hw * p.M * p.D * (p.dt == FAVOR_BF16 ? 2 : 4) / 16;
   dim3 cgrid((nq + kQuadsPerBlock - 1) / kQuadsPerBlock, p.BH + 1);
-  timing_begin(FAVOR_KERNEL_COMBINE, s);
-  if (p.dt == FAVOR_BF16)
-    hipLaunchKernelGGL((k_combine<bf16>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate, p.splits,
-                       p.M, p.D, p.BH, t.w, wp, n16w);
-  else
-    hipLaunchKernelGGL((k_combine<float>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
-                       p.splits, p.M, p.D, p.BH, t.w, wp, n16w);
-  timing_end(FAVOR_KERNEL_COMBINE, s);
-  e = hipGetLastError();
+  e = with_fmap(p.fmap, [&]<int FM>() {
+    timing_begin(FAVOR_KERNEL_COMBINE, s);
+    if (p.dt == FAVOR_BF16)
+      hipLaunchKernelGGL((k_combine<bf16, FM>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate,
+                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw);
+    else
+      hipLaunchKernelGGL((k_combine<float, FM>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
+                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw);
+    timing_end(FAVOR_KERNEL_COMBINE, s);
+    return hipGetLastError();
+  });
   if (e != hipSuccess) return e;
   return launch_apply(p, t, wp, mstate, zstate, s);
 }

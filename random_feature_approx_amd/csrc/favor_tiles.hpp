@@ -7,6 +7,45 @@
 
 namespace favor {
 
+// ---------------------------------------------------------------------------
+// Feature maps ("Linear Attention > Kernel Feature Maps", sections 1-4), all
+// applied to the projection p = W x:
+//   FM_POS   FAVOR+ positive features exp(p - |x|^2/2)/sqrt(m)   (section 4)
+//   FM_ELU1  ELU(p) + 1                                           (section 1)
+//   FM_RELU  max(0, p)                                            (section 2)
+//   FM_TRIG  (1/sqrt(m)) [sin p_i, cos p_i]: 2m features, stored as the m
+//            sines then the m cosines                              (section 3)
+// The kernels evaluate phi(x) with x = (W s) x + row_bias: W is scaled by
+// kWScale when it becomes a matrix operand (log2 e, so FAVOR+ is one exp2;
+// 1/(2 pi) for the trig map, whose sine and cosine take revolutions), and
+// row_bias is FAVOR+'s -(|x|^2/2 + ln(m)/2) log2 e and 0 otherwise.  Rows
+// past the end get a bias of -inf, which every map sends to 0.
+// ---------------------------------------------------------------------------
+enum { FM_POS = 0, FM_ELU1 = 1, FM_RELU = 2, FM_TRIG = 3 };
+
+template <int FM>
+struct FMap {
+  static constexpr float kWScale = FM == FM_POS ? kLog2e : (FM == FM_TRIG ? 0.15915494309189535f : 1.f);
+  static __device__ __forceinline__ float row_bias(float ss, float half_ln_m) {
+    if constexpr (FM == FM_POS) return -(0.5f * ss + half_ln_m) * kLog2e;
+    else return 0.f;
+  }
+  // cosine: the feature is in the second (cosine) half (FM_TRIG);
+  // scale: 1/sqrt(m) (FM_TRIG)
+  static __device__ __forceinline__ float phi(float x, bool cosine, float scale) {
+    if constexpr (FM == FM_POS) {
+      return exp2_fast(x);
+    } else if constexpr (FM == FM_ELU1) {
+      return x > 0.f ? x + 1.f : exp2_fast(x * kLog2e);
+    } else if constexpr (FM == FM_RELU) {
+      return fmaxf(x, 0.f);
+    } else {
+      if (x == -INFINITY) return 0.f;
+      return scale * (cosine ? __builtin_amdgcn_cosf(x) : __builtin_amdgcn_sinf(x));
+    }
+  }
+};
+
 // LDS row stride in bytes for a [rows][D] tile of element size ES: 16 bytes
 // of padding move consecutive rows to different LDS banks.
 template <int D, int ES> struct Rows {
@@ -57,7 +96,9 @@ struct TileLoader {
     }
   }
   // Squared norm of each row, reduced over the CPR consecutive lanes that
-  // hold it; the lane holding chunk 0 of a row writes bias(row) to sb.
+  // hold it; the lane holding chunk 0 of a row writes the feature map's
+  // row bias to sb (-inf for rows at or beyond nvalid).
+  template <int FM = FM_POS>
   __device__ __forceinline__ void row_bias(float* sb, int tid, int nvalid, float half_ln_m) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -77,27 +118,29 @@ struct TileLoader {
       ss = group_sum<CPR>(ss);
       int row = c / CPR;
       if (c < TT * CPR && (c % CPR) == 0)
-        sb[row] = row < nvalid ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
+        sb[row] = row < nvalid ? FMap<FM>::row_bias(ss, half_ln_m) : -INFINITY;
     }
   }
 };
 
-// Projection fragment of W (lane = feature f, d-major slots), scaled by
-// log2 e and converted to the projection operand type (fp16 for bf16 inputs).
-template <class Tr, int D>
+// Projection fragment of W (lane = feature f, d-major slots), scaled by the
+// feature map's factor (log2 e for FAVOR+) and converted to the projection
+// operand type (fp16 for bf16 inputs).
+template <class Tr, int D, int FM = FM_POS>
 __device__ __forceinline__ typename Tr::frag w_frag(const float* wrow, int hh, int s, bool ok) {
+  constexpr float sc = FMap<FM>::kWScale;
   const int d0 = (D / 2) * hh + Tr::VPS * s;
   if constexpr (Tr::VPS == 8) {
     f32x4 a = ok ? *(const f32x4*)(wrow + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 b = ok ? *(const f32x4*)(wrow + d0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 f;
-    f[0] = pack_f16(a[0] * kLog2e, a[1] * kLog2e);
-    f[1] = pack_f16(a[2] * kLog2e, a[3] * kLog2e);
-    f[2] = pack_f16(b[0] * kLog2e, b[1] * kLog2e);
-    f[3] = pack_f16(b[2] * kLog2e, b[3] * kLog2e);
+    f[0] = pack_f16(a[0] * sc, a[1] * sc);
+    f[1] = pack_f16(a[2] * sc, a[3] * sc);
+    f[2] = pack_f16(b[0] * sc, b[1] * sc);
+    f[3] = pack_f16(b[2] * sc, b[3] * sc);
     return f;
   } else {
-    return ok ? wrow[d0] * kLog2e : 0.f;
+    return ok ? wrow[d0] * sc : 0.f;
   }
 }
 
