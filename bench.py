@@ -19,7 +19,10 @@ The JSON line also carries
   * "paths" and "kernels": per-path and per-kernel timings;
   * "backward": the backward pass (gradients of sum(G * O) for a seeded
     upstream gradient G) of each path that has one, timed the same way after
-    the forward measurement; it is reported beside `value`, never in it.
+    the forward measurement; it is reported beside `value`, never in it;
+  * "feature_maps": the same forward step with each other feature map of
+    the Kernel Feature Maps page (ELU + 1, ReLU, random Fourier features),
+    also beside `value`.
 """
 from __future__ import annotations
 
@@ -222,6 +225,34 @@ def backward_leg(favor, torch, wl, q, k, v, w, to_dev, K: int, warmup: int) -> d
     return out
 
 
+def fmap_leg(favor, torch, wl, q, k, v, w, outs, K: int, warmup: int) -> dict:
+    """Time the forward step (every path) with each non-FAVOR+ feature map."""
+    out = {}
+    code = favor.BF16 if wl.dtype == "bf16" else favor.F32
+    for kind in ("elu1", "relu", "trig"):
+        wss = {p: torch.empty(favor.workspace_bytes(wl.B, wl.H, wl.L, wl.d, wl.m, p == "causal", code, fmap=kind),
+                              dtype=torch.uint8, device=q.device) for p in wl.paths}
+
+        def step():
+            for p in wl.paths:
+                favor.attn(q, k, v, w, causal=(p == "causal"), eps=wl.eps, out=outs[p], workspace=wss[p], fmap=kind)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / K
+        log(f"feature map {kind}: {ms:.4f} ms per step")
+        out[kind] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
+                     "features": 2 * wl.m if kind == "trig" else wl.m}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +263,7 @@ def main() -> int:
     ap.add_argument("--paths", default="", help="comma-separated subset of the workload's paths to run "
                                                 "(default: all; used to attribute profiler counters to a path)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-fmaps", action="store_true", help="skip the feature-map variant measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes 5 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -354,6 +386,7 @@ def main() -> int:
                             "hbm_frac_alg": r.get("hbm_frac_alg"), "mfma_frac_alg": r.get("mfma_frac_alg")}
 
     bwd = None if args.no_backward else backward_leg(favor, torch, wl, q, k, v, w, to_dev, K, args.warmup)
+    fmaps = None if args.no_fmaps else fmap_leg(favor, torch, wl, q, k, v, w, outs, K, args.warmup)
 
     tokens = wl.tokens
     value = tokens / (ms_step * 1e-3)
@@ -385,6 +418,7 @@ def main() -> int:
         "paths": paths_report,
         "kernels": kern_report,
         "backward": bwd,
+        "feature_maps": fmaps,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -96,7 +96,7 @@ def main() -> int:
     for path in wl.paths:
         for c in COUNTERS:
             rows, cmd = run_pass(c, os.path.join(args.out, f"{wl.name}_{path}_{c}_{stamp}"),
-                                 [bench_py, "--workload", wl.name, "--paths", path, "--steps", "3", "--warmup", "1",
+                                 [bench_py, "--workload", wl.name, "--paths", path, "--steps", "3", "--warmup", "1", "--no-backward", "--no-fmaps",
                                   "--cpu-seconds", "0"], run)
             commands.append(cmd)
             acc = {}
