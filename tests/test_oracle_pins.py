@@ -367,6 +367,25 @@ def test_softmax_reference_invariants():
                                rtol=1e-13)
 
 
+def test_causal_softmax_brute_force_and_invariants():
+    """Masked softmax written out entry by entry; row 0 is v_0; the last row
+    is the unmasked one; with scale 0 row i is the mean of v_0..v_i."""
+    rng = np.random.default_rng(32)
+    L, d = 6, 3
+    q = rng.standard_normal((L, d))
+    k = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, 2))
+    got = oracle.softmax_attention(q, k, v, scale=0.5, causal=True)
+    for i in range(L):
+        e = [math.exp(0.5 * sum(q[i][c] * k[j][c] for c in range(d))) for j in range(i + 1)]
+        ref = sum(e[j] * v[j] for j in range(i + 1)) / sum(e)
+        np.testing.assert_allclose(got[i], ref, rtol=1e-13)
+    np.testing.assert_allclose(got[0], v[0], rtol=1e-15)
+    np.testing.assert_allclose(got[-1], oracle.softmax_attention(q, k, v, scale=0.5)[-1], rtol=1e-13)
+    mean = oracle.softmax_attention(q, k, v, scale=0.0, causal=True)
+    np.testing.assert_allclose(mean, np.cumsum(v, 0) / np.arange(1, L + 1)[:, None], rtol=1e-13)
+
+
 def test_per_head_uses_the_right_projection():
     rng = np.random.default_rng(32)
     B, H, L, d, m = 2, 3, 5, 4, 8
