@@ -182,6 +182,93 @@ def softmax_attention(q, k, v, scale: float = 1.0, causal: bool = False) -> np.n
     return p @ np.asarray(v, dtype=np.float64)
 
 
+# ---------------------------------------------------------------------------
+# Backward pass.  The pages give no formulas for it; they only note (P2,
+# section 踩过的坑 / pitfalls) that the causal prefix sum must be accumulated
+# in reverse for the gradient.  What is computed is the gradient of the
+# forward definition above with respect to Q, K and V for an upstream
+# gradient G = dLoss/dO (W is a fixed random projection and gets none),
+# written out with the chain rule through the reassociated form.
+# ---------------------------------------------------------------------------
+def favor_features_vjp(x, w, phi, dphi) -> np.ndarray:
+    """dLoss/dx given dLoss/dphi for phi = favor_features(x, w).
+
+    d phi_f / d x = phi_f (omega_f - x)  (differentiating the feature-map
+    equation of P1), hence dx = (dphi * phi) W - sum_f(dphi_f phi_f) x."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(dphi, dtype=np.float64) * phi
+    return g @ np.asarray(w, dtype=np.float64) - g.sum(axis=-1, keepdims=True) * x
+
+
+def attn_noncausal_grad(q, k, v, w, g, eps: float = 1e-6):
+    """Gradients (dQ, dK, dV) of sum(G * O) for non-causal attention.
+
+    With M = phi(K)^T V, z = phi(K)^T 1, den_i = phi(q_i).z + eps and
+    o_i = phi(q_i) M / den_i:
+      dnum_i = g_i / den_i,  dden_i = -(g_i . o_i) / den_i,
+      dphi(q_i) = M dnum_i + z dden_i,
+      dM = phi(Q)^T dnum,  dz = phi(Q)^T dden,
+      dV = phi(K) dM,  dphi(k_j) = dM v_j + dz,
+    then each feature gradient goes through favor_features_vjp."""
+    fq = favor_features(q, w)
+    fk = favor_features(k, w)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    state = fk.T @ v
+    key_sum = fk.sum(axis=0)
+    den = fq @ key_sum + eps
+    o = (fq @ state) / den[:, None]
+    dnum = g / den[:, None]
+    dden = -(g * o).sum(axis=1) / den
+    dfq = dnum @ state.T + dden[:, None] * key_sum[None, :]
+    dstate = fq.T @ dnum
+    dkey_sum = fq.T @ dden
+    dv = fk @ dstate
+    dfk = v @ dstate.T + dkey_sum[None, :]
+    return favor_features_vjp(q, w, fq, dfq), favor_features_vjp(k, w, fk, dfk), dv
+
+
+def attn_causal_grad(q, k, v, w, g, eps: float = 1e-6):
+    """Gradients (dQ, dK, dV) of sum(G * O) for causal attention.
+
+    Forward walk (as attn_causal): S_i, z_i, den_i, o_i, and with them
+    dnum_i = g_i / den_i, dden_i = -(g_i . o_i) / den_i and
+    dphi(q_i) = S_i dnum_i + z_i dden_i.
+    Reverse walk (the reverse accumulation of P2's pitfalls): the suffix sums
+    R_j = sum_{i>=j} phi(q_i) dnum_i^T and r_j = sum_{i>=j} phi(q_i) dden_i
+    give dv_j = R_j^T phi(k_j) and dphi(k_j) = R_j v_j + r_j.
+    One Python step per token in each walk."""
+    fq = favor_features(q, w)
+    fk = favor_features(k, w)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    L, d = v.shape
+    m = fq.shape[1]
+    state = np.zeros((m, d))
+    key_sum = np.zeros(m)
+    dnum = np.empty((L, d))
+    dden = np.empty(L)
+    dfq = np.empty((L, m))
+    for i in range(L):
+        state += np.outer(fk[i], v[i])
+        key_sum += fk[i]
+        den = fq[i] @ key_sum + eps
+        o = (fq[i] @ state) / den
+        dnum[i] = g[i] / den
+        dden[i] = -(g[i] @ o) / den
+        dfq[i] = state @ dnum[i] + key_sum * dden[i]
+    rstate = np.zeros((m, d))
+    rsum = np.zeros(m)
+    dv = np.empty((L, d))
+    dfk = np.empty((L, m))
+    for j in range(L - 1, -1, -1):
+        rstate += np.outer(fq[j], dnum[j])
+        rsum += fq[j] * dden[j]
+        dv[j] = rstate.T @ fk[j]
+        dfk[j] = rstate @ v[j] + rsum
+    return favor_features_vjp(q, w, fq, dfq), favor_features_vjp(k, w, fk, dfk), dv
+
+
 def head_projection(w: np.ndarray, h: int) -> np.ndarray:
     """The projection of head h: W is (Hw, m, d) with Hw = 1 (shared by all
     heads) or Hw = H (one per head)."""
