@@ -212,6 +212,20 @@ favor_status favor_attn_causal_bwd(const void* Q, const void* K, const void* V,
                                    void* stream);
 
 /*
+ * Exact softmax attention O = softmax(scale * Q K^T) V, optionally masked
+ * to keys j <= i: the quadratic attention FAVOR+ approximates (softmax-kernel
+ * equation of "Linear Attention > Kernel Feature Maps"; the left side of the
+ * reordering diagram of the performer-2020 study notes, which write the
+ * scale as 1/sqrt(d)).  The library's own reference for speed and quality
+ * comparisons at equal shapes; it needs no workspace.  Q, K, V, O as for
+ * favor_attn (d in {32, 64, 128}); scores, the running maximum and the sums
+ * are float32, probabilities enter the value product in the input dtype.
+ */
+favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, void* O,
+                                int B, int H, int L, int d, float scale, int causal,
+                                favor_dtype dtype, void* stream);
+
+/*
  * Kernel timing (for benchmarks and profiling; host-side only, allocates no
  * device memory).  favor_timing_start(k, capacity) creates `capacity` pairs
  * of HIP timing events; every later launch of kernel k by this library
@@ -234,7 +248,8 @@ typedef enum {
   FAVOR_KERNEL_BWD_COMBINE = 8,/* backward: combine of their partials             */
   FAVOR_KERNEL_BWD_Q = 9,      /* backward: query side (dQ)                       */
   FAVOR_KERNEL_BWD_K = 10,     /* backward: key side (dK, dV)                     */
-  FAVOR_KERNEL_COUNT = 11
+  FAVOR_KERNEL_SOFTMAX = 11,   /* exact softmax attention (favor_softmax_attn)    */
+  FAVOR_KERNEL_COUNT = 12
 } favor_kernel;
 
 favor_status favor_timing_start(favor_kernel k, int capacity);

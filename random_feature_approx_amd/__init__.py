@@ -24,7 +24,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS",
+__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS", "softmax_attn",
            "workspace_bytes", "attn_backward", "bwd_workspace_bytes", "FavorError", "STATUS", "KERNELS",
            "timing_start", "timing_stop"]
 
@@ -37,7 +37,7 @@ STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid shape", 3: "unsupport
           4: "workspace missing or too small", 5: "HIP runtime error", 6: "internal error"}
 F32, BF16 = 0, 1
 KERNELS = {"k_features": 0, "k_reduce": 1, "k_combine": 2, "k_apply": 3, "k_span_scan": 4, "k_causal": 5,
-           "k_bprep": 6, "k_bred": 7, "k_bcombine": 8, "k_bside_q": 9, "k_bside_k": 10}
+           "k_bprep": 6, "k_bred": 7, "k_bcombine": 8, "k_bside_q": 9, "k_bside_k": 10, "k_softmax": 11}
 
 
 class FavorError(RuntimeError):
@@ -81,6 +81,8 @@ def load():
     lib.favor_features_fmap.argtypes = [vp, vp, i, vp, i, i, i, i, i, i, i, vp]
     lib.favor_attn_fmap.restype = i
     lib.favor_attn_fmap.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.favor_softmax_attn.restype = i
+    lib.favor_softmax_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.favor_bwd_workspace_bytes.restype = sz
     lib.favor_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     for name in ("favor_attn_noncausal_bwd", "favor_attn_causal_bwd"):
@@ -209,6 +211,27 @@ def attn_noncausal(q, k, v, w, eps: float = 1e-6, **kw):
 
 def attn_causal(q, k, v, w, eps: float = 1e-6, **kw):
     return attn(q, k, v, w, causal=True, eps=eps, **kw)
+
+
+def softmax_attn(q, k, v, scale=None, causal: bool = False, out=None):
+    """Exact softmax(scale * q k^T) v (scale defaults to 1/sqrt(d)),
+    optionally causal; the quadratic reference that FAVOR+ approximates."""
+    lib = load()
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, L, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, L, d = q.shape
+    _check_device(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    sc = float(d) ** -0.5 if scale is None else float(scale)
+    st = lib.favor_softmax_attn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()), B, H, L, d, sc,
+                                int(bool(causal)), _dtype_code(q), _stream())
+    if st != 0:
+        raise FavorError("favor_softmax_attn", st)
+    return o
 
 
 def bwd_workspace_bytes(B: int, H: int, L: int, d: int, m: int, causal: bool, dtype) -> int:

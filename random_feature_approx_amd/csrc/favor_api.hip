@@ -271,6 +271,18 @@ size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, 
   return p.btotal;
 }
 
+favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, void* O, int B, int H, int L, int d,
+                                float scale, int causal, favor_dtype dtype, void* stream) {
+  if (!Q || !K || !V || !O) return FAVOR_ERR_NULL;
+  favor_status st = check_shapes(B, H, L, d, 32, 1, dtype);
+  if (st != FAVOR_OK) return st;
+  Plan p{};
+  p.B = B; p.H = H; p.L = L; p.D = d; p.BH = B * H; p.dt = dtype;
+  p.esize = dtype == FAVOR_BF16 ? 2 : 4;
+  return launch_softmax(p, Q, K, V, O, scale, causal ? 1 : 0, (hipStream_t)stream) == hipSuccess ? FAVOR_OK
+                                                                                                   : FAVOR_ERR_HIP;
+}
+
 static favor_status bwd_common(const void* Q, const void* K, const void* V, const float* W, int Hw, const void* dO,
                                void* dQ, void* dK, void* dV, int B, int H, int L, int d, int m, float eps, int causal,
                                favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
@@ -346,6 +358,7 @@ const char* favor_kernel_name(favor_kernel k) {
     case FAVOR_KERNEL_BWD_COMBINE: return "k_bcombine";
     case FAVOR_KERNEL_BWD_Q: return "k_bside_q";
     case FAVOR_KERNEL_BWD_K: return "k_bside_k";
+    case FAVOR_KERNEL_SOFTMAX: return "k_softmax";
     default: return "unknown";
   }
 }
