@@ -160,6 +160,32 @@ favor_status favor_attn_fmap(const void* Q, const void* K, const void* V,
                              favor_feature_map fmap, favor_dtype dtype, void* ws,
                              size_t ws_bytes, void* stream);
 
+/*
+ * Attention with arbitrary layouts and a value width d_v that may differ
+ * from d (the page's code cell In[25] allows d_v != d_k).  Each tensor is
+ * described by its pointer and three element strides, for its batch, head
+ * and token dimensions (the last dimension is contiguous): Q, K are
+ * [B, H, L, dk], V and O are [B, H, L, dv] in that index order; for example
+ * a token-major [B, L, H, d] tensor has strides {L*H*d, d, H*d}.  dk must be
+ * a supported d; dv is any width from 1 to 65536.  Inputs that are not
+ * contiguous (and V, O when dv != dk) are gathered into, or scattered from,
+ * contiguous copies in the workspace; values are processed in column chunks
+ * of width dk (O is linear in V), each chunk recomputing the features.
+ * Workspace: favor_workspace_bytes_strided bytes (256-byte aligned).  O must
+ * not overlap the inputs.  Errors as favor_attn; negative strides are
+ * rejected with FAVOR_ERR_SHAPE.
+ */
+size_t favor_workspace_bytes_strided(int B, int H, int L, int dk, int dv, int m, int causal,
+                                     favor_feature_map fmap, favor_dtype dtype);
+
+favor_status favor_attn_strided(const void* Q, const long long* q_strides,
+                                const void* K, const long long* k_strides,
+                                const void* V, const long long* v_strides,
+                                const float* W, int Hw, void* O, const long long* o_strides,
+                                int B, int H, int L, int dk, int dv, int m, float eps, int causal,
+                                favor_feature_map fmap, favor_dtype dtype, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* Dispatcher: favor_attn_causal when causal != 0, else favor_attn_noncausal. */
 favor_status favor_attn(const void* Q, const void* K, const void* V,
                         const float* W, int Hw, void* O,

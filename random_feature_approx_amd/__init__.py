@@ -24,7 +24,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS", "softmax_attn",
+__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS", "softmax_attn", "attn_strided",
            "workspace_bytes", "attn_backward", "bwd_workspace_bytes", "FavorError", "STATUS", "KERNELS",
            "timing_start", "timing_stop"]
 
@@ -81,6 +81,12 @@ def load():
     lib.favor_features_fmap.argtypes = [vp, vp, i, vp, i, i, i, i, i, i, i, vp]
     lib.favor_attn_fmap.restype = i
     lib.favor_attn_fmap.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    ll3 = ctypes.POINTER(ctypes.c_longlong)
+    lib.favor_workspace_bytes_strided.restype = sz
+    lib.favor_workspace_bytes_strided.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.favor_attn_strided.restype = i
+    lib.favor_attn_strided.argtypes = [vp, ll3, vp, ll3, vp, ll3, vp, i, vp, ll3, i, i, i, i, i, i, f, i, i, i,
+                                       vp, sz, vp]
     lib.favor_softmax_attn.restype = i
     lib.favor_softmax_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.favor_bwd_workspace_bytes.restype = sz
@@ -211,6 +217,42 @@ def attn_noncausal(q, k, v, w, eps: float = 1e-6, **kw):
 
 def attn_causal(q, k, v, w, eps: float = 1e-6, **kw):
     return attn(q, k, v, w, causal=True, eps=eps, **kw)
+
+
+def attn_strided(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, fmap: str = "positive"):
+    """Attention for tensors of any layout whose last dimension is contiguous
+    (views such as a [B, L, H, d] tensor permuted to [B, H, L, d]) and for a
+    value width dv that may differ from d: q, k are [B, H, L, d] views, v is
+    [B, H, L, dv]; returns (or fills `out`, a [B, H, L, dv] view) O."""
+    lib = load()
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must share a [B, H, L, d] shape and v must be [B, H, L, dv]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or t.stride(3) != 1:
+            raise ValueError("tensors must live on a HIP device with a contiguous last dimension")
+    B, H, L, d = q.shape
+    dv = int(v.shape[3])
+    w, hw = _proj(w, H, (w.shape[-2], d))
+    m = int(w.shape[1])
+    code, fcode = _dtype_code(q), _fmap_code(fmap)
+    o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device) if out is None else out
+    if o.shape != (B, H, L, dv) or o.stride(3) != 1 or o.dtype != q.dtype:
+        raise ValueError("out must be a [B, H, L, dv] view of the input dtype with a contiguous last dimension")
+    need = int(lib.favor_workspace_bytes_strided(B, H, L, d, dv, m, int(bool(causal)), fcode, code))
+    if need == 0:
+        raise FavorError("favor_workspace_bytes_strided", 2)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st3 = lambda t: (ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2))  # noqa: E731
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = lib.favor_attn_strided(ptr(q), st3(q), ptr(k), st3(k), ptr(v), st3(v), ptr(w), hw, ptr(o), st3(o),
+                                B, H, L, d, dv, m, float(eps), int(bool(causal)), fcode, code, ptr(ws), need,
+                                _stream())
+    if st != 0:
+        raise FavorError("favor_attn_strided", st)
+    return o
 
 
 def softmax_attn(q, k, v, scale=None, causal: bool = False, out=None):

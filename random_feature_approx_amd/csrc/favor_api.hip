@@ -271,6 +271,76 @@ size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, 
   return p.btotal;
 }
 
+// ---------------------------------------------------------------------------
+// strided layouts and value widths d_v != d (gather, contiguous path, scatter)
+// ---------------------------------------------------------------------------
+static size_t strided_extra(const Plan& p) { return align256((size_t)p.BH * p.L * p.D * p.esize); }
+
+size_t favor_workspace_bytes_strided(int B, int H, int L, int dk, int dv, int m, int causal, favor_feature_map fmap,
+                                     favor_dtype dtype) {
+  Plan p;
+  if (dv < 1 || !make_plan(p, B, H, L, dk, m, 1, causal, dtype, device_cu_count(), (int)fmap)) return 0;
+  return align256(p.total) + 4 * strided_extra(p);
+}
+
+static bool contiguous(const long long* s, int H, int L, int d) {
+  return s[2] == d && s[1] == (long long)L * d && s[0] == (long long)H * L * d;
+}
+
+favor_status favor_attn_strided(const void* Q, const long long* q_strides, const void* K, const long long* k_strides,
+                                const void* V, const long long* v_strides, const float* W, int Hw, void* O,
+                                const long long* o_strides, int B, int H, int L, int dk, int dv, int m, float eps,
+                                int causal, favor_feature_map fmap, favor_dtype dtype, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!Q || !K || !V || !W || !O || !q_strides || !k_strides || !v_strides || !o_strides) return FAVOR_ERR_NULL;
+  favor_status st = check_shapes(B, H, L, dk, m, Hw, dtype);
+  if (st != FAVOR_OK) return st;
+  if (dv < 1 || dv > 65536) return FAVOR_ERR_SHAPE;
+  if ((int)fmap < FAVOR_FMAP_POSITIVE || (int)fmap > FAVOR_FMAP_TRIG) return FAVOR_ERR_UNSUPPORTED;
+  for (const long long* sp : {q_strides, k_strides, v_strides, o_strides})
+    for (int i = 0; i < 3; ++i)
+      if (sp[i] < 0) return FAVOR_ERR_SHAPE;
+  Plan p;
+  if (!make_plan(p, B, H, L, dk, m, Hw, causal, dtype, device_cu_count(), (int)fmap)) return FAVOR_ERR_HIP;
+  const size_t inner = align256(p.total), ex = strided_extra(p);
+  if (!ws || ws_bytes < inner + 4 * ex || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  char* qc = base + inner;
+  char* kc = qc + ex;
+  char* vc = kc + ex;
+  char* oc = vc + ex;
+  const bool qcont = contiguous(q_strides, H, L, dk), kcont = contiguous(k_strides, H, L, dk);
+  const bool same_w = dv == dk;
+  const bool vcont = same_w && contiguous(v_strides, H, L, dk), ocont = same_w && contiguous(o_strides, H, L, dk);
+  hipError_t e = hipSuccess;
+  const void* qp = Q;
+  const void* kp = K;
+  if (!qcont) {
+    e = gather_rows(Q, qc, p, q_strides, 0, dk, dk, s);
+    qp = qc;
+  }
+  if (e == hipSuccess && !kcont) {
+    e = gather_rows(K, kc, p, k_strides, 0, dk, dk, s);
+    kp = kc;
+  }
+  for (int c0 = 0; e == hipSuccess && c0 < dv; c0 += dk) {
+    const void* vp = V;
+    void* op = O;
+    if (!vcont) {
+      e = gather_rows(V, vc, p, v_strides, c0, dv, dk, s);
+      vp = vc;
+    }
+    if (!ocont) op = oc;
+    if (e != hipSuccess) break;
+    Tensors t{qp, kp, vp, W, op, eps, base};
+    e = causal ? launch_causal(p, t, s) : launch_noncausal(p, t, s);
+    if (e == hipSuccess && !ocont) e = scatter_rows(oc, O, p, o_strides, c0, dv - c0 < dk ? dv - c0 : dk, dk, s);
+  }
+  if (e == hipErrorNotSupported) return FAVOR_ERR_UNSUPPORTED;
+  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
 favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, void* O, int B, int H, int L, int d,
                                 float scale, int causal, favor_dtype dtype, void* stream) {
   if (!Q || !K || !V || !O) return FAVOR_ERR_NULL;

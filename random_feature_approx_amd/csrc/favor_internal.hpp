@@ -77,6 +77,10 @@ void timing_end(favor_kernel k, hipStream_t s);
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t gather_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int width, int n,
+                       hipStream_t s);
+hipError_t scatter_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int n, int srow,
+                        hipStream_t s);
 hipError_t launch_softmax(const Plan& p, const void* q, const void* k, const void* v, void* o, float scale,
                           int causal, hipStream_t s);
 hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
