@@ -26,8 +26,11 @@
  *    and the m x d states enter the other products as bf16 (nearest even);
  *    every product accumulates in float32, and states and sums are float32.
  *    FAVOR_F32: everything is float32.
- *  - Supported shapes: d in {32, 64, 128}; m a multiple of 32 with
- *    32 <= m <= 512; L >= 1; B, H >= 1; B*H*L*max(d,m) < 2^31.
+ *  - Supported shapes: d in {32, 64, 128}; 1 <= m <= 512 (the kernels work
+ *    in blocks of 32 features; for m not a multiple of 32 the missing
+ *    features are padding whose key-side features are set to exactly 0, so
+ *    they add nothing to any sum; the backward entry points need m a
+ *    multiple of 32); L >= 1; B, H >= 1; B*H*L*max(d,m) < 2^31.
  *  - stream is a hipStream_t passed as void* (NULL = default stream).  Calls
  *    only enqueue work; results are valid once the stream has been
  *    synchronised.

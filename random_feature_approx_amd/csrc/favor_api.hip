@@ -24,7 +24,7 @@ static favor_status check_shapes(int B, int H, int L, int d, int m, int Hw, favo
   if (Hw != 1 && Hw != H) return FAVOR_ERR_SHAPE;
   if (dt != FAVOR_F32 && dt != FAVOR_BF16) return FAVOR_ERR_UNSUPPORTED;
   if (d != 32 && d != 64 && d != 128) return FAVOR_ERR_UNSUPPORTED;
-  if (m < 32 || m > 512 || (m % 32) != 0) return FAVOR_ERR_UNSUPPORTED;
+  if (m < 1 || m > 512) return FAVOR_ERR_UNSUPPORTED;
   const int64_t big = (int64_t)B * H * L * (d > m ? d : m);
   if (big >= ((int64_t)1 << 31)) return FAVOR_ERR_SHAPE;
   return FAVOR_OK;
@@ -35,8 +35,9 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   if (check_shapes(B, H, L, d, m, Hw, dt) != FAVOR_OK || num_cus <= 0) return false;
   if (fmap < FAVOR_FMAP_POSITIVE || fmap > FAVOR_FMAP_TRIG) return false;
   p.fmap = fmap;
-  p.Mw = m;
-  if (fmap == FAVOR_FMAP_TRIG) m *= 2;      // a sine and a cosine per row of W
+  p.mt = m;
+  p.Mw = (m + 31) / 32 * 32;                // padding features up to a multiple of 32
+  m = fmap == FAVOR_FMAP_TRIG ? 2 * p.Mw : p.Mw;   // features: a sine and a cosine per row of W
   p.B = B; p.H = H; p.L = L; p.D = d; p.M = m; p.Hw = Hw; p.causal = causal ? 1 : 0; p.dt = dt;
   p.BH = B * H;
   p.esize = dt == FAVOR_BF16 ? 2 : 4;
@@ -44,7 +45,7 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   // least 256 tokens, whole 64-token chunks.
   // the bf16 FAVOR+ scan for d <= 64 owns two feature blocks per wave; the
   // generic scan (other maps, widths and float32) one
-  p.fbw = (dt == FAVOR_BF16 && d <= 64 && fmap == FAVOR_FMAP_POSITIVE) ? 2 : 1;
+  p.fbw = (dt == FAVOR_BF16 && d <= 64 && fmap == FAVOR_FMAP_POSITIVE && p.mt == p.Mw) ? 2 : 1;
   const int nfb = m / 32;
   p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
   p.rfbw = 1;   // two blocks per wave (4 waves) measured slower: fewer waves to hide latency
@@ -266,6 +267,7 @@ static void timer_free(Timer& t) {
 }
 
 size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype) {
+  if (m % 32 != 0) return 0;
   Plan p;
   if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count())) return 0;
   return p.btotal;
@@ -359,6 +361,7 @@ static favor_status bwd_common(const void* Q, const void* K, const void* V, cons
   if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
   if (st != FAVOR_OK) return st;
+  if (m % 32 != 0) return FAVOR_ERR_UNSUPPORTED;     // the backward needs whole 32-feature blocks
   Plan p;
   if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count())) return FAVOR_ERR_HIP;
   if (!ws || ws_bytes < p.btotal || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;

@@ -97,7 +97,8 @@ struct CausalArgs {
   float* den;             // [BH][L]
   int L, M, H, Hw, spans, span_len, fgroups;
   float eps;
-  int Mw;                 // rows of W per head (M, or M/2 for the trig map)
+  int Mw;                 // feature rows per head (M, or M/2 for the trig map), a multiple of 32
+  int mt;                 // rows of W per head as given; features of rows >= mt are padding
 };
 
 // LDS layout (bytes), computed identically on host and device.
@@ -148,9 +149,10 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
   const E* Kg = (const E*)a.k + hoff;
   const E* Vg = (const E*)a.v + hoff;
   E* Og = (E*)a.o + hoff;
-  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.Mw * D;
-  const float half_ln_m = 0.5f * logf((float)a.M);
-  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.mt * D;
+  const float half_ln_m = 0.5f * logf((float)a.mt);
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.mt) : 1.f;
+  const bool ragged = a.mt != a.Mw;
   const int t0 = span * a.span_len;
   const int t1 = min(a.L, t0 + a.span_len);
 
@@ -163,9 +165,11 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
     for (int i = 0; i < FBW; ++i) {
       const bool ok = fb0 + i < nfb;
       const int fbase = (ok ? fb0 + i : 0) * 32;
-      const float* wrow = wh + (size_t)((FM == FM_TRIG ? fbase % a.Mw : fbase) + l32) * D;
+      const int wr = (FM == FM_TRIG ? fbase % a.Mw : fbase) + l32;    // this lane's row of W
+      const bool wok = ok && wr < a.mt;
+      const float* wrow = wh + (size_t)(wok ? wr : 0) * D;
 #pragma unroll
-      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, ok);
+      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, wok);
       const float* pre = a.prefix + ((size_t)bh * a.spans + span) * a.M * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -223,6 +227,15 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
           for (int r = 0; r < 16; ++r) {
             aq[r] = fvalid ? FMap<FM>::phi(aq[r] + bq, cosine, tscale) : 0.f;
             ak[r] = fvalid ? FMap<FM>::phi(ak[r] + bk, cosine, tscale) : 0.f;
+          }
+          if (ragged) {
+            // padding features (rows of W past m) get phi(K) = 0, which keeps
+            // the state, the key sums and the chunk scores free of them
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int f = (fb0 + i) * 32 + crow(r, hh);
+              if ((FM == FM_TRIG ? f % a.Mw : f) >= a.mt) ak[r] = 0.f;
+            }
           }
 #pragma unroll
           for (int s2 = 0; s2 < NKT; ++s2) {
@@ -741,7 +754,7 @@ static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
   float* partz = (float*)(t.ws + p.off_partz);
   if (p.fbw != FBW) return hipErrorInvalidValue;
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
-               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw};
+               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw, p.mt};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
   hipLaunchKernelGGL((k_causal<Tr, D, FBW, FM>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
   timing_end(FAVOR_KERNEL_CAUSAL, s);
@@ -774,7 +787,7 @@ static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
   float* partz = (float*)(t.ws + p.off_partz);
   if (p.fbw != FBW) return hipErrorInvalidValue;
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
-               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw};
+               p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw, p.mt};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
   hipLaunchKernelGGL((k_causal2<D, FBW, C>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
   timing_end(FAVOR_KERNEL_CAUSAL, s);
@@ -794,7 +807,9 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (p.fmap) {
-    case FM_POS: break;
+    case FM_POS:
+      if (p.mt != p.Mw) return causal_fmap<FM_POS>(p, t, s);   // padding features: the generic scan
+      break;
     case FM_ELU1: return causal_fmap<FM_ELU1>(p, t, s);
     case FM_RELU: return causal_fmap<FM_RELU>(p, t, s);
     case FM_TRIG: return causal_fmap<FM_TRIG>(p, t, s);

@@ -15,7 +15,9 @@ struct Plan {
   int B, H, L, D, M, Hw, causal;
   favor_dtype dt;
   int fmap;             // feature map (FM_POS, FM_ELU1, FM_RELU, FM_TRIG)
-  int Mw;               // rows of W per head; M (features) is 2 Mw for the trig map
+  int mt;               // rows of W per head as given (m)
+  int Mw;               // m rounded up to a multiple of 32 (padding features are zero)
+                        // M (features) is Mw, or 2 Mw for the trig map
   int BH;
   int esize;            // bytes per element of Q, K, V, O
   // K-side reduction (non-causal state, or causal span aggregates)

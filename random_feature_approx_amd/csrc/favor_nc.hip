@@ -28,7 +28,8 @@ struct FeatArgs {
   const float* w;
   float* phi;
   int L, M, H, Hw;
-  int Mw;               // rows of W per head (M, or M/2 for the trig map)
+  int Mw;               // feature rows per head (M, or M/2 for the trig map), a multiple of 32
+  int mt;               // rows of W per head as given (Mw rounded m up to 32)
 };
 
 template <class Tr, int D, int FM>
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void k_features(FeatArgs a) {
   const int tok = blockIdx.x * 128 + w * 32 + l32;
   const bool tok_ok = tok < a.L;
   const E* xrow = (const E*)a.x + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * D;
-  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.Mw * D;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.mt * D;
   F xf[NKD];
   float ss = 0.f;
 #pragma unroll
@@ -62,28 +63,33 @@ __global__ __launch_bounds__(256) void k_features(FeatArgs a) {
     }
   }
   ss = half_sum(ss);
-  const float bias = FMap<FM>::row_bias(ss, 0.5f * logf((float)a.M));
-  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
+  const float bias = FMap<FM>::row_bias(ss, 0.5f * logf((float)a.mt));
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.mt) : 1.f;
   const int nfbw = a.Mw >> 5;
-  float* out = a.phi + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * a.M;
+  const int outw = FM == FM_TRIG ? 2 * a.mt : a.mt;       // features per row of Phi
+  float* out = a.phi + ((size_t)bh * a.L + (tok_ok ? tok : 0)) * outw;
   for (int fb = 0; fb < (a.M >> 5); ++fb) {
-    const float* wrow = wh + (size_t)((FM == FM_TRIG ? fb % nfbw : fb) * 32 + l32) * D;
+    const int wr = (FM == FM_TRIG ? fb % nfbw : fb) * 32 + l32;    // this lane's row of W
+    const bool wok = wr < a.mt;
+    const float* wrow = wh + (size_t)(wok ? wr : 0) * D;
     const bool cosine = fb >= nfbw;
     f32x16 acc = zero16();
 #pragma unroll
-    for (int s = 0; s < NKD; ++s) acc = Tr::pmma(w_frag<Tr, D, FM>(wrow, hh, s, true), xf[s], acc);
+    for (int s = 0; s < NKD; ++s) acc = Tr::pmma(w_frag<Tr, D, FM>(wrow, hh, s, wok), xf[s], acc);
     if (tok_ok) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = FMap<FM>::phi(acc[4 * i + j] + bias, cosine, tscale);
-        if constexpr (FM == FM_TRIG) {
-          // the page's order: feature 2i is the sine of omega_i, 2i+1 its cosine
+        if (FM == FM_TRIG || a.mt != a.Mw) {
+          // one feature at a time: rows past m are padding, and the trig map
+          // stores the page's order (2i the sine of omega_i, 2i+1 its cosine)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int f = fb * 32 + 8 * i + 4 * hh + j;
-            out[cosine ? 2 * (f - a.Mw) + 1 : 2 * f] = v[j];
+            const int r = cosine ? f - a.Mw : f;
+            if (r < a.mt) out[FM == FM_TRIG ? (cosine ? 2 * r + 1 : 2 * r) : f] = v[j];
           }
         } else {
           *(f32x4*)(out + fb * 32 + 8 * i + 4 * hh) = v;
@@ -106,7 +112,8 @@ struct RedArgs {
   float* part;   // [BH][splits][M][D]
   float* partz;  // [BH][splits][M]
   int L, M, H, Hw, splits, split_len;
-  int Mw;        // rows of W per head (M, or M/2 for the trig map)
+  int Mw;        // feature rows per head (M, or M/2 for the trig map), a multiple of 32
+  int mt;        // rows of W per head as given; features of rows >= mt are padding, set to 0
 };
 
 // Pipeline shape of the K-side kernels: tiles of TT tokens copied into a
@@ -163,19 +170,23 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
   const int fb0 = (fg * NW + w) * FBW;
   const E* K = (const E*)a.k + (size_t)bh * a.L * D;
   const E* V = (const E*)a.v + (size_t)bh * a.L * D;
-  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.Mw * D;
-  const float half_ln_m = 0.5f * logf((float)a.M);
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.mt * D;
+  const float half_ln_m = 0.5f * logf((float)a.mt);
   const int nfbw = a.Mw >> 5;
-  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.mt) : 1.f;
+  const bool ragged = a.mt != a.Mw;
 
   F wf[FBW][NKD];
+  bool wok[FBW];
 #pragma unroll
   for (int i = 0; i < FBW; ++i) {
     const bool ok = fb0 + i < nfb;
     const int fbw_ = ok ? fb0 + i : 0;
-    const float* wrow = wh + (size_t)((FM == FM_TRIG ? fbw_ % nfbw : fbw_) * 32 + l32) * D;
+    const int wr = (FM == FM_TRIG ? fbw_ % nfbw : fbw_) * 32 + l32;   // this lane's row of W
+    wok[i] = ok && wr < a.mt;
+    const float* wrow = wh + (size_t)(wok[i] ? wr : 0) * D;
 #pragma unroll
-    for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, ok);
+    for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, wok[i]);
   }
   f32x16 st[FBW][NDB];
   float zs[FBW];
@@ -318,6 +329,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
           const bool cosine = fb0 + i >= nfbw;
 #pragma unroll
           for (int r = 0; r < 16; ++r) e[r] = FMap<FM>::phi(e[r], cosine, tscale);
+          if (ragged && !wok[i]) e = zero16();           // padding features (lane = feature)
 #pragma unroll
           for (int s2 = 0; s2 < NKT; ++s2) {
             F pf = CFrag<Tr>::make(e, s2);
@@ -388,28 +400,29 @@ constexpr int kQuadsPerBlock = 256 / kSplitGroups;
 // lane (f, h) at k-group g hold d = (D/2) h + (16/WES) g + 0.. (the d-major
 // k order of the projection), so a wave reads 1 KB of contiguous memory.
 // The operand covers M features per head; for the trig map feature f uses
-// W row f mod Mw (its sine and its cosine share a row).
+// W row f mod Mw (its sine and its cosine share a row); rows past the mt
+// rows of W (padding up to a multiple of 32) are zero.
 template <class E, int FM>
-__device__ __forceinline__ void wprep_chunk(const float* w, void* out, int idx, int D, int M, int Mw) {
+__device__ __forceinline__ void wprep_chunk(const float* w, void* out, int idx, int D, int M, int Mw, int mt) {
   constexpr int WES = sizeof(E);
   constexpr int PER = 16 / WES;                      // d values per 16 bytes
   constexpr float sc = FMap<FM>::kWScale;
   const int nkg = D * WES / 32;
   const int f = idx & 31, h = (idx >> 5) & 1, rest = idx >> 6;
   const int g = rest % nkg, blk = rest / nkg;
-  int row = blk * 32 + f;
-  if constexpr (FM == FM_TRIG) {
-    const int nb = M >> 5;                           // feature blocks per head
-    row = (blk / nb) * Mw + ((blk % nb) * 32 + f) % Mw;
-  }
-  const float* src = w + (size_t)row * D + (D / 2) * h + PER * g;
+  const int nb = M >> 5;                             // feature blocks per head
+  const int lf = (blk % nb) * 32 + f;                // feature within the head
+  const int wr = FM == FM_TRIG ? lf % Mw : lf;       // its row of W
+  const bool ok = wr < mt;
+  const float* src = w + ((size_t)(blk / nb) * mt + (ok ? wr : 0)) * D + (D / 2) * h + PER * g;
   if constexpr (WES == 2) {
-    const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+    f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+    if (!ok) x0 = x1 = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 v = {pack_f16(x0[0] * sc, x0[1] * sc), pack_f16(x0[2] * sc, x0[3] * sc),
                pack_f16(x1[0] * sc, x1[1] * sc), pack_f16(x1[2] * sc, x1[3] * sc)};
     ((u32x4*)out)[idx] = v;
   } else {
-    ((f32x4*)out)[idx] = *(const f32x4*)src * sc;
+    ((f32x4*)out)[idx] = ok ? *(const f32x4*)src * sc : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -418,12 +431,12 @@ __device__ __forceinline__ void wprep_chunk(const float* w, void* out, int idx, 
 template <class E, int FM>
 __global__ __launch_bounds__(256) void k_combine(const float* part, const float* partz, E* mstate, E* zstate,
                                                  int splits, int M, int D, int BH, const float* w, void* wp,
-                                                 int n16w, int Mw) {
+                                                 int n16w, int Mw, int mt) {
   __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
   const int bh = blockIdx.y;
   if (bh == BH) {
     for (int idx = blockIdx.x * 256 + threadIdx.x; idx < n16w; idx += gridDim.x * 256)
-      wprep_chunk<E, FM>(w, wp, idx, D, M, Mw);
+      wprep_chunk<E, FM>(w, wp, idx, D, M, Mw, mt);
     return;
   }
   const int g = threadIdx.x / kQuadsPerBlock, qi = threadIdx.x % kQuadsPerBlock;
@@ -490,7 +503,8 @@ struct ApplyArgs {
   float eps;
   int groups_per_head, groups_total, steps, fch, nbuf;
   int stage_off;        // LDS offset of the per-wave output staging areas
-  int Mw;               // rows of W per head (M, or M/2 for the trig map)
+  int Mw;               // feature rows per head (M, or M/2 for the trig map), a multiple of 32
+  int mt;               // rows of W per head as given (padding features have zero state rows)
 };
 
 // NW waves per workgroup, TB 32-token blocks per wave.  LEAN: no Q prefetch,
@@ -519,8 +533,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
   const int nch = (a.M + FCH - 1) / FCH;
-  const float half_ln_m = 0.5f * logf((float)a.M);
-  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.Mw) : 1.f;
+  const float half_ln_m = 0.5f * logf((float)a.mt);
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.mt) : 1.f;
   const int g0 = blockIdx.x * a.steps;
   const int g1 = min(a.groups_total, g0 + a.steps);
 
@@ -820,7 +834,7 @@ static hipError_t with_fmap(int fmap, Fn&& f) {
 
 template <class Tr, int D>
 static hipError_t features_t(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s) {
-  FeatArgs a{x, w, phi, p.L, p.M, p.H, p.Hw, p.Mw};
+  FeatArgs a{x, w, phi, p.L, p.M, p.H, p.Hw, p.Mw, p.mt};
   dim3 grid((p.L + 127) / 128, p.BH);
   return with_fmap(p.fmap, [&]<int FM>() {
     timing_begin(FAVOR_KERNEL_FEATURES, s);
@@ -850,7 +864,7 @@ hipError_t launch_features(const Plan& p, const void* x, const float* w, float* 
 template <class Tr, int D>
 hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
                            hipStream_t s) {
-  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw};
+  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw, p.mt};
   // 8 waves of one feature block each, or 4 where a wave's registers exceed
   // half a SIMD's (two blocks per wave, sharing each K/V fragment read, ran
   // slower: half as many waves to hide the latency of each block's chain)
@@ -900,7 +914,7 @@ static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const
   const int nbuf = (p.fch >= p.M && 2 * buf + stage <= 150 * 1024) ? 2 : 1;
   const size_t stage_off = (nbuf * buf + 15) / 16 * 16;
   ApplyArgs a{t.q, wp, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch, nbuf,
-              (int)stage_off, p.Mw};
+              (int)stage_off, p.Mw, p.mt};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
   const size_t lds = stage_off + stage;
   if (TB * 32 != p.apply_tile || NW != p.apply_nw) return hipErrorInvalidValue;
@@ -939,16 +953,16 @@ hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
   hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
   if (e != hipSuccess) return e;
   const int nq = (p.M * p.D + p.M) / 4;
-  const int n16w = p.Hw * p.M * p.D * (p.dt == FAVOR_BF16 ? 2 : 4) / 16;
+  const int n16w = p.Hw * p.M * p.D * (p.dt == FAVOR_BF16 ? 2 : 4) / 16;   // M features per head
   dim3 cgrid((nq + kQuadsPerBlock - 1) / kQuadsPerBlock, p.BH + 1);
   e = with_fmap(p.fmap, [&]<int FM>() {
     timing_begin(FAVOR_KERNEL_COMBINE, s);
     if (p.dt == FAVOR_BF16)
       hipLaunchKernelGGL((k_combine<bf16, FM>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate,
-                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw);
+                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw, p.mt);
     else
       hipLaunchKernelGGL((k_combine<float, FM>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
-                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw);
+                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw, p.mt);
     timing_end(FAVOR_KERNEL_COMBINE, s);
     return hipGetLastError();
   });

@@ -56,7 +56,7 @@ def _nc(lib, q=1, k=1, v=1, w=1, hw=1, o=1, B=1, H=1, L=16, d=64, m=256, eps=1e-
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(w=0), 1), (dict(o=0), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(L=0), 2), (dict(hw=3, H=2), 2), (dict(B=1 << 14, H=1 << 14, L=64), 2),
-    (dict(d=48), 3), (dict(d=256), 3), (dict(m=48), 3), (dict(m=16), 3), (dict(m=544), 3), (dict(dt=7), 3),
+    (dict(d=48), 3), (dict(d=256), 3), (dict(m=0), 3), (dict(m=-32), 3), (dict(m=544), 3), (dict(dt=7), 3),
 ])
 def test_validation_errors(kw, code):
     assert _nc(_lib(), **kw) == code
@@ -69,13 +69,13 @@ def test_causal_and_dispatcher_validate_the_same_way():
                           ctypes.c_void_p(1), 1, 1, 16, 60, 256, 1e-6, 1, 1, None, 0, None) == 3
     assert lib.favor_features(None, None, 1, None, 1, 1, 16, 64, 256, 1, None) == 1
     assert lib.favor_features(ctypes.c_void_p(1), ctypes.c_void_p(1), 1, ctypes.c_void_p(1),
-                              1, 1, 16, 64, 100, 1, None) == 3
+                              1, 1, 16, 64, 600, 1, None) == 3
 
 
 def test_workspace_bytes_rejects_bad_shapes():
     lib = _lib()
     assert lib.favor_workspace_bytes(0, 1, 16, 64, 256, 0, 1) == 0
-    assert lib.favor_workspace_bytes(1, 1, 16, 64, 100, 1, 1) == 0
+    assert lib.favor_workspace_bytes(1, 1, 16, 64, 600, 1, 1) == 0
 
 
 def test_timing_api_argument_checks():

@@ -204,3 +204,38 @@ def test_causal_full_size_sampled(gpu, name):
         got = o[b, h, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
         worst = max(worst, row_rel_err(got, ref))
     assert worst <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# m not a multiple of 32 (padding features)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d,m,L", [("bf16", 64, 100, 300), ("bf16", 64, 1, 130), ("bf16", 32, 200, 257),
+                                         ("f32", 64, 33, 129), ("f32", 128, 250, 100)])
+def test_ragged_feature_count(gpu, causal, dtype, d, m, L):
+    """m not a multiple of 32: the kernels pad to whole 32-feature blocks
+    whose key-side features are exactly zero; the result equals the
+    definition with the m given features (1/sqrt(m) with the true m)."""
+    x = synth.random_case(4000 + d + m + L, 1, 2, L, d, m, dtype)
+    print(f"[ragged] causal={causal} {dtype} d={d} m={m} L={L}", flush=True)
+    out = _run_attn(gpu, x, dtype, causal=causal)
+    assert row_rel_err(out, _ref(x, causal)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("kind", ["positive", "trig", "relu"])
+def test_ragged_features_and_maps(gpu, kind):
+    import torch
+    x = synth.random_case(4100, 1, 2, 200, 64, 72, "f32", qk_scale=0.15 if kind == "trig" else None)
+    phi = gpu.features(to_device(x["q"], "f32"), torch.from_numpy(x["w"]).cuda(), fmap=kind)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.feature_map(x["q64"][0, h], x["w64"][h], kind) for h in range(2)])[None]
+    assert phi.shape == ref.shape
+    assert row_rel_err(to_f64(phi), ref) <= 1e-4
+    for causal in (False, True):
+        q, k, v = (to_device(x[n], "f32") for n in ("q", "k", "v"))
+        o = gpu.attn(q, k, v, torch.from_numpy(x["w"]).cuda(), causal=causal, fmap=kind)
+        torch.cuda.synchronize()
+        fn = oracle.attn_causal if causal else oracle.attn_noncausal
+        ref_o = oracle.per_head(fn, x["q64"], x["k64"], x["v64"], x["w64"], kind=kind)
+        assert row_rel_err(to_f64(o), ref_o) <= TOL["f32"]
