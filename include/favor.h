@@ -241,6 +241,25 @@ favor_status favor_attn_causal_bwd(const void* Q, const void* K, const void* V,
                                    void* stream);
 
 /*
+ * Draw the random projection W [Hw, m, d] (float32, device memory owned by
+ * the caller) from a seed on the device, as the Performer page's code draws
+ * a fresh projection for every call; orthogonal != 0 gives the orthogonal
+ * random features of the performer-2020 notes' key points.  Definition:
+ * Philox4x64-10 (Salmon et al., SC 2011) keyed by (seed, 0); block
+ * (c, row, head, purpose) gives four 64-bit words w, u = ((w >> 11) + 1/2)
+ * 2^-53, and Box-Muller on (u0, u1), (u2, u3) gives normals 4c .. 4c+3 of
+ * (row, head, purpose).  Orthogonal: block b of head h is the d x d matrix
+ * G[i][j] = normal j of (b d + i, h, 0); row b d + i of W is column i of the
+ * Q factor of G (QR with a positive diagonal), times the norm of d normals
+ * of (b d + i, h, 1).  Otherwise W[h][f][j] = normal j of (f, h, 0).  Every
+ * row is multiplied by scale (1: rows N(0, I); 1/sqrt(d): the page code's
+ * randn / sqrt(d)).  Deterministic for a given seed and shape.  Shapes:
+ * Hw >= 1, 1 <= m <= 65536, 1 <= d <= 128.
+ */
+favor_status favor_draw_projection(unsigned long long seed, int Hw, int m, int d, int orthogonal,
+                                   float scale, float* W, void* stream);
+
+/*
  * Exact softmax attention O = softmax(scale * Q K^T) V, optionally masked
  * to keys j <= i: the quadratic attention FAVOR+ approximates (softmax-kernel
  * equation of "Linear Attention > Kernel Feature Maps"; the left side of the
@@ -278,7 +297,8 @@ typedef enum {
   FAVOR_KERNEL_BWD_Q = 9,      /* backward: query side (dQ)                       */
   FAVOR_KERNEL_BWD_K = 10,     /* backward: key side (dK, dV)                     */
   FAVOR_KERNEL_SOFTMAX = 11,   /* exact softmax attention (favor_softmax_attn)    */
-  FAVOR_KERNEL_COUNT = 12
+  FAVOR_KERNEL_DRAW = 12,      /* projection sampler (favor_draw_projection)     */
+  FAVOR_KERNEL_COUNT = 13
 } favor_kernel;
 
 favor_status favor_timing_start(favor_kernel k, int capacity);

@@ -24,7 +24,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS", "softmax_attn", "attn_strided",
+__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS", "softmax_attn", "attn_strided", "draw_projection",
            "workspace_bytes", "attn_backward", "bwd_workspace_bytes", "FavorError", "STATUS", "KERNELS",
            "timing_start", "timing_stop"]
 
@@ -37,7 +37,8 @@ STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid shape", 3: "unsupport
           4: "workspace missing or too small", 5: "HIP runtime error", 6: "internal error"}
 F32, BF16 = 0, 1
 KERNELS = {"k_features": 0, "k_reduce": 1, "k_combine": 2, "k_apply": 3, "k_span_scan": 4, "k_causal": 5,
-           "k_bprep": 6, "k_bred": 7, "k_bcombine": 8, "k_bside_q": 9, "k_bside_k": 10, "k_softmax": 11}
+           "k_bprep": 6, "k_bred": 7, "k_bcombine": 8, "k_bside_q": 9, "k_bside_k": 10, "k_softmax": 11,
+           "k_draw": 12}
 
 
 class FavorError(RuntimeError):
@@ -87,6 +88,8 @@ def load():
     lib.favor_attn_strided.restype = i
     lib.favor_attn_strided.argtypes = [vp, ll3, vp, ll3, vp, ll3, vp, i, vp, ll3, i, i, i, i, i, i, f, i, i, i,
                                        vp, sz, vp]
+    lib.favor_draw_projection.restype = i
+    lib.favor_draw_projection.argtypes = [ctypes.c_ulonglong, i, i, i, i, f, vp, vp]
     lib.favor_softmax_attn.restype = i
     lib.favor_softmax_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.favor_bwd_workspace_bytes.restype = sz
@@ -253,6 +256,20 @@ def attn_strided(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, 
     if st != 0:
         raise FavorError("favor_attn_strided", st)
     return o
+
+
+def draw_projection(seed: int, heads: int, m: int, d: int, orthogonal: bool = True, scale: float = 1.0,
+                    device=None):
+    """W [heads, m, d] float32 drawn on the device from `seed` (Philox4x64-10
+    normals; orthogonal blocks with chi(d) row lengths, or independent rows)."""
+    lib = load()
+    torch = _torch()
+    W = torch.empty((heads, m, d), dtype=torch.float32, device=device or "cuda")
+    st = lib.favor_draw_projection(int(seed) & ((1 << 64) - 1), heads, m, d, int(bool(orthogonal)), float(scale),
+                                   ctypes.c_void_p(W.data_ptr()), _stream())
+    if st != 0:
+        raise FavorError("favor_draw_projection", st)
+    return W
 
 
 def softmax_attn(q, k, v, scale=None, causal: bool = False, out=None):

@@ -343,6 +343,15 @@ favor_status favor_attn_strided(const void* Q, const long long* q_strides, const
   return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
+favor_status favor_draw_projection(unsigned long long seed, int Hw, int m, int d, int orthogonal, float scale,
+                                   float* W, void* stream) {
+  if (!W) return FAVOR_ERR_NULL;
+  if (Hw < 1 || m < 1 || m > 65536 || d < 1 || d > 128) return FAVOR_ERR_SHAPE;
+  if ((int64_t)Hw * m * d >= ((int64_t)1 << 31)) return FAVOR_ERR_SHAPE;
+  return launch_draw(seed, Hw, m, d, orthogonal ? 1 : 0, scale, W, (hipStream_t)stream) == hipSuccess ? FAVOR_OK
+                                                                                                     : FAVOR_ERR_HIP;
+}
+
 favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, void* O, int B, int H, int L, int d,
                                 float scale, int causal, favor_dtype dtype, void* stream) {
   if (!Q || !K || !V || !O) return FAVOR_ERR_NULL;
@@ -432,6 +441,7 @@ const char* favor_kernel_name(favor_kernel k) {
     case FAVOR_KERNEL_BWD_Q: return "k_bside_q";
     case FAVOR_KERNEL_BWD_K: return "k_bside_k";
     case FAVOR_KERNEL_SOFTMAX: return "k_softmax";
+    case FAVOR_KERNEL_DRAW: return "k_draw";
     default: return "unknown";
   }
 }

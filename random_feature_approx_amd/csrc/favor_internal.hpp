@@ -83,6 +83,8 @@ hipError_t gather_rows(const void* src, void* dst, const Plan& p, const long lon
                        hipStream_t s);
 hipError_t scatter_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int n, int srow,
                         hipStream_t s);
+hipError_t launch_draw(unsigned long long seed, int Hw, int m, int d, int orthogonal, float scale, float* W,
+                       hipStream_t s);
 hipError_t launch_softmax(const Plan& p, const void* q, const void* k, const void* v, void* o, float scale,
                           int causal, hipStream_t s);
 hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
