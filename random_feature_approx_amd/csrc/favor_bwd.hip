@@ -412,7 +412,7 @@ struct BSideArgs {
   float eps;
 };
 
-template <class Tr, int D, bool SIDE_Q>
+template <class Tr, int D, bool SIDE_Q, int TB>
 __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
@@ -425,40 +425,47 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
   constexpr int WES = VPS == 8 ? 2 : 4;
   constexpr int NKG = D * WES / 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, l32 = lane & 31;
-  const int g = blockIdx.x * 4 + w;
+  const int g = blockIdx.x * 4 + w;                  // group of TB x 32 tokens
   if (g >= a.total) return;                         // no barriers below
   const int bh = g / a.tiles_per_head, tile = g % a.tiles_per_head;
   const int head = bh % a.H;
   const int nfb = a.M >> 5;
-  const int tok = tile * 32 + l32;
-  const bool ok = tok < a.L;
-  const E* xrow = (const E*)a.x + ((size_t)bh * a.L + (ok ? tok : 0)) * D;
-  const E* yrow = (const E*)a.y + ((size_t)bh * a.L + (ok ? tok : 0)) * D;
   const float half_ln_m = 0.5f * logf((float)a.M);
 
-  // this lane's half of its token's row of X (projection type) and of Y
-  F xf[NKD], yf[NKD];
-  float ss = 0.f;
+  // this lane's half of its tokens' rows of X (projection type) and of Y
+  int tok[TB];
+  bool ok[TB];
+  const E* xrow[TB];
+  F xf[TB][NKD], yf[TB][NKD];
+  float bias[TB];
 #pragma unroll
-  for (int s = 0; s < NKD; ++s) {
-    const int d0 = (D / 2) * hh + VPS * s;
-    if constexpr (VPS == 8) {
-      const u32x4 xv = ok ? *(const u32x4*)(xrow + d0) : u32x4{0u, 0u, 0u, 0u};
-      yf[s] = ok ? *(const u32x4*)(yrow + d0) : u32x4{0u, 0u, 0u, 0u};
-      xf[s] = Tr::to_proj(xv);
+  for (int tb = 0; tb < TB; ++tb) {
+    tok[tb] = (tile * TB + tb) * 32 + l32;
+    ok[tb] = tok[tb] < a.L;
+    xrow[tb] = (const E*)a.x + ((size_t)bh * a.L + (ok[tb] ? tok[tb] : 0)) * D;
+    const E* yrow = (const E*)a.y + ((size_t)bh * a.L + (ok[tb] ? tok[tb] : 0)) * D;
+    float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = bf16_lo(xv[j]), q = bf16_hi(xv[j]);
-        ss = fmaf(p, p, fmaf(q, q, ss));
+    for (int s = 0; s < NKD; ++s) {
+      const int d0 = (D / 2) * hh + VPS * s;
+      if constexpr (VPS == 8) {
+        const u32x4 xv = ok[tb] ? *(const u32x4*)(xrow[tb] + d0) : u32x4{0u, 0u, 0u, 0u};
+        yf[tb][s] = ok[tb] ? *(const u32x4*)(yrow + d0) : u32x4{0u, 0u, 0u, 0u};
+        xf[tb][s] = Tr::to_proj(xv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = bf16_lo(xv[j]), q = bf16_hi(xv[j]);
+          ss = fmaf(p, p, fmaf(q, q, ss));
+        }
+      } else {
+        xf[tb][s] = ok[tb] ? xrow[tb][d0] : 0.f;
+        yf[tb][s] = ok[tb] ? yrow[d0] : 0.f;
+        ss = fmaf(xf[tb][s], xf[tb][s], ss);
       }
-    } else {
-      xf[s] = ok ? xrow[d0] : 0.f;
-      yf[s] = ok ? yrow[d0] : 0.f;
-      ss = fmaf(xf[s], xf[s], ss);
     }
+    ss = half_sum(ss);
+    bias[tb] = ok[tb] ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
   }
-  ss = half_sum(ss);
-  const float bias = ok ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
 
   const int hw = a.Hw == 1 ? 0 : head;
   const char* wph = (const char*)a.wph + (size_t)hw * nfb * NKG * 2 * 32 * 16;
@@ -469,44 +476,53 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
   const E* rlo = (const E*)a.rows_lo + (size_t)bh * a.M * D;
   const float* zf = a.zf + (size_t)bh * a.M;
 
-  // phi^T[f][t] of feature block fb (rows f = 32 fb + crow(r, h))
-  auto features = [&](int fb) -> f32x16 {
-    f32x16 p = zero16();
+  // projection operand of block fb (hi, lo)
+  auto wproj = [&](int fb, F (&wfr)[SP::NS][NKD]) {
 #pragma unroll
     for (int pp = 0; pp < SP::NS; ++pp) {
       const char* base = (pp == 0 ? wph : wpl) + (size_t)fb * NKG * 2 * 32 * 16;
       if constexpr (WES == 2) {
 #pragma unroll
-        for (int s = 0; s < NKD; ++s) p = Tr::pmma(*(const u32x4*)(base + ((s * 2 + hh) * 32 + l32) * 16), xf[s], p);
+        for (int s = 0; s < NKD; ++s) wfr[pp][s] = *(const u32x4*)(base + ((s * 2 + hh) * 32 + l32) * 16);
       } else {
 #pragma unroll
         for (int gk = 0; gk < NKG; ++gk) {
           const f32x4 v = *(const f32x4*)(base + ((gk * 2 + hh) * 32 + l32) * 16);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p = Tr::pmma(v[j], xf[4 * gk + j], p);
+          for (int j = 0; j < 4; ++j) wfr[pp][4 * gk + j] = v[j];
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(p[r] + bias);
-    return p;
   };
-  // rows-operand product R Y^T for feature block fb (R = M or dM, hi + lo),
-  // accumulated onto acc: rows f, lane = token
-  auto rows_times_y = [&](int fb, f32x16 acc) -> f32x16 {
+  // rows operand (M or dM, hi + lo) of block fb
+  auto rows = [&](int fb, F (&rf)[SP::NS][NKD]) {
     const size_t rb = (size_t)(fb * 32 + l32) * D + (D / 2) * hh;
 #pragma unroll
     for (int s = 0; s < NKD; ++s) {
-      F rf[SP::NS];
       if constexpr (VPS == 8) {
-        rf[0] = *(const u32x4*)(rhi + rb + VPS * s);
-        if constexpr (SP::NS == 2) rf[1] = *(const u32x4*)(rlo + rb + VPS * s);
+        rf[0][s] = *(const u32x4*)(rhi + rb + VPS * s);
+        if constexpr (SP::NS == 2) rf[1][s] = *(const u32x4*)(rlo + rb + VPS * s);
       } else {
-        rf[0] = rhi[rb + s];
+        rf[0][s] = rhi[rb + s];
       }
-#pragma unroll
-      for (int pp = 0; pp < SP::NS; ++pp) acc = Tr::mma(rf[pp], yf[s], acc);
     }
+  };
+  // phi^T[f][t] of block fb for token block tb (rows f = 32 fb + crow(r, h))
+  auto features = [&](const F (&wfr)[SP::NS][NKD], int tb) -> f32x16 {
+    f32x16 p = zero16();
+#pragma unroll
+    for (int s = 0; s < NKD; ++s)
+#pragma unroll
+      for (int pp = 0; pp < SP::NS; ++pp) p = Tr::pmma(wfr[pp][s], xf[tb][s], p);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(p[r] + bias[tb]);
+    return p;
+  };
+  auto rows_times_y = [&](const F (&rf)[SP::NS][NKD], int tb, f32x16 acc) -> f32x16 {
+#pragma unroll
+    for (int s = 0; s < NKD; ++s)
+#pragma unroll
+      for (int pp = 0; pp < SP::NS; ++pp) acc = Tr::mma(rf[pp][s], yf[tb][s], acc);
     return acc;
   };
   // z or dz values of the rows of feature block fb, in accumulator order
@@ -520,13 +536,14 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
     }
     return zr;
   };
-  // acc[db] += W^T gacc (the c-row feature order of gacc), both operands
-  // split into hi + lo (three products: hi hi, hi lo, lo hi)
-  auto wt_times = [&](int fb, const f32x16& gacc, f32x16 (&acc)[NDB]) {
+  // acc[tb][db] += W^T gacc[tb] (c-row feature order), both operands split
+  // into hi + lo (three products: hi hi, hi lo, lo hi)
+  auto wt_times = [&](int fb, const f32x16 (&gacc)[TB], f32x16 (&acc)[TB][NDB]) {
 #pragma unroll
     for (int s2 = 0; s2 < NKT; ++s2) {
-      F gfr[SP::NS];
-      SP::split(gacc, s2, gfr);
+      F gfr[TB][SP::NS];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) SP::split(gacc[tb], s2, gfr[tb]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const size_t e = (((((size_t)fb * NKT + s2) * NDB + db) * 2 + hh) * 32 + l32) * VPS;
@@ -537,50 +554,84 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
         } else {
           wfr[0] = wt[e];
         }
-        acc[db] = Tr::mma(wfr[0], gfr[0], acc[db]);
-        if constexpr (SP::NS == 2) {
-          acc[db] = Tr::mma(wfr[0], gfr[1], acc[db]);
-          acc[db] = Tr::mma(wfr[1], gfr[0], acc[db]);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          acc[tb][db] = Tr::mma(wfr[0], gfr[tb][0], acc[tb][db]);
+          if constexpr (SP::NS == 2) {
+            acc[tb][db] = Tr::mma(wfr[0], gfr[tb][1], acc[tb][db]);
+            acc[tb][db] = Tr::mma(wfr[1], gfr[tb][0], acc[tb][db]);
+          }
         }
       }
     }
   };
+  // store 16 values of a d^T accumulator for token block tb (columns d0..d0+3)
+  auto store4 = [&](E* row, int d0, const float (&v)[4]) {
+    if constexpr (ES == 2) {
+      *(u32x2*)(row + d0) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    } else {
+      *(f32x4*)(row + d0) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+  };
 
-  f32x16 dacc[NDB];
+  f32x16 dacc[TB][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dacc[db] = zero16();
-  E* drow = (E*)a.dx + ((size_t)bh * a.L + (ok ? tok : 0)) * D;
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dacc[tb][db] = zero16();
 
   if constexpr (SIDE_Q) {
-    float den = 0.f, sy = 0.f;
-    for (int fb = 0; fb < nfb; ++fb) {
-      const f32x16 phi = features(fb);
-      const f32x16 zr = zrows(fb);
-      const f32x16 y = rows_times_y(fb, zero16());
+    float den[TB], sy[TB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        den = fmaf(phi[r], zr[r], den);
-        sy = fmaf(phi[r], y[r], sy);
+    for (int tb = 0; tb < TB; ++tb) den[tb] = sy[tb] = 0.f;
+    for (int fb = 0; fb < nfb; ++fb) {
+      F wfr[SP::NS][NKD], rf[SP::NS][NKD];
+      wproj(fb, wfr);
+      rows(fb, rf);
+      const f32x16 zr = zrows(fb);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const f32x16 phi = features(wfr, tb);
+        const f32x16 y = rows_times_y(rf, tb, zero16());
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          den[tb] = fmaf(phi[r], zr[r], den[tb]);
+          sy[tb] = fmaf(phi[r], y[r], sy[tb]);
+        }
       }
     }
-    den = half_sum(den) + a.eps;
-    sy = half_sum(sy);
-    const float ratio = sy / den;
-    if (ok && hh == 0) {
-      a.lg[(size_t)bh * a.L + tok] = log2f(den);
-      a.cw[(size_t)bh * a.L + tok] = -ratio;
+    float ratio[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      den[tb] = half_sum(den[tb]) + a.eps;
+      sy[tb] = half_sum(sy[tb]);
+      ratio[tb] = sy[tb] / den[tb];
+      if (ok[tb] && hh == 0) {
+        a.lg[(size_t)bh * a.L + tok[tb]] = log2f(den[tb]);
+        a.cw[(size_t)bh * a.L + tok[tb]] = -ratio[tb];
+      }
     }
     for (int fb = 0; fb < nfb; ++fb) {
-      f32x16 phi = features(fb);
+      F wfr[SP::NS][NKD], rf[SP::NS][NKD];
+      wproj(fb, wfr);
+      rows(fb, rf);
       const f32x16 zr = zrows(fb);
-      const f32x16 y = rows_times_y(fb, zero16());
+      f32x16 gq[TB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) phi[r] *= y[r] - zr[r] * ratio;
-      wt_times(fb, phi, dacc);
+      for (int tb = 0; tb < TB; ++tb) {
+        gq[tb] = features(wfr, tb);
+        const f32x16 y = rows_times_y(rf, tb, zero16());
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gq[tb][r] *= y[r] - zr[r] * ratio[tb];
+      }
+      wt_times(fb, gq, dacc);
     }
-    const float inv = 1.f / den;
-    const float rs = sy * a.eps * inv;               // sum_f phi_f (y_f - z_f s/D)
-    if (ok) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      if (!ok[tb]) continue;
+      const float inv = 1.f / den[tb];
+      const float rs = sy[tb] * a.eps * inv;           // sum_f phi_f (y_f - z_f s/D)
+      E* drow = (E*)a.dx + ((size_t)bh * a.L + tok[tb]) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -588,31 +639,39 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
           const int d0 = db * 32 + 8 * i + 4 * hh;
           float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (dacc[db][4 * i + j] - rs * (float)xrow[d0 + j]) * inv;
-          if constexpr (ES == 2) {
-            *(u32x2*)(drow + d0) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-          } else {
-            *(f32x4*)(drow + d0) = f32x4{v[0], v[1], v[2], v[3]};
-          }
+          for (int j = 0; j < 4; ++j) v[j] = (dacc[tb][db][4 * i + j] - rs * (float)xrow[tb][d0 + j]) * inv;
+          store4(drow, d0, v);
         }
     }
   } else {
-    f32x16 vacc[NDB];
+    f32x16 vacc[TB][NDB];
+    float rs[TB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) vacc[db] = zero16();
+    for (int tb = 0; tb < TB; ++tb) {
+      rs[tb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vacc[tb][db] = zero16();
+    }
     const char* opb = (const char*)a.op + (size_t)bh * a.M * D * ES;
-    float rs = 0.f;
     for (int fb = 0; fb < nfb; ++fb) {
-      f32x16 phi = features(fb);
+      F wfr[SP::NS][NKD], rf[SP::NS][NKD];
+      wproj(fb, wfr);
+      rows(fb, rf);
+      const f32x16 zr = zrows(fb);
+      f32x16 gk[TB];
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) gk[tb] = features(wfr, tb);
       // dv^T[d][t] += dM^T phi^T: the state operand in the apply's order
       if constexpr (VPS == 8) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int gi = 2 * fb + s2;
-          const F pf = CFrag<Tr>::make(phi, s2);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            vacc[db] = Tr::mma(*(const u32x4*)(opb + ((gi * 2 + hh) * D + db * 32 + l32) * 16), pf, vacc[db]);
+          for (int db = 0; db < NDB; ++db) {
+            const F mf = *(const u32x4*)(opb + ((gi * 2 + hh) * D + db * 32 + l32) * 16);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) vacc[tb][db] = Tr::mma(mf, CFrag<Tr>::make(gk[tb], s2), vacc[tb][db]);
+          }
         }
       } else {
 #pragma unroll
@@ -622,21 +681,29 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
           for (int db = 0; db < NDB; ++db) {
             const f32x4 mf = *(const f32x4*)(opb + ((gi * 2 + hh) * D + db * 32 + l32) * 16);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vacc[db] = Tr::mma(mf[j], phi[4 * s4 + j], vacc[db]);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb) vacc[tb][db] = Tr::mma(mf[j], gk[tb][4 * s4 + j], vacc[tb][db]);
           }
         }
       }
-      const f32x16 u = rows_times_y(fb, zrows(fb));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        phi[r] *= u[r];
-        rs += phi[r];
+      for (int tb = 0; tb < TB; ++tb) {
+        const f32x16 u = rows_times_y(rf, tb, zr);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          gk[tb][r] *= u[r];
+          rs[tb] += gk[tb][r];
+        }
       }
-      wt_times(fb, phi, dacc);
+      wt_times(fb, gk, dacc);
     }
-    rs = half_sum(rs);
-    if (ok) {
-      E* vrow = (E*)a.dy + ((size_t)bh * a.L + tok) * D;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const float rsum = half_sum(rs[tb]);
+      if (!ok[tb]) continue;
+      E* drow = (E*)a.dx + ((size_t)bh * a.L + tok[tb]) * D;
+      E* vrow = (E*)a.dy + ((size_t)bh * a.L + tok[tb]) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -645,16 +712,11 @@ __global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
           float v[4], dv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            v[j] = dacc[db][4 * i + j] - rs * (float)xrow[d0 + j];
-            dv[j] = vacc[db][4 * i + j];
+            v[j] = dacc[tb][db][4 * i + j] - rsum * (float)xrow[tb][d0 + j];
+            dv[j] = vacc[tb][db][4 * i + j];
           }
-          if constexpr (ES == 2) {
-            *(u32x2*)(drow + d0) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-            *(u32x2*)(vrow + d0) = u32x2{pack_bf16(dv[0], dv[1]), pack_bf16(dv[2], dv[3])};
-          } else {
-            *(f32x4*)(drow + d0) = f32x4{v[0], v[1], v[2], v[3]};
-            *(f32x4*)(vrow + d0) = f32x4{dv[0], dv[1], dv[2], dv[3]};
-          }
+          store4(drow, d0, v);
+          store4(vrow, d0, dv);
         }
     }
   }
@@ -706,7 +768,9 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   const int nq = (p.M * D + p.M) / 4;
   const dim3 cgrid((nq + kBQuads - 1) / kBQuads, p.BH);
   E* rlo = Tr::VPS == 8 ? (E*)b.rows_lo : nullptr;
-  const int tph = (p.L + 31) / 32;
+  // per-token side: TB 32-token blocks per wave share each operand read
+  constexpr int TB = (Tr::VPS == 8 && D <= 64) ? 2 : 1;
+  const int tph = (p.L + 32 * TB - 1) / (32 * TB);
   const int total = p.BH * tph;
   const dim3 sgrid((total + 3) / 4);
   // state M, z from K, V
@@ -725,7 +789,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     BSideArgs a{t.q, t.g, b.rows_hi, b.rows_lo, nullptr, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dq, nullptr, b.lg, b.cw,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps};
     timing_begin(FAVOR_KERNEL_BWD_Q, s);
-    hipLaunchKernelGGL((k_bside<Tr, D, true>), sgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bside<Tr, D, true, TB>), sgrid, dim3(256), 0, s, a);
     timing_end(FAVOR_KERNEL_BWD_Q, s);
   }
   // dM, dz from Q, G
@@ -744,7 +808,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     BSideArgs a{t.k, t.v, b.rows_hi, b.rows_lo, b.op, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dk, t.dv, nullptr, nullptr,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps};
     timing_begin(FAVOR_KERNEL_BWD_K, s);
-    hipLaunchKernelGGL((k_bside<Tr, D, false>), sgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bside<Tr, D, false, TB>), sgrid, dim3(256), 0, s, a);
     timing_end(FAVOR_KERNEL_BWD_K, s);
   }
   return hipGetLastError();
