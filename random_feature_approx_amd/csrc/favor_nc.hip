@@ -329,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
           const bool cosine = fb0 + i >= nfbw;
 #pragma unroll
           for (int r = 0; r < 16; ++r) e[r] = FMap<FM>::phi(e[r], cosine, tscale);
-          if (ragged && !wok[i]) e = zero16();           // padding features (lane = feature)
+
 #pragma unroll
           for (int s2 = 0; s2 < NKT; ++s2) {
             F pf = CFrag<Tr>::make(e, s2);
@@ -348,12 +348,24 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
     if (more) prep_write(tt + 1);
   }
 
+  // the partials are linear in phi: features of padding rows of W (m not a
+  // multiple of 32) are written as exact zeros
   float* P = a.part + ((size_t)bh * a.splits + split) * a.M * D;
   float* Pz = a.partz + ((size_t)bh * a.splits + split) * a.M;
 #pragma unroll
   for (int i = 0; i < FBW; ++i) {
     if (fb0 + i < nfb) {
       const int f0 = (fb0 + i) * 32;
+      if (ragged) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int f = f0 + crow(r, hh);
+            if ((FM == FM_TRIG ? f % a.Mw : f) >= a.mt) st[i][db][r] = 0.f;
+          }
+        if (!wok[i]) zs[i] = 0.f;
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
