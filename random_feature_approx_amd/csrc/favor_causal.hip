@@ -454,7 +454,10 @@ struct CausalLds2 {
   static constexpr int kTotal = kZ + 4 * 64 * 4;          // z of 4 waves x 64 features
 };
 
-template <int D, int FBW, int C>
+// FULL: every feature group fills all 4 x FBW blocks (M a multiple of
+// 128 FBW), so no block needs the -inf bias of a missing feature block and
+// the projection accumulators start at the row biases.
+template <int D, int FBW, int C, bool FULL>
 __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
   using Tr = TrBF16;
   using E = bf16;
@@ -584,11 +587,13 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
           kf[s] = row_frag<Tr, D>(cur + LY::kKh + (tb * 32 + l32) * RS, hh, s);
         }
         const float bq0 = sBq[tb * 32 + l32], bk0 = sBk[tb * 32 + l32];
+        // FULL: both blocks start from the token's bias (lane = token)
+        const f32x16 bq16 = splat16(FULL ? bq0 : 0.f), bk16 = splat16(FULL ? bk0 : 0.f);
 #pragma unroll
         for (int i = 0; i < FBW; ++i) {
           const bool fvalid = fb0 + i < nfb;
           const float bq = fvalid ? bq0 : -INFINITY, bk = fvalid ? bk0 : -INFINITY;
-          f32x16 aq = zero16(), ak = zero16();
+          f32x16 aq = bq16, ak = bk16;
 #pragma unroll
           for (int s = 0; s < NKD; ++s) {
             aq = Tr::pmma(wf[i][s], qf[s], aq);          // P^T[f][t]
@@ -596,8 +601,8 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            aq[r] = exp2_fast(aq[r] + bq);
-            ak[r] = exp2_fast(ak[r] + bk);
+            aq[r] = exp2_fast(FULL ? aq[r] : aq[r] + bq);
+            ak[r] = exp2_fast(FULL ? ak[r] : ak[r] + bk);
           }
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
@@ -780,7 +785,7 @@ static hipError_t causal_fmap(const Plan& p, const Tensors& t, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int D, int FBW, int C>
+template <int D, int FBW, int C, bool FULL>
 static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
   using LY = CausalLds2<D, C>;
   float* part = (float*)(t.ws + p.off_part);
@@ -789,7 +794,7 @@ static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
                p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw, p.mt};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
-  hipLaunchKernelGGL((k_causal2<D, FBW, C>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
+  hipLaunchKernelGGL((k_causal2<D, FBW, C, FULL>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
   timing_end(FAVOR_KERNEL_CAUSAL, s);
   return hipGetLastError();
 }
@@ -817,8 +822,8 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   }
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
-      case 32: return causal2_t<32, 2, 32>(p, t, s);
-      case 64: return causal2_t<64, 2, 32>(p, t, s);
+      case 32: return p.M % 256 ? causal2_t<32, 2, 32, false>(p, t, s) : causal2_t<32, 2, 32, true>(p, t, s);
+      case 64: return p.M % 256 ? causal2_t<64, 2, 32, false>(p, t, s) : causal2_t<64, 2, 32, true>(p, t, s);
       case 128: return causal_t<TrBF16, 128, 1, FM_POS>(p, t, s);
     }
   } else {

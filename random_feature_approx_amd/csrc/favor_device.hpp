@@ -255,4 +255,12 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// Accumulator with every element equal to x (a per-lane starting value).
+__device__ __forceinline__ f32x16 splat16(float x) {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = x;
+  return z;
+}
+
 }  // namespace favor

@@ -709,11 +709,13 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
         const bool cosine = f0 + fb * 32 >= a.Mw;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-          pacc[tb] = zero16();
+          // the accumulator starts at the token's bias (every row of lane t
+          // is token t), so the projection returns P^T[f][t] + bias[t]
+          pacc[tb] = splat16(bias[tb]);
 #pragma unroll
           for (int s = 0; s < NKD; ++s) pacc[tb] = Tr::pmma(wfr[s], qf[tb][s], pacc[tb]);   // P^T[f][t], lane = t
 #pragma unroll
-          for (int r = 0; r < 16; ++r) pacc[tb][r] = FMap<FM>::phi(pacc[tb][r] + bias[tb], cosine, tscale);
+          for (int r = 0; r < 16; ++r) pacc[tb][r] = FMap<FM>::phi(pacc[tb][r], cosine, tscale);
         }
         if constexpr (Tr::VPS == 8) {
           // group gi = 2 fb + s2 holds 16 features; lane (d, hh) reads 8 of them
