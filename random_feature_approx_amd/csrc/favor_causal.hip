@@ -530,6 +530,7 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
     }
   };
 
+
   for (int fg = 0; fg < a.fgroups; ++fg) {
     const int fb0 = (fg * 4 + w) * FBW;
     F wf[FBW][NKD];
@@ -551,40 +552,19 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
       zreg[i] = ok ? a.prefixz[((size_t)bh * a.spans + span) * a.M + fbase + l32] : 0.f;
     }
 
-    // prologue: chunk 0 into buffer 0 with its V^T, chunk 1 in registers
-    load_chunk(t0);
-    __syncthreads();                                     // previous feature group fully done
-#pragma unroll
-    for (int i = 0; i < FBW; ++i) sZ[i * 32 + l32] = zreg[i];
-    store_chunk(smem, min(C, t1 - t0));
-    if (t0 + C < t1) load_chunk(t0 + C);
-    wait_lgkm0();
-    raw_barrier();
-    transpose_v(smem);
-
-    int c = 0;
-    for (int c0 = t0; c0 < t1; c0 += C, ++c) {
-      const int nv = min(C, t1 - c0);
-      char* cur = smem + (c & 1) * LY::BUF;
-      char* nxt = smem + ((c + 1) & 1) * LY::BUF;
-      wait_lgkm0();
-      raw_barrier();                                     // chunk c staged everywhere; last reduction read
-      // branch-free so that the whole chunk is one scheduling region: past
-      // the end the staged rows are zero and no row is loaded
-      store_chunk(nxt, min(C, t1 - c0 - C));
-      load_chunk(c0 + 2 * C);
-
-      // ---- feature maps of this wave's features, lane = token -------------
-      F pq[FBW][NTB][2], pk[FBW][NTB][2];
-      const float* sBq = (const float*)(cur + LY::kBq);
-      const float* sBk = (const float*)(cur + LY::kBk);
+    // feature maps of this wave's features for the chunk staged in buf,
+    // lane = token; computed one chunk ahead (see the chunk loop)
+    F pq[FBW][NTB][2], pk[FBW][NTB][2];
+    auto feature_maps = [&](const char* buf) {
+      const float* sBq = (const float*)(buf + LY::kBq);
+      const float* sBk = (const float*)(buf + LY::kBk);
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
         F qf[NKD], kf[NKD];
 #pragma unroll
         for (int s = 0; s < NKD; ++s) {
-          qf[s] = row_frag<Tr, D>(cur + LY::kQh + (tb * 32 + l32) * RS, hh, s);
-          kf[s] = row_frag<Tr, D>(cur + LY::kKh + (tb * 32 + l32) * RS, hh, s);
+          qf[s] = row_frag<Tr, D>(buf + LY::kQh + (tb * 32 + l32) * RS, hh, s);
+          kf[s] = row_frag<Tr, D>(buf + LY::kKh + (tb * 32 + l32) * RS, hh, s);
         }
         const float bq0 = sBq[tb * 32 + l32], bk0 = sBk[tb * 32 + l32];
         // FULL: both blocks start from the token's bias (lane = token)
@@ -611,6 +591,32 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
           }
         }
       }
+    };
+
+    // prologue: chunk 0 into buffer 0 with its V^T, chunk 1 in registers
+    load_chunk(t0);
+    __syncthreads();                                     // previous feature group fully done
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) sZ[i * 32 + l32] = zreg[i];
+    store_chunk(smem, min(C, t1 - t0));
+    if (t0 + C < t1) load_chunk(t0 + C);
+    wait_lgkm0();
+    raw_barrier();
+    transpose_v(smem);
+    feature_maps(smem);
+
+    int c = 0;
+    for (int c0 = t0; c0 < t1; c0 += C, ++c) {
+      const int nv = min(C, t1 - c0);
+      char* cur = smem + (c & 1) * LY::BUF;
+      char* nxt = smem + ((c + 1) & 1) * LY::BUF;
+      wait_lgkm0();
+      raw_barrier();                                     // chunk c staged everywhere; last reduction read
+      // branch-free so that the whole chunk is one scheduling region: past
+      // the end the staged rows are zero and no row is loaded
+      store_chunk(nxt, min(C, t1 - c0 - C));
+      load_chunk(c0 + 2 * C);
+
 
       // ---- numerators per 32-query block: intra-chunk scores, then phi(Q) S
 #pragma unroll
@@ -694,7 +700,12 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
       for (int i = 0; i < FBW; ++i) sZ[i * 32 + l32] = zreg[i];
 
       wait_lgkm0();
-      raw_barrier();                                     // partials complete
+      raw_barrier();                                     // partials complete; the next chunk staged
+      // The next chunk's feature maps (matrix cores and exponentials) and its
+      // V^T go here, where they overlap the reduction's LDS reads and adds;
+      // past the end the staged rows are zero and the result is unused.
+      feature_maps(nxt);
+      if (c0 + C < t1) transpose_v(nxt);
       {
         constexpr int TPR = 256 / C;                     // threads per output row
         constexpr int DP = D / TPR;                      // outputs per thread
@@ -747,7 +758,6 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
           }
         }
       }
-      if (c0 + C < t1) transpose_v(nxt);
     }
   }
 }

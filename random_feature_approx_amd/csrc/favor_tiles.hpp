@@ -67,7 +67,7 @@ struct TileLoader {
       int row = c / CPR, cc = c % CPR;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (c < TT * CPR && row < nvalid)
-        v = __builtin_nontemporal_load((const u32x4*)((const char*)src + ((size_t)row * D) * sizeof(E) + cc * 16));
+        v = *(const u32x4*)((const char*)src + ((size_t)row * D) * sizeof(E) + cc * 16);
       r[i] = v;
     }
   }
