@@ -412,8 +412,14 @@ struct BSideArgs {
   float eps;
 };
 
+// Waves per SIMD the compiler must fit: two for the bf16 query side at d <= 64
+// (a few registers spill outside the hot loop; measured 11% faster than one),
+// one elsewhere (forcing two spills dozens of registers inside it).
+template <class Tr, int D, bool SIDE_Q>
+constexpr int bside_waves() { return (Tr::VPS == 8 && D <= 64 && SIDE_Q) ? 2 : 1; }
+
 template <class Tr, int D, bool SIDE_Q, int TB>
-__global__ __launch_bounds__(256) void k_bside(BSideArgs a) {
+__global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(BSideArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
   using SP = Bw<Tr>;
@@ -991,8 +997,14 @@ __device__ __forceinline__ f32x16 rows_of(const float* v, int hh) {
 // MODE kK:  the key side, walking the chunks of a span in reverse.
 constexpr int kQ1 = 0, kQ2 = 1, kK = 2;
 
+// Two waves per SIMD for the bf16 query walks at d <= 64 (the second walk
+// spills a few registers and runs 30% faster than at one wave), one for the
+// key walk, whose state would spill inside the chunk loop.
 template <class Tr, int D, int MODE>
-__global__ __launch_bounds__(256) void k_bcausal(BCausalArgs a) {
+constexpr int bcausal_waves() { return (Tr::VPS == 8 && D <= 64 && MODE != kK) ? 2 : 1; }
+
+template <class Tr, int D, int MODE>
+__global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal(BCausalArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
   using SP = Bw<Tr>;
