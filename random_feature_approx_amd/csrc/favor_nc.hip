@@ -281,6 +281,9 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
     if (tt + 2 < ntiles) issue(tt + 2);
     const bool more = tt + 1 < ntiles;
     if (more) prep_read(tt + 1);
+    // matrix work of tile tt at raised issue priority: the other workgroup's
+    // preparation (vector and LDS work) fills in behind it (measured ~5%)
+    __builtin_amdgcn_s_setprio(1);
     const char* pb = prep_buf(tt);
     const float* sBias = (const float*)(pb + LY::kBias);
     // projections of every 32-token block of the tile first, then their
@@ -345,6 +348,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (more) prep_write(tt + 1);
   }
 
