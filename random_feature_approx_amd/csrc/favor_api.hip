@@ -43,9 +43,9 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.esize = dt == FAVOR_BF16 ? 2 : 4;
   // reduction split: about two workgroups per compute unit, ranges of at
   // least 256 tokens, whole 64-token chunks.
-  // the bf16 FAVOR+ scan for d <= 64 owns two feature blocks per wave; the
-  // generic scan (other maps, widths and float32) one
-  p.fbw = (dt == FAVOR_BF16 && d <= 64 && fmap == FAVOR_FMAP_POSITIVE && p.mt == p.Mw) ? 2 : 1;
+  // the bf16 scan for d <= 64 (every feature map) owns two feature blocks
+  // per wave; the generic scan (bf16 d = 128 and float32) one
+  p.fbw = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
   const int nfb = m / 32;
   p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
   p.rfbw = 1;   // two blocks per wave (4 waves) measured slower: fewer waves to hide latency

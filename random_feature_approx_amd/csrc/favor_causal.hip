@@ -454,10 +454,12 @@ struct CausalLds2 {
   static constexpr int kTotal = kZ + 4 * 64 * 4;          // z of 4 waves x 64 features
 };
 
-// FULL: every feature group fills all 4 x FBW blocks (M a multiple of
-// 128 FBW), so no block needs the -inf bias of a missing feature block and
-// the projection accumulators start at the row biases.
-template <int D, int FBW, int C, bool FULL>
+// FM: the feature map (FMap).  FULL (FAVOR+ only): every feature group
+// fills all 4 x FBW blocks (M a multiple of 128 FBW), so no block needs the
+// -inf bias of a missing feature block and the projection accumulators start
+// at the row biases.  RAG: m is not a multiple of 32; padding features
+// (rows of W past m) get phi(K) = 0.
+template <int D, int FBW, int C, bool FULL, int FM, bool RAG>
 __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
   using Tr = TrBF16;
   using E = bf16;
@@ -483,8 +485,10 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
   const E* Kg = (const E*)a.k + hoff;
   const E* Vg = (const E*)a.v + hoff;
   E* Og = (E*)a.o + hoff;
-  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.M * D;
-  const float half_ln_m = 0.5f * logf((float)a.M);
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.mt * D;
+  const float half_ln_m = 0.5f * logf((float)a.mt);
+  const float tscale = FM == FM_TRIG ? rsqrtf((float)a.mt) : 1.f;
+  const int nfbw = a.Mw >> 5;                              // blocks of distinct rows of W
   const int t0 = span * a.span_len;
   const int t1 = min(a.L, t0 + a.span_len);
   if (t0 >= t1) return;                                    // whole workgroup
@@ -511,8 +515,8 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
     lq.store_proj(buf + LY::kQh, tid);
     lk.store_proj(buf + LY::kKh, tid);
     lv.store(buf + LY::kV, tid);
-    lq.row_bias((float*)(buf + LY::kBq), tid, nv, half_ln_m);
-    lk.row_bias((float*)(buf + LY::kBk), tid, nv, half_ln_m);
+    lq.template row_bias<FM>((float*)(buf + LY::kBq), tid, nv, half_ln_m);
+    lk.template row_bias<FM>((float*)(buf + LY::kBk), tid, nv, half_ln_m);
   };
   // V^T fragment (tb, s2, db): lane (d, hh) holds V[32 tb + crow(8 s2 + j, hh)][32 db + d]
   auto vt_at = [&](const char* buf, int tb, int s2, int db) -> const char* {
@@ -541,9 +545,11 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
     for (int i = 0; i < FBW; ++i) {
       const bool ok = fb0 + i < nfb;
       const int fbase = (ok ? fb0 + i : 0) * 32;
-      const float* wrow = wh + (size_t)(fbase + l32) * D;
+      const int wr = (FM == FM_TRIG ? fbase % a.Mw : fbase) + l32;    // this lane's row of W
+      const bool wok = ok && wr < a.mt;
+      const float* wrow = wh + (size_t)(wok ? wr : 0) * D;
 #pragma unroll
-      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D>(wrow, hh, s, ok);
+      for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, wok);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -568,7 +574,8 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
         }
         const float bq0 = sBq[tb * 32 + l32], bk0 = sBk[tb * 32 + l32];
         // FULL: both blocks start from the token's bias (lane = token)
-        const f32x16 bq16 = splat16(FULL ? bq0 : 0.f), bk16 = splat16(FULL ? bk0 : 0.f);
+        constexpr bool kInit = FULL && FM == FM_POS;
+        const f32x16 bq16 = splat16(kInit ? bq0 : 0.f), bk16 = splat16(kInit ? bk0 : 0.f);
 #pragma unroll
         for (int i = 0; i < FBW; ++i) {
           const bool fvalid = fb0 + i < nfb;
@@ -579,10 +586,20 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
             aq = Tr::pmma(wf[i][s], qf[s], aq);          // P^T[f][t]
             ak = Tr::pmma(wf[i][s], kf[s], ak);
           }
+          const bool cosine = fb0 + i >= nfbw;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            aq[r] = exp2_fast(FULL ? aq[r] : aq[r] + bq);
-            ak[r] = exp2_fast(FULL ? ak[r] : ak[r] + bk);
+            aq[r] = FMap<FM>::phi(kInit ? aq[r] : aq[r] + bq, cosine, tscale);
+            ak[r] = FMap<FM>::phi(kInit ? ak[r] : ak[r] + bk, cosine, tscale);
+          }
+          if constexpr (RAG) {
+            // padding features: phi(K) = 0 keeps the state, the key sums and
+            // the chunk scores free of them
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int f = (fb0 + i) * 32 + crow(r, hh);
+              if ((FM == FM_TRIG ? f % a.Mw : f) >= a.mt) ak[r] = 0.f;
+            }
           }
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
@@ -783,12 +800,26 @@ static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
 }
 
 // the other feature maps run the generic scan (one feature block per wave)
+template <int D, int FBW, int C, bool FULL, int FM, bool RAG>
+static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s);
+
+template <int D, int FM>
+static hipError_t causal2_full(const Plan& p, const Tensors& t, hipStream_t s) {
+  if (p.mt != p.Mw) return causal2_t<D, 2, 32, false, FM, true>(p, t, s);
+  if constexpr (FM == FM_POS) {
+    if (p.M % 256 == 0) return causal2_t<D, 2, 32, true, FM, false>(p, t, s);
+  }
+  return causal2_t<D, 2, 32, false, FM, false>(p, t, s);
+}
+
+// bf16 d <= 64: the 32-token scan with two feature blocks per wave; bf16
+// d = 128 and float32: the generic scan
 template <int FM>
 static hipError_t causal_fmap(const Plan& p, const Tensors& t, hipStream_t s) {
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
-      case 32: return causal_t<TrBF16, 32, 1, FM>(p, t, s);
-      case 64: return causal_t<TrBF16, 64, 1, FM>(p, t, s);
+      case 32: return causal2_full<32, FM>(p, t, s);
+      case 64: return causal2_full<64, FM>(p, t, s);
       case 128: return causal_t<TrBF16, 128, 1, FM>(p, t, s);
     }
   } else {
@@ -801,7 +832,7 @@ static hipError_t causal_fmap(const Plan& p, const Tensors& t, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int D, int FBW, int C, bool FULL>
+template <int D, int FBW, int C, bool FULL, int FM, bool RAG>
 static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
   using LY = CausalLds2<D, C>;
   float* part = (float*)(t.ws + p.off_part);
@@ -810,7 +841,7 @@ static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
                p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw, p.mt};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
-  hipLaunchKernelGGL((k_causal2<D, FBW, C, FULL>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
+  hipLaunchKernelGGL((k_causal2<D, FBW, C, FULL, FM, RAG>), dim3(p.splits, p.BH), dim3(256), (size_t)LY::kTotal, s, a);
   timing_end(FAVOR_KERNEL_CAUSAL, s);
   return hipGetLastError();
 }
@@ -828,28 +859,12 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (p.fmap) {
-    case FM_POS:
-      if (p.mt != p.Mw) return causal_fmap<FM_POS>(p, t, s);   // padding features: the generic scan
-      break;
+    case FM_POS: return causal_fmap<FM_POS>(p, t, s);
     case FM_ELU1: return causal_fmap<FM_ELU1>(p, t, s);
     case FM_RELU: return causal_fmap<FM_RELU>(p, t, s);
     case FM_TRIG: return causal_fmap<FM_TRIG>(p, t, s);
     default: return hipErrorInvalidValue;
   }
-  if (p.dt == FAVOR_BF16) {
-    switch (p.D) {
-      case 32: return p.M % 256 ? causal2_t<32, 2, 32, false>(p, t, s) : causal2_t<32, 2, 32, true>(p, t, s);
-      case 64: return p.M % 256 ? causal2_t<64, 2, 32, false>(p, t, s) : causal2_t<64, 2, 32, true>(p, t, s);
-      case 128: return causal_t<TrBF16, 128, 1, FM_POS>(p, t, s);
-    }
-  } else {
-    switch (p.D) {
-      case 32: return causal_t<TrF32, 32, 1, FM_POS>(p, t, s);
-      case 64: return causal_t<TrF32, 64, 1, FM_POS>(p, t, s);
-      case 128: return causal_t<TrF32, 128, 1, FM_POS>(p, t, s);
-    }
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace favor
