@@ -77,7 +77,11 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   if (p.apply_steps < 1) p.apply_steps = 1;
   p.apply_groups = (total + p.apply_steps - 1) / p.apply_steps;
   const int wes = dt == FAVOR_BF16 ? 2 : 4;         // projection operand bytes
-  int fch = 98304 / (d * wes + d * p.esize + p.esize);   // projection operand, M and z per feature
+  // LDS for the apply's per-head operands: what the 160 KB leave after the
+  // lean kernel's per-wave Q slots and output rounds (16 waves), else 96 KB
+  const int lean_extra = lean ? 16 * 32 * d * 2 + 16 * (64 / (d * 2 / 16)) * (d * 2 + 16) : 0;
+  const int budget = lean ? 160 * 1024 - lean_extra - 1024 : 98304;
+  int fch = budget / (d * wes + d * p.esize + p.esize);   // projection operand, M and z per feature
   fch = fch / 32 * 32;
   p.fch = fch < m ? fch : m;
   // workspace

@@ -518,7 +518,8 @@ struct ApplyArgs {
   int L, M, H, Hw;
   float eps;
   int groups_per_head, groups_total, steps, fch, nbuf;
-  int stage_off;        // LDS offset of the per-wave output staging areas
+  int stage_off;        // LDS offset of the per-wave output staging areas (LEAN: Q slots)
+  int ostage_off;       // LEAN, 16-bit: LDS offset of the per-wave output rounds
   int Mw;               // feature rows per head (M, or M/2 for the trig map), a multiple of 32
   int mt;               // rows of W per head as given (padding features have zero state rows)
 };
@@ -597,13 +598,14 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
   // global->LDS loads while the current group is computed (no registers held)
   using QT = DmaTile<E, D, 32, 64>;
   char* qslot = smem + a.stage_off + w * QT::BYTES;
-  const typename QT::Lane qplan = QT::lane_plan(0, lane);
+  // copy addresses are recomputed per group (a few integer operations) rather
+  // than held in registers for the whole kernel
   auto issue_q = [&](int g) {
     const int bh = g / a.groups_per_head;
     const int tbase = (g % a.groups_per_head) * (NW * TB * 32) + w * TB * 32;
     const E* Q = (const E*)a.q + (size_t)bh * a.L * D;
     const bool any = tbase < a.L;                        // rows past the end re-read row 0
-    QT::issue_plan(qslot, (const char*)(Q + (size_t)(any ? tbase : 0) * D), any ? a.L - tbase : 1, qplan, 0);
+    QT::issue(qslot, Q + (size_t)(any ? tbase : 0) * D, any ? a.L - tbase : 1, 0, lane);
   };
   if constexpr (LEAN) {
     if (g0 < g1) issue_q(g0);
@@ -713,13 +715,16 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
         const bool cosine = f0 + fb * 32 >= a.Mw;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-          // the accumulator starts at the token's bias (every row of lane t
-          // is token t), so the projection returns P^T[f][t] + bias[t]
-          pacc[tb] = splat16(bias[tb]);
+          // non-LEAN: the accumulator starts at the token's bias (every row of
+          // lane t is token t), so the projection returns P^T[f][t] + bias[t];
+          // LEAN adds the bias afterwards (the 16 copies would not fit its
+          // 128 registers: spilled values reloaded in the group loop wait for
+          // every outstanding copy and store)
+          pacc[tb] = LEAN ? zero16() : splat16(bias[tb]);
 #pragma unroll
           for (int s = 0; s < NKD; ++s) pacc[tb] = Tr::pmma(wfr[s], qf[tb][s], pacc[tb]);   // P^T[f][t], lane = t
 #pragma unroll
-          for (int r = 0; r < 16; ++r) pacc[tb][r] = FMap<FM>::phi(pacc[tb][r], cosine, tscale);
+          for (int r = 0; r < 16; ++r) pacc[tb][r] = FMap<FM>::phi(LEAN ? pacc[tb][r] + bias[tb] : pacc[tb][r], cosine, tscale);
         }
         if constexpr (Tr::VPS == 8) {
           // group gi = 2 fb + s2 holds 16 features; lane (d, hh) reads 8 of them
@@ -785,7 +790,51 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
     char* stage = smem + a.stage_off + w * 32 * RSO;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      if constexpr (!kStage) {
+      if constexpr (LEAN && ES == 2) {
+        // Whole rows per store: the lane halves first swap 4-value groups so
+        // that each lane holds 16-byte pieces of its row, then rounds of RPR
+        // rows pass through this wave's small LDS area and come back with 8
+        // (d = 64) or 4 (d = 32) lanes per row, every store instruction
+        // writing RPR consecutive rows (one contiguous KB).
+        constexpr int RB = D * ES, CPO = RB / 16, RPR = 64 / CPO, RSS = RB + 16;
+        const float inv = 1.0f / (half_sum(den[tb]) + a.eps);
+        u32x4 piece[NDB][2];                             // d = 32 db + 16 j + 8 hh, 8 values
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const unsigned a0 = pack_bf16(oacc[tb][db][8 * j] * inv, oacc[tb][db][8 * j + 1] * inv);
+            const unsigned a1 = pack_bf16(oacc[tb][db][8 * j + 2] * inv, oacc[tb][db][8 * j + 3] * inv);
+            const unsigned b0 = pack_bf16(oacc[tb][db][8 * j + 4] * inv, oacc[tb][db][8 * j + 5] * inv);
+            const unsigned b1 = pack_bf16(oacc[tb][db][8 * j + 6] * inv, oacc[tb][db][8 * j + 7] * inv);
+            // rows 8j..8j+3 of half 0 are d 16j..16j+3, of half 1 d 16j+4..16j+7;
+            // rows 8j+4..8j+7: d 16j+8..16j+11 (half 0), 16j+12..16j+15 (half 1).
+            // Half 0 keeps a and sends b; half 1 sends a and keeps b.
+            const unsigned send0 = hh ? a0 : b0, send1 = hh ? a1 : b1;
+            const auto s0 = __builtin_amdgcn_permlane32_swap(send0, send0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(send1, send1, false, false);
+            const unsigned r0 = hh ? s0[0] : s0[1], r1 = hh ? s1[0] : s1[1];   // the other half's values
+            piece[db][j] = hh ? u32x4{r0, r1, b0, b1} : u32x4{a0, a1, r0, r1};
+          }
+        char* ost = smem + a.ostage_off + w * RPR * RSS;
+        const int row0 = tbase + tb * 32;
+#pragma unroll
+        for (int rd = 0; rd < 32 / RPR; ++rd) {
+          if (l32 >= rd * RPR && l32 < (rd + 1) * RPR) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                *(u32x4*)(ost + (l32 - rd * RPR) * RSS + (db * 4 + 2 * j + hh) * 16) = piece[db][j];
+          }
+          const int r = lane / CPO, c = lane % CPO;
+          const u32x4 v = *(const u32x4*)(ost + r * RSS + c * 16);
+          const int tok = row0 + rd * RPR + r;
+          if (tok < a.L) *(u32x4*)(O + (size_t)tok * D + c * 8) = v;
+          wait_lgkm0();                                  // read before the next round's writes
+        }
+        continue;
+      } else if constexpr (!kStage) {
         const int tok = tbase + tb * 32 + l32;
         const float inv = 1.0f / (half_sum(den[tb]) + a.eps);
         if (tok < a.L) {
@@ -929,12 +978,14 @@ static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const
   // output staging rows (non-LEAN, rows up to 128 bytes) or the LEAN Q slots
   const size_t stage = LEAN ? (size_t)NW * 32 * D * sizeof(E)
                             : (D * sizeof(E) <= 128 ? (size_t)NW * 32 * (D * sizeof(E) + 16) : 0);
-  const int nbuf = (p.fch >= p.M && 2 * buf + stage <= 150 * 1024) ? 2 : 1;
+  // LEAN, 16-bit: per wave, rounds of 64 / (row bytes / 16) rows of D + 8 elements
+  const size_t ostage = (LEAN && sizeof(E) == 2) ? (size_t)NW * (64 / (D * sizeof(E) / 16)) * (D * sizeof(E) + 16) : 0;
+  const int nbuf = (p.fch >= p.M && 2 * buf + stage + ostage <= 150 * 1024) ? 2 : 1;
   const size_t stage_off = (nbuf * buf + 15) / 16 * 16;
   ApplyArgs a{t.q, wp, mstate, zstate, t.o, p.L, p.M, p.H, p.Hw, t.eps, gph, total, p.apply_steps, p.fch, nbuf,
-              (int)stage_off, p.Mw, p.mt};
+              (int)stage_off, (int)(stage_off + stage), p.Mw, p.mt};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
-  const size_t lds = stage_off + stage;
+  const size_t lds = stage_off + stage + ostage;
   if (TB * 32 != p.apply_tile || NW != p.apply_nw) return hipErrorInvalidValue;
   return with_fmap(p.fmap, [&]<int FM>() {
     timing_begin(FAVOR_KERNEL_APPLY, s);
