@@ -56,7 +56,9 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   // chunk scan runs one workgroup per (span, head) and walks feature groups
   // in turn, so spans alone fill the device.
   const int per_head = causal ? p.BH : p.BH * p.rfgroups;
-  int splits = (target + per_head - 1) / per_head;
+  // at most one round of resident workgroups: a few extra workgroups would
+  // run as a second, mostly empty round
+  int splits = target / per_head;
   const int max_splits = (L + 255) / 256;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
