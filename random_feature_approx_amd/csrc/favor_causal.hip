@@ -4,12 +4,14 @@
 // z_i = sum_{j<=i} phi(k_j)   (prefix-sum form of the study notes' case 2;
 // the denominator is its analogue of the non-causal normaliser).
 //
-// L is cut into spans (one workgroup each) and spans into chunks of 64 tokens.
+// L is cut into spans (one workgroup each) and spans into chunks of tokens
+// (32 in the bf16 scan for d <= 64, 64 in the generic scan).
 //   1. k_reduce (shared with the non-causal path) computes every span's
 //      aggregate [sum phi(k) v^T | sum phi(k)] in float32.
 //   2. k_span_scan turns the aggregates into exclusive prefixes in place, in
 //      a fixed order of additions (deterministic).
-//   3. k_causal walks the chunks of a span starting from its prefix.  For a
+//   3. k_causal2 (bf16, d <= 64) or k_causal walks the chunks of a span
+//      starting from its prefix.  For a
 //      chunk c with queries Q_c, keys K_c and values V_c:
 //        num = tril(phi(Q_c) phi(K_c)^T) V_c + phi(Q_c) S      (masked tile
 //              includes the diagonal)
@@ -799,9 +801,11 @@ static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
   return hipGetLastError();
 }
 
-// the other feature maps run the generic scan (one feature block per wave)
 template <int D, int FBW, int C, bool FULL, int FM, bool RAG>
 static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s);
+
+// the bf16 32-token scan's variant: ragged m, FAVOR+ with whole feature
+// groups (bias-initialised projections), or the general case
 
 template <int D, int FM>
 static hipError_t causal2_full(const Plan& p, const Tensors& t, hipStream_t s) {
