@@ -239,3 +239,23 @@ def test_ragged_features_and_maps(gpu, kind):
         fn = oracle.attn_causal if causal else oracle.attn_noncausal
         ref_o = oracle.per_head(fn, x["q64"], x["k64"], x["v64"], x["w64"], kind=kind)
         assert row_rel_err(to_f64(o), ref_o) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("kind", ["positive", "elu1", "relu", "trig"])
+@pytest.mark.parametrize("d,m,L", [(64, 72, 300), (32, 40, 97)])
+def test_ragged_maps_bf16(gpu, kind, d, m, L):
+    """bf16, m not a multiple of 32, every feature map: the 32-token causal
+    scan's padded-feature path (and for trig a feature pair whose sine and
+    cosine blocks share a wave) against the definition with m features."""
+    import torch
+    x = synth.random_case(4200 + d + m, 1, 2, L, d, m, "bf16", qk_scale=0.15 if kind == "trig" else None)
+    print(f"[ragged bf16] {kind} d={d} m={m} L={L}", flush=True)
+    for causal in (False, True):
+        q, k, v = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+        o = gpu.attn(q, k, v, torch.from_numpy(x["w"]).cuda(), causal=causal, fmap=kind)
+        torch.cuda.synchronize()
+        fn = oracle.attn_causal if causal else oracle.attn_noncausal
+        ref_o = oracle.per_head(fn, x["q64"], x["k64"], x["v64"], x["w64"], kind=kind)
+        err = row_rel_err(to_f64(o), ref_o)
+        print(f"[ragged bf16]   causal={causal} err {err:.3g}", flush=True)
+        assert err <= TOL["bf16"]
