@@ -636,6 +636,15 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
       // heavy) issues first, and the other wave's reduction and exponentials
       // fill in behind it (measured 10-15% faster than equal priorities).
       __builtin_amdgcn_s_setprio(1);
+      // this chunk's V^T fragments, used by the intra-chunk products and the
+      // state update, read once
+      F vtf[NTB][2][NDB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) vtf[tb][s2][db] = *(const F*)vt_at(cur, tb, s2, db);
       // branch-free so that the whole chunk is one scheduling region: past
       // the end the staged rows are zero and no row is loaded
       store_chunk(nxt, min(C, t1 - c0 - C));
@@ -667,7 +676,7 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) dacc = dot2_bf16(af[j], 0x3f803f80u, dacc);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) nacc[db] = Tr::mma(*(const F*)vt_at(cur, tkb, s2, db), af, nacc[db]);
+            for (int db = 0; db < NDB; ++db) nacc[db] = Tr::mma(vtf[tkb][s2][db], af, nacc[db]);
           }
         }
 #pragma unroll
@@ -712,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) zc = dot2_bf16(ktf[j], 0x3f803f80u, zc);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) st[i][db] = Tr::mma(ktf, *(const F*)vt_at(cur, tb, s2, db), st[i][db]);
+            for (int db = 0; db < NDB; ++db) st[i][db] = Tr::mma(ktf, vtf[tb][s2][db], st[i][db]);
           }
         }
         zc = half_sum(zc);

@@ -605,7 +605,13 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
     const int tbase = (g % a.groups_per_head) * (NW * TB * 32) + w * TB * 32;
     const E* Q = (const E*)a.q + (size_t)bh * a.L * D;
     const bool any = tbase < a.L;                        // rows past the end re-read row 0
-    QT::issue(qslot, Q + (size_t)(any ? tbase : 0) * D, any ? a.L - tbase : 1, 0, lane);
+    // the lane index comes from an opaque instruction so that the per-lane
+    // offsets are recomputed here rather than kept live (and spilled) across
+    // the group loop: a spill reload waits for every outstanding memory
+    // operation, this group's output stores included
+    int lane_now;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_now));
+    QT::issue(qslot, Q + (size_t)(any ? tbase : 0) * D, any ? a.L - tbase : 1, 0, lane_now);
   };
   if constexpr (LEAN) {
     if (g0 < g1) issue_q(g0);
