@@ -59,6 +59,10 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
   const int s0 = min(spans, g * per), s1 = min(spans, s0 + per);
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 sum = zero;
+  // at most 8 spans per group (up to 64 spans): the values stay in registers
+  // for the second pass instead of being read again
+  f32x4 keep[8];
+  const bool kept = s1 - s0 <= 8;
   if (active) {
     for (int s = s0; s < s1; s += 8) {
       f32x4 v[8];
@@ -66,6 +70,10 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
       for (int j = 0; j < 8; ++j) v[j] = s + j < s1 ? p[(size_t)(s + j) * stride] : zero;
 #pragma unroll
       for (int j = 0; j < 8; ++j) sum += v[j];
+      if (kept) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) keep[j] = v[j];
+      }
     }
   }
   tot[g][qi] = sum;
@@ -73,6 +81,16 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
   if (!active) return;
   f32x4 run = zero;
   for (int gg = 0; gg < g; ++gg) run += tot[gg][qi];
+  if (kept) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < s1) {
+        p[(size_t)(s0 + j) * stride] = run;
+        run += keep[j];
+      }
+    }
+    return;
+  }
   for (int s = s0; s < s1; s += 8) {
     f32x4 v[8];
 #pragma unroll
