@@ -570,12 +570,6 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
       const float* wrow = wh + (size_t)(wok ? wr : 0) * D;
 #pragma unroll
       for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, wok);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          st[i][db][r] = ok ? pre[(size_t)(fbase + crow(r, hh)) * D + db * 32 + l32] : 0.f;
-      zreg[i] = ok ? a.prefixz[((size_t)bh * a.spans + span) * a.M + fbase + l32] : 0.f;
     }
 
     // feature maps of this wave's features for the chunk staged in buf,
@@ -630,13 +624,26 @@ __global__ __launch_bounds__(256, 2) void k_causal2(CausalArgs a) {
       }
     };
 
-    // prologue: chunk 0 into buffer 0 with its V^T, chunk 1 in registers
+    // prologue: chunk 0 into buffer 0 with its V^T, chunk 1 in registers; the
+    // span's prefix state (64 KB per workgroup) is requested after the two
+    // chunks, so that staging chunk 0 does not wait for it
     load_chunk(t0);
     __syncthreads();                                     // previous feature group fully done
-#pragma unroll
-    for (int i = 0; i < FBW; ++i) sZ[i * 32 + l32] = zreg[i];
     store_chunk(smem, min(C, t1 - t0));
     if (t0 + C < t1) load_chunk(t0 + C);
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) {
+      const bool ok = fb0 + i < nfb;
+      const int fbase = (ok ? fb0 + i : 0) * 32;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st[i][db][r] = ok ? pre[(size_t)(fbase + crow(r, hh)) * D + db * 32 + l32] : 0.f;
+      zreg[i] = ok ? a.prefixz[((size_t)bh * a.spans + span) * a.M + fbase + l32] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) sZ[i * 32 + l32] = zreg[i];
     wait_lgkm0();
     raw_barrier();
     transpose_v(smem);
