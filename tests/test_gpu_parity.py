@@ -118,6 +118,27 @@ def test_noncausal_encoder_full_size_sampled(gpu):
     assert worst <= TOL["bf16"]
 
 
+def test_noncausal_long_full_size_sampled(gpu):
+    """The non-causal half of the long workload (B=1, H=8, L=65536, d=64,
+    m=256, bf16) in the benchmark's launch configuration; every head is
+    checked on sampled rows, the first and last included."""
+    import torch
+    wl = synth.WORKLOADS["long"]
+    x = synth.make_inputs(wl, with64=False)
+    q, k, v = (to_device(x[n], "bf16") for n in ("q", "k", "v"))
+    o = gpu.attn(q, k, v, torch.from_numpy(x["w"]).cuda(), causal=False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    worst = 0.0
+    for h in range(wl.H):
+        rows = np.unique(np.concatenate([[0, 511, 512, wl.L - 1], rng.choice(wl.L, 28, replace=False)]))
+        q64, k64, v64 = (synth.as_f64(x[n][0, h], "bf16") for n in ("q", "k", "v"))
+        ref = oracle.attn_rows(q64, k64, v64, x["w64"][h], rows)
+        got = o[0, h, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+        worst = max(worst, row_rel_err(got, ref))
+    assert worst <= TOL["bf16"]
+
+
 def test_noncausal_deterministic(gpu):
     import torch
     x = synth.random_case(9, 1, 4, 2048, 64, 256, "bf16")
@@ -204,6 +225,31 @@ def test_causal_full_size_sampled(gpu, name):
         got = o[b, h, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
         worst = max(worst, row_rel_err(got, ref))
     assert worst <= TOL["bf16"]
+
+
+def test_causal_wide_full_size_sampled(gpu):
+    """The float32 wide-state workload (B=2, H=32, L=32768, d=128, m=512,
+    causal) at full size; eight heads spread over both batches are checked on
+    sampled rows (first, chunk and span edges, last, random) to the float32
+    tolerance."""
+    import torch
+    wl = synth.WORKLOADS["wide"]
+    x = synth.make_inputs(wl, with64=False)
+    q, k, v = (to_device(x[n], "f32") for n in ("q", "k", "v"))
+    o = gpu.attn(q, k, v, torch.from_numpy(x["w"]).cuda(), causal=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    rng = np.random.default_rng(3)
+    fixed = np.array([0, 1, 31, 32, 33, 255, 256, 1023, 1024, wl.L - 1])
+    worst = 0.0
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    for b, h in heads[:: len(heads) // 8]:
+        rows = np.unique(np.concatenate([fixed, rng.choice(wl.L, 10, replace=False)]))
+        q64, k64, v64 = (np.asarray(x[n][b, h], dtype=np.float64) for n in ("q", "k", "v"))
+        ref = oracle.attn_rows(q64, k64, v64, x["w64"][h], rows, causal=True)
+        got = o[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        worst = max(worst, row_rel_err(got, ref))
+    assert worst <= TOL["f32"]
 
 
 # ---------------------------------------------------------------------------
