@@ -257,7 +257,11 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the default warmup (about 20 ms of back-to-back steps) outlasts the
+    # shader clock's settling after a burst of work begins: a few ms in, the
+    # clock falls from about 2.0 to about 1.5 GHz and climbs back over the
+    # next ~10 ms, so a short warmup puts that dip into the timed steps
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default="long", choices=["t1", "encoder", "causal_lm", "long", "wide"])
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time budget per path (0 = skip)")
     ap.add_argument("--paths", default="", help="comma-separated subset of the workload's paths to run "
