@@ -283,8 +283,9 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return 0
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is described "
-              "in DESIGN.md and not run here", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): heads are independent, so several "
+              "GPUs would each run this library on their own heads; nothing here runs on more than one",
+              file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py is a single-process benchmark; do not launch it with several ranks", file=sys.stderr)

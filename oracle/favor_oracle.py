@@ -21,7 +21,7 @@ omega_i, and every function takes the values actually handed to the device,
 upcast to float64.  No stabiliser, no 1/sqrt(d) temperature and no rescaling
 of eps are applied: the caller pre-scales Q and K if it wants a temperature.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
 * causal denominator = phi(q_i) . sum_{j<=i} phi(k_j) + eps, by analogy with
   the non-causal denominator (P2 key points; P1 In[25]);
 * the causal sum includes the diagonal j = i (P2 案例 2 says j <= i);

@@ -1,6 +1,6 @@
 """Measure HBM traffic per kernel launch with rocprofv3 counters for bench.py.
 
-    python traffic.py [--workload long] [--out gpurun_out/traffic]
+    python traffic.py [--workload long] [--out DIR]   (DIR defaults to counter_runs/)
     python traffic.py --workload long --resummarise STAMP   (re-read the runs of STAMP)
 
 Every counter is collected in a rocprofv3 run of its own (FETCH_SIZE, then
@@ -71,7 +71,8 @@ def run_pass(counter: str, out_dir: str, prog: list, run: bool = True) -> tuple:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="long", choices=list(synth.WORKLOADS))
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "traffic"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "counter_runs"),
+                    help="folder for the raw rocprofv3 runs and a copy of the summaries")
     ap.add_argument("--resummarise", metavar="STAMP", default=None,
                     help="rebuild the summary from the runs an earlier call left under --out")
     args = ap.parse_args()
@@ -137,7 +138,10 @@ def main() -> int:
             continue
         lines.append(f"{key[len(wl.name) + 1:]:32s} {v['fetch_bytes'] / 1e6:10.2f} {v['write_bytes'] / 1e6:10.2f} "
                      f"{v['bytes_per_launch'] / 1e6:10.2f}")
-    lines += ["", "made by: python3 traffic.py --workload {} ($REPO = the repository root), which runs,".format(wl.name),
+    out_arg = "" if os.path.abspath(args.out) == os.path.join(ROOT, "counter_runs") else \
+        " --out " + os.path.relpath(os.path.abspath(args.out), ROOT)
+    lines += ["", "made by: python3 traffic.py --workload {}{} ($REPO = the repository root), which runs,".format(
+        wl.name, out_arg),
               "from /tmp with TMPDIR=/tmp:"] + ["  " + c for c in commands]
     txt = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl.name}.txt")
     with open(txt, "w") as f:
