@@ -186,6 +186,14 @@ def test_causal_parity(gpu, dtype, d, m, B, H, L):
     assert row_rel_err(out, _ref(x, True)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 64, 256), ("bf16", 32, 96), ("f32", 64, 128), ("bf16", 128, 256)])
+def test_causal_shared_projection(gpu, dtype, d, m):
+    """One W for every head (Hw = 1), several batches and heads, both scans."""
+    x = synth.random_case(8 + d + m, 2, 3, 700, d, m, dtype, heads_w=1)
+    out = _run_attn(gpu, x, dtype, causal=True)
+    assert row_rel_err(out, _ref(x, True)) <= TOL[dtype]
+
+
 def test_causal_deterministic(gpu):
     """The causal path adds in a fixed order (span scan, chunk walk, cross-wave
     sums): repeated calls give identical bits."""
