@@ -122,10 +122,16 @@ struct CausalArgs {
 };
 
 // LDS layout (bytes), computed identically on host and device.
+// Tokens per chunk of the generic scan: 64, or 32 for float32 rows of 128
+// (the per-wave numerators and feature fragments of a 64-token chunk would
+// not fit the register file next to the float32 operands of d = 128).
+template <class Tr, int D>
+constexpr int generic_chunk() { return D == 128 ? 32 : 64; }
+
 template <class Tr, int D, int FBW>
 struct CausalLds {
   using E = typename Tr::elem;
-  static constexpr int C = 64;                                  // tokens per chunk
+  static constexpr int C = generic_chunk<Tr, D>();              // tokens per chunk
   static constexpr int RS = Rows<D, sizeof(E)>::RS;             // Q, K, V rows
   static constexpr int FW = 32 * FBW;                           // features per wave
   static constexpr int RSF = FW * (int)sizeof(E) + 16;          // phi(K) rows
@@ -145,6 +151,7 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
   using F = typename Tr::frag;
   using LY = CausalLds<Tr, D, FBW>;
   constexpr int C = LY::C;
+  constexpr int NTB = C / 32;                 // 32-token blocks per chunk
   constexpr int NKD = D / Tr::KS;
   constexpr int NDB = D / 32;
   constexpr int NKT = 32 / Tr::KS;            // k-steps per 32-token block
@@ -222,9 +229,9 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
       }
 
       // ---- feature maps of this wave's features, lane = token -------------
-      F pq[FBW][2][NKT], pk[FBW][2][NKT];
+      F pq[FBW][NTB][NKT], pk[FBW][NTB][NKT];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+      for (int tb = 0; tb < NTB; ++tb) {
         F qf[NKD], kf[NKD];
 #pragma unroll
         for (int s = 0; s < NKD; ++s) {
@@ -277,10 +284,10 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
         }
       }
 
-      f32x16 nacc[NDB][2];
-      float dacc[2];
+      f32x16 nacc[NDB][NTB];
+      float dacc[NTB];
 #pragma unroll
-      for (int tqb = 0; tqb < 2; ++tqb) {
+      for (int tqb = 0; tqb < NTB; ++tqb) {
         dacc[tqb] = 0.f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) nacc[db][tqb] = zero16();
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
 
       // ---- intra-chunk: A^T[tk][tq] = phi(K) phi(Q)^T over this wave's features
 #pragma unroll
-      for (int tqb = 0; tqb < 2; ++tqb) {
+      for (int tqb = 0; tqb < NTB; ++tqb) {
 #pragma unroll
         for (int tkb = 0; tkb <= tqb; ++tkb) {
           f32x16 at = zero16();
@@ -335,10 +342,10 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
           for (int db = 0; db < NDB; ++db) {
             F sf = CFrag<Tr>::make(st[i][db], s2);           // S^T[d][f] operand
 #pragma unroll
-            for (int tqb = 0; tqb < 2; ++tqb) nacc[db][tqb] = Tr::mma(sf, pq[i][tqb][s2], nacc[db][tqb]);
+            for (int tqb = 0; tqb < NTB; ++tqb) nacc[db][tqb] = Tr::mma(sf, pq[i][tqb][s2], nacc[db][tqb]);
           }
 #pragma unroll
-          for (int tqb = 0; tqb < 2; ++tqb) {
+          for (int tqb = 0; tqb < NTB; ++tqb) {
             if constexpr (Tr::VPS == 8) {
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
       for (int i = 0; i < FBW; ++i) {
         float zc = 0.f;
 #pragma unroll
-        for (int tkb = 0; tkb < 2; ++tkb)
+        for (int tkb = 0; tkb < NTB; ++tkb)
 #pragma unroll
           for (int s2 = 0; s2 < NKT; ++s2) {
             F kt = col_frag<Tr, RSF>(sPhi, tkb * 32, i * 32, s2, lane);    // phi(K)^T[f][t]
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
       // ---- sum the four waves' contributions -------------------------------
       __syncthreads();                                   // staging area is free
 #pragma unroll
-      for (int tqb = 0; tqb < 2; ++tqb) {
+      for (int tqb = 0; tqb < NTB; ++tqb) {
         float* rrow = sRed + (size_t)w * C * (RSR / 4) + (tqb * 32 + l32) * (RSR / 4);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -400,8 +407,9 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
       }
       __syncthreads();
       {
-        constexpr int DP = D / 4;                        // outputs per thread
-        const int tq = tid >> 2, d0 = (tid & 3) * DP;
+        constexpr int TPR = 256 / C;                     // threads per output row
+        constexpr int DP = D / TPR;                      // outputs per thread
+        const int tq = tid / TPR, d0 = (tid % TPR) * DP;
         float acc[DP];
 #pragma unroll
         for (int j = 0; j < DP; ++j) acc[j] = 0.f;
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
             if (fg + 1 < a.fgroups) {
 #pragma unroll
               for (int j = 0; j < DP; ++j) a.num[hoff + oi + j] = acc[j];
-              if ((tid & 3) == 0) a.den[(size_t)bh * a.L + tok] = dsum;
+              if ((tid % TPR) == 0) a.den[(size_t)bh * a.L + tok] = dsum;
             }
           }
           if (fg + 1 == a.fgroups) {
