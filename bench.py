@@ -46,10 +46,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def causal_chunk(wl) -> int:
-    """Tokens per chunk of the causal scan: the bf16 kernel for d <= 64 and the
-    generic kernel at d = 128 carry the state every 32 tokens (their registers
-    hold a 32-token chunk), the generic kernel at d = 32 or 64 every 64."""
-    return 32 if (wl.dtype == "bf16" and wl.d <= 64) or wl.d == 128 else 64
+    """Tokens per chunk of the causal scan: both scans carry the state every
+    32 tokens (their registers hold a 32-token chunk)."""
+    return 32
 
 
 def log(msg: str) -> None:

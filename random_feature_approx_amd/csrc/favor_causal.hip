@@ -122,11 +122,12 @@ struct CausalArgs {
 };
 
 // LDS layout (bytes), computed identically on host and device.
-// Tokens per chunk of the generic scan: 64, or 32 for float32 rows of 128
-// (the per-wave numerators and feature fragments of a 64-token chunk would
-// not fit the register file next to the float32 operands of d = 128).
+// Tokens per chunk of the generic scan.  32: the per-wave numerators
+// (NDB x chunk/32 accumulator tiles) and feature fragments of a 64-token
+// chunk spill at d = 128 and hold more registers than needed at d <= 64;
+// 32-token chunks measured faster at every d.
 template <class Tr, int D>
-constexpr int generic_chunk() { return D == 128 ? 32 : 64; }
+constexpr int generic_chunk() { return 32; }
 
 template <class Tr, int D, int FBW>
 struct CausalLds {
