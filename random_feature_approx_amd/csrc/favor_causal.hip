@@ -146,8 +146,15 @@ struct CausalLds {
   static constexpr int kTotal = kZ + 4 * FW * 4;
 };
 
+// Workgroups per compute unit the generic scan is compiled for: two for
+// float32 d <= 64 (at most 256 registers; the d = 64 build then keeps 18
+// spilled values outside the chunk loop, and ran 13% faster than at one),
+// one otherwise.
+template <class Tr, int D>
+constexpr int generic_wgs() { return (sizeof(typename Tr::elem) == 4 && D <= 64) ? 2 : 1; }
+
 template <class Tr, int D, int FBW, int FM>
-__global__ __launch_bounds__(256) void k_causal(CausalArgs a) {
+__global__ __launch_bounds__(256, (generic_wgs<Tr, D>())) void k_causal(CausalArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
   using LY = CausalLds<Tr, D, FBW>;
