@@ -3,6 +3,7 @@
 #include "favor_internal.hpp"
 
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace favor {
 
@@ -51,6 +52,8 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.rfbw = 1;   // two blocks per wave (4 waves) measured slower: fewer waves to hide latency
   p.rnw = (dt == FAVOR_F32 && d == 128) ? 4 : 8;
   p.rfgroups = (nfb + p.rnw * p.rfbw - 1) / (p.rnw * p.rfbw);
+  // the causal scan for bf16 FAVOR+ with d <= 64 and m = 256 (k_causal3)
+  p.scan3 = (causal && dt == FAVOR_BF16 && fmap == FAVOR_FMAP_POSITIVE && p.mt == 256 && (d == 32 || d == 64)) ? 1 : 0;
   const int target = 2 * num_cus;
   // non-causal: reduction workgroups = BH * splits * rfgroups; causal: the
   // chunk scan runs one workgroup per (span, head) and walks feature groups
@@ -60,6 +63,16 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   // run as a second, mostly empty round
   int splits = target / per_head;
   const int max_splits = (L + 255) / 256;
+  // the causal backward keeps two span workgroups per compute unit
+  int bwd_splits = (2 * num_cus) / per_head;
+  // FAVOR_SPANS (testing and tuning): the number of causal spans per head
+  if (causal) {
+    const char* env = getenv("FAVOR_SPANS");
+    const int forced = env ? atoi(env) : 0;
+    if (forced > 0) splits = bwd_splits = forced;
+  }
+  if (bwd_splits > max_splits) bwd_splits = max_splits;
+  if (bwd_splits < 1) bwd_splits = 1;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int len = (L + splits - 1) / splits;
@@ -112,8 +125,10 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   // of the forward's chunk scan
   p.bfgroups = (nfb + 3) / 4;
   if (causal) {
-    p.bsplits = p.splits;
-    p.bsplit_len = p.split_len;
+    int bl = (L + bwd_splits - 1) / bwd_splits;
+    bl = (bl + 63) / 64 * 64;
+    p.bsplit_len = bl;
+    p.bsplits = (L + bl - 1) / bl;
   } else {
     const int per = p.BH * p.bfgroups;
     int bs = (target + per - 1) / per;

@@ -912,6 +912,7 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   timing_end(FAVOR_KERNEL_SPAN_SCAN, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.scan3) return launch_causal3(p, t, s);
   switch (p.fmap) {
     case FM_POS: return causal_fmap<FM_POS>(p, t, s);
     case FM_ELU1: return causal_fmap<FM_ELU1>(p, t, s);

@@ -27,6 +27,7 @@ struct Plan {
   int rfbw;             // 32-feature blocks per reduction wave
   int rfgroups;         // reduction feature groups per head (workgroups sharing K, V tiles)
   // causal chunk scan
+  int scan3;            // the pipelined one-workgroup-per-CU scan (bf16, d <= 64, m = 256, FAVOR+)
   int fgroups;          // feature groups walked in turn by one workgroup
   int fbw;              // 32-feature blocks per wave
   // Q-side apply (non-causal)
@@ -79,6 +80,7 @@ void timing_end(favor_kernel k, hipStream_t s);
 hipError_t launch_features(const Plan& p, const void* x, const float* w, float* phi, hipStream_t s);
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_causal3(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t gather_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int width, int n,
                        hipStream_t s);
 hipError_t scatter_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int n, int srow,
