@@ -30,13 +30,20 @@
  *    in blocks of 32 features; for m not a multiple of 32 the missing
  *    features are padding whose key-side features are set to exactly 0, so
  *    they add nothing to any sum; the backward entry points need m a
- *    multiple of 32); L >= 1; B, H >= 1; B*H*L*max(d,m) < 2^31.
+ *    multiple of 32); L >= 1; B, H >= 1; B*H <= 65534 and
+ *    L*max(d,m) < 2^30 (offsets between heads are 64-bit, offsets inside
+ *    one head 32-bit); otherwise FAVOR_ERR_SHAPE.
  *  - stream is a hipStream_t passed as void* (NULL = default stream).  Calls
  *    only enqueue work; results are valid once the stream has been
  *    synchronised.
  *  - Errors are returned, never thrown.  Arguments are validated before
  *    anything is enqueued: a non-OK return means nothing was launched, except
- *    FAVOR_ERR_HIP, which reports a launch failure (hipGetLastError).
+ *    FAVOR_ERR_HIP, which reports a launch failure (hipGetLastError), and
+ *    FAVOR_ERR_INTERNAL, which reports a disagreement between the call's
+ *    work split and the compiled kernels (a library bug).  Entry points that
+ *    launch kernels first clear the calling thread's pending HIP error
+ *    (hipGetLastError), so that the status reflects their own launches only:
+ *    a caller who needs an earlier error must read it before the call.
  *    Pointer values other than NULL cannot be checked on the host.
  *  - Calls are thread-safe as long as concurrent calls use distinct
  *    workspaces.
@@ -106,10 +113,12 @@ favor_status favor_attn_noncausal(const void* Q, const void* K, const void* V,
  * phi(k_j) v_j^T and z_i = sum_{j<=i} phi(k_j) (the diagonal included),
  * o_i = phi(q_i)^T S_i / (phi(q_i)^T z_i + eps).  The denominator is the
  * causal analogue of the non-causal one (the notes give the numerator
- * only).  Computed in chunks (32 tokens for bf16 with d <= 64, 64
- * otherwise): inside a chunk the masked chunk-by-chunk score tile is
- * multiplied by V; across chunks the m x d state is carried as a prefix
- * sum.  Deterministic as above.
+ * only).  Computed in chunks of 32 tokens by every scan (a chunk length C
+ * of 64 is the same computation carried as two 32-token steps, identical
+ * up to rounding order): inside a chunk the masked chunk-by-chunk score
+ * tile is multiplied by V; across chunks the m x d state is carried as a
+ * prefix sum, across spans of the sequence by an exclusive scan of the
+ * spans' states.  Deterministic as above.
  */
 favor_status favor_attn_causal(const void* Q, const void* K, const void* V,
                                const float* W, int Hw, void* O,
@@ -194,6 +203,7 @@ favor_status favor_attn(const void* Q, const void* K, const void* V,
                         const float* W, int Hw, void* O,
                         int B, int H, int L, int d, int m, float eps, int causal,
                         favor_dtype dtype, void* ws, size_t ws_bytes, void* stream);
+
 
 /*
  * Backward pass of non-causal attention: the gradients dQ, dK, dV of

@@ -131,6 +131,27 @@ def _check_device(*ts):
             raise ValueError("FAVOR+ tensors must be contiguous")
 
 
+def _check_out(out, shape, dtype, device):
+    """A caller-supplied output must match exactly: the kernels write every
+    element of the expected shape through its pointer."""
+    if not out.is_cuda or out.device != device:
+        raise ValueError(f"out must live on {device}")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.dtype != dtype:
+        raise TypeError(f"out must have dtype {dtype}, got {out.dtype}")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+
+
+def _check_workspace(ws, device):
+    torch = _torch()
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError(f"workspace must live on {device}")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+
+
 def _proj(w, H, m_d):
     """Return (w, Hw) with w float32 [Hw, m, d] contiguous on the device."""
     torch = _torch()
@@ -140,6 +161,8 @@ def _proj(w, H, m_d):
         w = w.unsqueeze(0)
     if w.dim() != 3 or tuple(w.shape[1:]) != m_d or w.shape[0] not in (1, H):
         raise ValueError(f"W must be [m, d] or [H, m, d], got {tuple(w.shape)}")
+    if not w.is_cuda:
+        raise ValueError("the projection W must live on a HIP device (no CPU path)")
     return w.contiguous(), int(w.shape[0])
 
 
@@ -169,6 +192,8 @@ def features(x, w, fmap: str = "positive"):
     w, hw = _proj(w, H, (w.shape[-2], d))
     m = int(w.shape[1])
     _check_device(x, w)
+    if w.device != x.device:
+        raise ValueError("x and W must live on one device")
     code = _fmap_code(fmap)
     phi = torch.empty((B, H, L, 2 * m if fmap == "trig" else m), dtype=torch.float32, device=x.device)
     st = lib.favor_features_fmap(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), hw,
@@ -191,13 +216,20 @@ def attn(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, workspac
     w, hw = _proj(w, H, (w.shape[-2], d))
     m = int(w.shape[1])
     _check_device(q, k, v, w)
+    if k.device != q.device or v.device != q.device or w.device != q.device:
+        raise ValueError("q, k, v and W must live on one device")
     code = _dtype_code(q)
-    o = torch.empty_like(q) if out is None else out
-    _check_device(o)
+    if out is None:
+        o = torch.empty_like(q)
+    else:
+        _check_out(out, q.shape, q.dtype, q.device)
+        o = out
     fcode = _fmap_code(fmap)
     need = int(lib.favor_workspace_bytes_fmap(B, H, L, d, m, int(bool(causal)), fcode, code))
     if need == 0:
         raise FavorError("favor_workspace_bytes_fmap", 2)
+    if workspace is not None:
+        _check_workspace(workspace, q.device)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ptrs = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
@@ -234,16 +266,22 @@ def attn_strided(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, 
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
     for t in (q, k, v):
-        if not t.is_cuda or t.stride(3) != 1:
-            raise ValueError("tensors must live on a HIP device with a contiguous last dimension")
+        if not t.is_cuda or t.stride(3) != 1 or t.device != q.device:
+            raise ValueError("tensors must live on one HIP device with a contiguous last dimension")
     B, H, L, d = q.shape
     dv = int(v.shape[3])
     w, hw = _proj(w, H, (w.shape[-2], d))
+    if w.device != q.device:
+        raise ValueError("W must live on the device of q")
     m = int(w.shape[1])
     code, fcode = _dtype_code(q), _fmap_code(fmap)
     o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device) if out is None else out
+    if not o.is_cuda or o.device != q.device:
+        raise ValueError(f"out must live on {q.device}")
     if o.shape != (B, H, L, dv) or o.stride(3) != 1 or o.dtype != q.dtype:
         raise ValueError("out must be a [B, H, L, dv] view of the input dtype with a contiguous last dimension")
+    if any(st < 0 for st in o.stride()):
+        raise ValueError("out must have non-negative strides")
     need = int(lib.favor_workspace_bytes_strided(B, H, L, d, dv, m, int(bool(causal)), fcode, code))
     if need == 0:
         raise FavorError("favor_workspace_bytes_strided", 2)
@@ -283,7 +321,13 @@ def softmax_attn(q, k, v, scale=None, causal: bool = False, out=None):
         raise TypeError("q, k, v must share one dtype")
     B, H, L, d = q.shape
     _check_device(q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must live on one device")
+    if out is None:
+        o = torch.empty_like(q)
+    else:
+        _check_out(out, q.shape, q.dtype, q.device)
+        o = out
     sc = float(d) ** -0.5 if scale is None else float(scale)
     st = lib.favor_softmax_attn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                                 ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()), B, H, L, d, sc,
@@ -311,10 +355,14 @@ def attn_backward(q, k, v, w, g, causal: bool = False, eps: float = 1e-6, worksp
     w, hw = _proj(w, H, (w.shape[-2], d))
     m = int(w.shape[1])
     _check_device(q, k, v, g, w)
+    if any(t.device != q.device for t in (k, v, g, w)):
+        raise ValueError("q, k, v, g and W must live on one device")
     code = _dtype_code(q)
     need = int(lib.favor_bwd_workspace_bytes(B, H, L, d, m, int(bool(causal)), code))
     if need == 0:
         raise FavorError("favor_bwd_workspace_bytes", 2)
+    if workspace is not None:
+        _check_workspace(workspace, q.device)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)

@@ -20,16 +20,31 @@ int device_cu_count() {
   return n;
 }
 
+// Size limits: every offset between heads is 64-bit; offsets inside one head
+// are 32-bit byte offsets, so L * max(d, m) must stay below 2^30 (a head's
+// float32 features fit 4 GiB); B * H is a grid dimension (plus one slice for
+// the projection operand), at most 65535.
 static favor_status check_shapes(int B, int H, int L, int d, int m, int Hw, favor_dtype dt) {
   if (B < 1 || H < 1 || L < 1) return FAVOR_ERR_SHAPE;
   if (Hw != 1 && Hw != H) return FAVOR_ERR_SHAPE;
   if (dt != FAVOR_F32 && dt != FAVOR_BF16) return FAVOR_ERR_UNSUPPORTED;
   if (d != 32 && d != 64 && d != 128) return FAVOR_ERR_UNSUPPORTED;
   if (m < 1 || m > 512) return FAVOR_ERR_UNSUPPORTED;
-  const int64_t big = (int64_t)B * H * L * (d > m ? d : m);
-  if (big >= ((int64_t)1 << 31)) return FAVOR_ERR_SHAPE;
+  if ((int64_t)L * (d > m ? d : m) >= ((int64_t)1 << 30)) return FAVOR_ERR_SHAPE;
+  if ((int64_t)B * H > 65534) return FAVOR_ERR_SHAPE;
   return FAVOR_OK;
 }
+
+// Status of a launch sequence.  A pending HIP error left by the caller's own
+// work is cleared before launching (see favor.h), so hipGetLastError after
+// the launches reports this call's launches only.
+static favor_status launch_status(hipError_t e) {
+  if (e == hipSuccess) return FAVOR_OK;
+  if (e == hipErrorNotSupported) return FAVOR_ERR_UNSUPPORTED;
+  if (e == kErrPlan) return FAVOR_ERR_INTERNAL;
+  return FAVOR_ERR_HIP;
+}
+static void clear_pending_error() { (void)hipGetLastError(); }
 
 bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, favor_dtype dt, int num_cus,
                int fmap) {
@@ -43,7 +58,8 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.BH = B * H;
   p.esize = dt == FAVOR_BF16 ? 2 : 4;
   // reduction split: about two workgroups per compute unit, ranges of at
-  // least 256 tokens, whole 64-token chunks.
+  // least 256 tokens, whole 64-token tiles (two 32-token chunks of the
+  // causal scans).
   // the bf16 scan for d <= 64 (every feature map) owns two feature blocks
   // per wave; the generic scan (bf16 d = 128 and float32) one
   p.fbw = (dt == FAVOR_BF16 && d <= 64) ? 2 : 1;
@@ -243,7 +259,8 @@ favor_status favor_features_fmap(const void* X, const float* W, int Hw, float* P
   if ((int)fmap < FAVOR_FMAP_POSITIVE || (int)fmap > FAVOR_FMAP_TRIG) return FAVOR_ERR_UNSUPPORTED;
   Plan p;
   if (!make_plan(p, B, H, L, d, m, Hw, 0, dtype, device_cu_count(), (int)fmap)) return FAVOR_ERR_HIP;
-  return launch_features(p, X, W, Phi, (hipStream_t)stream) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  clear_pending_error();
+  return launch_status(launch_features(p, X, W, Phi, (hipStream_t)stream));
 }
 
 favor_status favor_features(const void* X, const float* W, int Hw, float* Phi, int B, int H, int L, int d, int m,
@@ -262,9 +279,8 @@ static favor_status attn_common(const void* Q, const void* K, const void* V, con
   if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count(), fmap)) return FAVOR_ERR_HIP;
   if (!ws || ws_bytes < p.total || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
   Tensors t{Q, K, V, W, O, eps, (char*)ws};
-  hipError_t e = causal ? launch_causal(p, t, (hipStream_t)stream) : launch_noncausal(p, t, (hipStream_t)stream);
-  if (e == hipErrorNotSupported) return FAVOR_ERR_UNSUPPORTED;
-  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  clear_pending_error();
+  return launch_status(causal ? launch_causal(p, t, (hipStream_t)stream) : launch_noncausal(p, t, (hipStream_t)stream));
 }
 
 favor_status favor_attn_noncausal(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
@@ -328,6 +344,7 @@ favor_status favor_attn_strided(const void* Q, const long long* q_strides, const
   const size_t inner = align256(p.total), ex = strided_extra(p);
   if (!ws || ws_bytes < inner + 4 * ex || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  clear_pending_error();
   char* base = (char*)ws;
   char* qc = base + inner;
   char* kc = qc + ex;
@@ -360,8 +377,7 @@ favor_status favor_attn_strided(const void* Q, const long long* q_strides, const
     e = causal ? launch_causal(p, t, s) : launch_noncausal(p, t, s);
     if (e == hipSuccess && !ocont) e = scatter_rows(oc, O, p, o_strides, c0, dv - c0 < dk ? dv - c0 : dk, dk, s);
   }
-  if (e == hipErrorNotSupported) return FAVOR_ERR_UNSUPPORTED;
-  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  return launch_status(e);
 }
 
 favor_status favor_draw_projection(unsigned long long seed, int Hw, int m, int d, int orthogonal, float scale,
@@ -369,8 +385,8 @@ favor_status favor_draw_projection(unsigned long long seed, int Hw, int m, int d
   if (!W) return FAVOR_ERR_NULL;
   if (Hw < 1 || m < 1 || m > 65536 || d < 1 || d > 128) return FAVOR_ERR_SHAPE;
   if ((int64_t)Hw * m * d >= ((int64_t)1 << 31)) return FAVOR_ERR_SHAPE;
-  return launch_draw(seed, Hw, m, d, orthogonal ? 1 : 0, scale, W, (hipStream_t)stream) == hipSuccess ? FAVOR_OK
-                                                                                                     : FAVOR_ERR_HIP;
+  clear_pending_error();
+  return launch_status(launch_draw(seed, Hw, m, d, orthogonal ? 1 : 0, scale, W, (hipStream_t)stream));
 }
 
 favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, void* O, int B, int H, int L, int d,
@@ -381,8 +397,8 @@ favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, voi
   Plan p{};
   p.B = B; p.H = H; p.L = L; p.D = d; p.BH = B * H; p.dt = dtype;
   p.esize = dtype == FAVOR_BF16 ? 2 : 4;
-  return launch_softmax(p, Q, K, V, O, scale, causal ? 1 : 0, (hipStream_t)stream) == hipSuccess ? FAVOR_OK
-                                                                                                   : FAVOR_ERR_HIP;
+  clear_pending_error();
+  return launch_status(launch_softmax(p, Q, K, V, O, scale, causal ? 1 : 0, (hipStream_t)stream));
 }
 
 static favor_status bwd_common(const void* Q, const void* K, const void* V, const float* W, int Hw, const void* dO,
@@ -396,8 +412,8 @@ static favor_status bwd_common(const void* Q, const void* K, const void* V, cons
   if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count())) return FAVOR_ERR_HIP;
   if (!ws || ws_bytes < p.btotal || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;
   BwdTensors t{Q, K, V, W, dO, dQ, dK, dV, eps, (char*)ws};
-  const hipError_t e = causal ? launch_causal_bwd(p, t, (hipStream_t)stream) : launch_noncausal_bwd(p, t, (hipStream_t)stream);
-  return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  clear_pending_error();
+  return launch_status(causal ? launch_causal_bwd(p, t, (hipStream_t)stream) : launch_noncausal_bwd(p, t, (hipStream_t)stream));
 }
 
 favor_status favor_attn_noncausal_bwd(const void* Q, const void* K, const void* V, const float* W, int Hw,

@@ -834,7 +834,7 @@ hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t 
       case 128: return bwd_noncausal_t<TrF32, 128>(p, t, s);
     }
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 // ===========================================================================
@@ -1455,7 +1455,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   const dim3 sgrid((nq + 255) / 256, p.BH);
   const size_t clds = BCLds<Tr, D>::kTotal;
   const int fgroups = (p.M / 32 + 3) / 4;
-  if (fgroups > 1 && p.boff_acc == p.btotal) return hipErrorInvalidValue;   // no room for the sums
+  if (fgroups > 1 && p.boff_acc == p.btotal) return kErrPlan;   // no room for the sums
   BCausalArgs ca{t.q, t.k, t.v, t.g, b.wph, b.wpl, b.wt, b.wtl, b.part, b.partz, b.lg, b.cw, b.lg, b.cw,
                  t.dq, nullptr, b.acc, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, fgroups, t.eps};
   // span aggregates of phi(K) V^T, phi(K) -> exclusive prefixes
@@ -1506,7 +1506,7 @@ hipError_t launch_causal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s) 
       case 128: return bwd_causal_t<TrF32, 128>(p, t, s);
     }
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 }  // namespace favor

@@ -4,13 +4,14 @@
 // z_i = sum_{j<=i} phi(k_j)   (prefix-sum form of the study notes' case 2;
 // the denominator is its analogue of the non-causal normaliser).
 //
-// L is cut into spans (one workgroup each) and spans into chunks of tokens
-// (32 in the bf16 scan for d <= 64, 64 in the generic scan).
+// L is cut into spans (one workgroup each) and spans into chunks
+// of 32 tokens in every scan (a chunk of 64 is carried as two 32-token steps).
 //   1. k_reduce (shared with the non-causal path) computes every span's
 //      aggregate [sum phi(k) v^T | sum phi(k)] in float32.
 //   2. k_span_scan turns the aggregates into exclusive prefixes in place, in
 //      a fixed order of additions (deterministic).
-//   3. k_causal2 (bf16, d <= 64) or k_causal walks the chunks of a span
+//   3. k_causal3 (bf16 FAVOR+, d <= 64, m = 256), k_causal2 (other bf16,
+//      d <= 64) or k_causal walks the chunks of a span
 //      starting from its prefix.  For a
 //      chunk c with queries Q_c, keys K_c and values V_c:
 //        num = tril(phi(Q_c) phi(K_c)^T) V_c + phi(Q_c) S      (masked tile
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(256, (generic_wgs<Tr, D>())) void k_causal(CausalAr
 }
 
 // ---------------------------------------------------------------------------
-// bf16 chunked scan for d <= 64, chunks of C = 32 or 64 tokens.  Same split
+// bf16 chunked scan for d <= 64, chunks of C = 32 tokens.  Same split
 // of the features over four waves as k_causal, with every operand read as a
 // 16-byte fragment and few enough live registers for two workgroups per
 // compute unit at C = 32:
@@ -842,7 +843,7 @@ static hipError_t causal_t(const Plan& p, const Tensors& t, hipStream_t s) {
   using LY = CausalLds<Tr, D, FBW>;
   float* part = (float*)(t.ws + p.off_part);
   float* partz = (float*)(t.ws + p.off_partz);
-  if (p.fbw != FBW) return hipErrorInvalidValue;
+  if (p.fbw != FBW) return kErrPlan;
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
                p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw, p.mt};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
@@ -883,7 +884,7 @@ static hipError_t causal_fmap(const Plan& p, const Tensors& t, hipStream_t s) {
       case 128: return causal_t<TrF32, 128, 1, FM>(p, t, s);
     }
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 template <int D, int FBW, int C, bool FULL, int FM, bool RAG>
@@ -891,7 +892,7 @@ static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
   using LY = CausalLds2<D, C>;
   float* part = (float*)(t.ws + p.off_part);
   float* partz = (float*)(t.ws + p.off_partz);
-  if (p.fbw != FBW) return hipErrorInvalidValue;
+  if (p.fbw != FBW) return kErrPlan;
   CausalArgs a{t.q, t.k, t.v, t.w, t.o, part, partz, (float*)(t.ws + p.off_num), (float*)(t.ws + p.off_den),
                p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.fgroups, t.eps, p.Mw, p.mt};
   timing_begin(FAVOR_KERNEL_CAUSAL, s);
@@ -918,7 +919,7 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
     case FM_ELU1: return causal_fmap<FM_ELU1>(p, t, s);
     case FM_RELU: return causal_fmap<FM_RELU>(p, t, s);
     case FM_TRIG: return causal_fmap<FM_TRIG>(p, t, s);
-    default: return hipErrorInvalidValue;
+    default: return kErrPlan;
   }
 }
 

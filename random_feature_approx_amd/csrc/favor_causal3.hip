@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
 }
 
 hipError_t launch_causal3(const Plan& p, const Tensors& t, hipStream_t s) {
-  if (!p.scan3 || p.M != 256 || p.fgroups != 1 || (p.D != 64 && p.D != 32)) return hipErrorInvalidValue;
+  if (!p.scan3 || p.M != 256 || p.fgroups != 1 || (p.D != 64 && p.D != 32)) return kErrPlan;
   float* part = (float*)(t.ws + p.off_part);
   float* partz = (float*)(t.ws + p.off_partz);
   Causal3Args a{t.q, t.k, t.v, t.w, t.o, part, partz, p.L, p.H, p.Hw, p.splits, p.split_len, t.eps};

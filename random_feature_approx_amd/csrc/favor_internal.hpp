@@ -8,6 +8,11 @@
 
 namespace favor {
 
+// What a launcher returns when the plan and the compiled kernels disagree (a
+// library bug, reported as FAVOR_ERR_INTERNAL).  The launches themselves use
+// plan-computed grids, so a launch reporting this code is a library bug too.
+constexpr hipError_t kErrPlan = hipErrorInvalidConfiguration;
+
 // How one call is split over workgroups, and where its scratch lives inside
 // the caller's workspace.  Computed only from the shapes and the device's
 // compute-unit count, so workspace sizing and the call agree.

@@ -688,6 +688,11 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
       ss = half_sum(ss);
       bias[tb] = FMap<FM>::row_bias(ss, half_ln_m);
     }
+    // LEAN FAVOR+: the accumulator starts at the token's bias through one
+    // float32 32x32x2 product (A = 1/2 in every lane, B = the lane's bias in
+    // both k rows: exactly bias[t] in every row of column t), so the matrix
+    // cores return the base-2 exponent without a per-value add or copy
+    constexpr bool kBiasK = LEAN && FM == FM_POS && Tr::VPS == 8;
 
     f32x16 oacc[TB][NDB];
     float den[TB];
@@ -726,11 +731,14 @@ __global__ __launch_bounds__(NW * 64) void k_apply(ApplyArgs a) {
           // LEAN adds the bias afterwards (the 16 copies would not fit its
           // 128 registers: spilled values reloaded in the group loop wait for
           // every outstanding copy and store)
-          pacc[tb] = LEAN ? zero16() : splat16(bias[tb]);
+          if constexpr (kBiasK) pacc[tb] = __builtin_amdgcn_mfma_f32_32x32x2f32(0.5f, bias[tb], zero16(), 0, 0, 0);
+          else pacc[tb] = LEAN ? zero16() : splat16(bias[tb]);
 #pragma unroll
           for (int s = 0; s < NKD; ++s) pacc[tb] = Tr::pmma(wfr[s], qf[tb][s], pacc[tb]);   // P^T[f][t], lane = t
+          // (LEAN with other feature maps: their bias is 0, no add)
+          constexpr bool kAdd = LEAN && !kBiasK && FM == FM_POS;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) pacc[tb][r] = FMap<FM>::phi(LEAN ? pacc[tb][r] + bias[tb] : pacc[tb][r], cosine, tscale);
+          for (int r = 0; r < 16; ++r) pacc[tb][r] = FMap<FM>::phi(kAdd ? pacc[tb][r] + bias[tb] : pacc[tb][r], cosine, tscale);
         }
         if constexpr (Tr::VPS == 8) {
           // group gi = 2 fb + s2 holds 16 features; lane (d, hh) reads 8 of them
@@ -907,7 +915,7 @@ static hipError_t with_fmap(int fmap, Fn&& f) {
     case FM_RELU: return f.template operator()<FM_RELU>();
     case FM_TRIG: return f.template operator()<FM_TRIG>();
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 template <class Tr, int D>
@@ -936,7 +944,7 @@ hipError_t launch_features(const Plan& p, const void* x, const float* w, float* 
       case 128: return features_t<TrF32, 128>(p, x, w, phi, s);
     }
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 template <class Tr, int D>
@@ -948,7 +956,7 @@ hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const fl
   // slower: half as many waves to hide the latency of each block's chain)
   constexpr int FBW = 1;
   constexpr int NW = (Tr::VPS == 1 && D == 128) ? 4 : 8;
-  if (p.rnw != NW || p.rfbw != FBW) return hipErrorInvalidValue;
+  if (p.rnw != NW || p.rfbw != FBW) return kErrPlan;
   dim3 grid(p.splits, p.rfgroups, p.BH);
   const size_t lds = RedLds<Tr, D, NW * 64>::kTotal;
   return with_fmap(p.fmap, [&]<int FM>() {
@@ -974,7 +982,7 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const floa
       case 128: return launch_reduce_t<TrF32, 128>(p, k, v, w, part, partz, s);
     }
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 template <class Tr, int D, int TB, int NW, bool LEAN>
@@ -997,7 +1005,7 @@ static hipError_t apply_t(const Plan& p, const Tensors& t, const void* wp, const
               (int)stage_off, (int)(stage_off + stage), p.Mw, p.mt};
   const int nblk = (total + p.apply_steps - 1) / p.apply_steps;
   const size_t lds = stage_off + stage + ostage;
-  if (TB * 32 != p.apply_tile || NW != p.apply_nw) return hipErrorInvalidValue;
+  if (TB * 32 != p.apply_tile || NW != p.apply_nw) return kErrPlan;
   return with_fmap(p.fmap, [&]<int FM>() {
     timing_begin(FAVOR_KERNEL_APPLY, s);
     hipLaunchKernelGGL((k_apply<Tr, D, TB, NW, LEAN, FM>), dim3(nblk), dim3(NW * 64), lds, s, a);
@@ -1021,7 +1029,7 @@ static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* wp, 
       case 128: return apply_t<TrF32, 128, 1, 8, false>(p, t, wp, mstate, zstate, s);
     }
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {

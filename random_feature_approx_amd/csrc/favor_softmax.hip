@@ -188,7 +188,7 @@ hipError_t launch_softmax(const Plan& p, const void* q, const void* k, const voi
       case 128: return softmax_t<TrF32, 128>(p, q, k, v, o, scale, causal, s);
     }
   }
-  return hipErrorInvalidValue;
+  return kErrPlan;
 }
 
 }  // namespace favor

@@ -55,7 +55,10 @@ def _nc(lib, q=1, k=1, v=1, w=1, hw=1, o=1, B=1, H=1, L=16, d=64, m=256, eps=1e-
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(w=0), 1), (dict(o=0), 1),
-    (dict(B=0), 2), (dict(H=0), 2), (dict(L=0), 2), (dict(hw=3, H=2), 2), (dict(B=1 << 14, H=1 << 14, L=64), 2),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(L=0), 2), (dict(hw=3, H=2), 2),
+    (dict(B=1 << 8, H=1 << 8, L=64), 2),             # B*H above the grid's 65534
+    (dict(L=1 << 22, d=64, m=256), 2),              # L*max(d, m) >= 2^30 (one head's 32-bit offsets)
+    (dict(L=1 << 21, d=128, m=512), 2),
     (dict(d=48), 3), (dict(d=256), 3), (dict(m=0), 3), (dict(m=-32), 3), (dict(m=544), 3), (dict(dt=7), 3),
 ])
 def test_validation_errors(kw, code):
@@ -93,3 +96,52 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         favor.attn(x, x, x, torch.zeros(256, 64))
+
+
+def test_status_codes_of_the_header():
+    """The header's status enumeration and the binding's table agree."""
+    import random_feature_approx_amd as favor
+    text = open(HEADER).read()
+    codes = dict((name, int(v)) for name, v in re.findall(r"(FAVOR_(?:OK|ERR_[A-Z]+))\s*=\s*(\d+)", text))
+    assert codes == {"FAVOR_OK": 0, "FAVOR_ERR_NULL": 1, "FAVOR_ERR_SHAPE": 2, "FAVOR_ERR_UNSUPPORTED": 3,
+                     "FAVOR_ERR_WORKSPACE": 4, "FAVOR_ERR_HIP": 5, "FAVOR_ERR_INTERNAL": 6}
+    lib = _lib()
+    for name, code in codes.items():
+        assert lib.favor_status_string(code).decode() == favor.STATUS[code]
+
+
+def test_large_shapes_pass_the_size_check():
+    """Shapes whose total B*H*L*max(d, m) exceeds 2^31 are valid as long as
+    one head stays below the 32-bit limit: such a call gets past the shape
+    checks (here it stops at the NULL workspace, or at the device query when
+    no GPU is present), never at FAVOR_ERR_SHAPE."""
+    lib = _lib()
+    st = _nc(lib, B=1, H=64, L=131072, d=64, m=256)
+    assert st in (4, 5)                               # workspace missing / no device; not 2
+    st = _nc(lib, B=4, H=64, L=1 << 20, d=128, m=512)  # 2^40 elements in total
+    assert st in (4, 5)
+
+
+@pytest.mark.parametrize("call", ["attn", "attn_causal", "features", "softmax_attn", "attn_strided",
+                                  "attn_backward"])
+def test_binding_rejects_host_tensors(call):
+    """The binding refuses host tensors before any launch (there is no CPU
+    path): a host pointer handed to a kernel would fault the device."""
+    import torch
+    import random_feature_approx_amd as favor
+    _lib()
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    w = torch.zeros(2, 32, 64)
+    with pytest.raises((ValueError, TypeError)):
+        if call == "attn":
+            favor.attn(q, q, q, w)
+        elif call == "attn_causal":
+            favor.attn_causal(q, q, q, w)
+        elif call == "features":
+            favor.features(q, w)
+        elif call == "softmax_attn":
+            favor.softmax_attn(q, q, q)
+        elif call == "attn_strided":
+            favor.attn_strided(q, q, q, w)
+        else:
+            favor.attn_backward(q, q, q, w, q)
