@@ -204,6 +204,24 @@ favor_status favor_attn(const void* Q, const void* K, const void* V,
                         int B, int H, int L, int d, int m, float eps, int causal,
                         favor_dtype dtype, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * favor_attn for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with the workspace taken from a static
+ * device array of FAVOR_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on (from the first such call on that device until the
+ * process ends).  The call allocates nothing; the caller still provides Q,
+ * K, V, W and O.  A call whose workspace (favor_workspace_bytes) exceeds the
+ * scratch returns FAVOR_ERR_WORKSPACE and launches nothing.  Every call on
+ * one device shares that device's scratch: calls that may overlap on one
+ * device (concurrent streams, threads) race and must be serialised by the
+ * caller.  Results equal favor_attn's bit for bit.
+ */
+#define FAVOR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+favor_status favor_attn_noalloc(const void* Q, const void* K, const void* V,
+                                const float* W, int Hw, void* O,
+                                int B, int H, int L, int d, int m, float eps, int causal,
+                                favor_dtype dtype, void* stream);
 
 /*
  * Backward pass of non-causal attention: the gradients dQ, dK, dV of

@@ -24,7 +24,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["load", "library_path", "features", "attn", "attn_noncausal", "attn_causal", "FMAPS", "softmax_attn", "attn_strided", "draw_projection",
+__all__ = ["load", "library_path", "features", "attn", "attn_noalloc", "attn_noncausal", "attn_causal", "FMAPS", "softmax_attn", "attn_strided", "draw_projection",
            "workspace_bytes", "attn_backward", "bwd_workspace_bytes", "FavorError", "STATUS", "KERNELS",
            "timing_start", "timing_stop"]
 
@@ -76,6 +76,8 @@ def load():
         getattr(lib, name).argtypes = attn_args
     lib.favor_attn.restype = i
     lib.favor_attn.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.favor_attn_noalloc.restype = i
+    lib.favor_attn_noalloc.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, f, i, i, vp]
     lib.favor_workspace_bytes_fmap.restype = sz
     lib.favor_workspace_bytes_fmap.argtypes = [i, i, i, i, i, i, i, i]
     lib.favor_features_fmap.restype = i
@@ -244,6 +246,32 @@ def attn(q, k, v, w, causal: bool = False, eps: float = 1e-6, out=None, workspac
     if st != 0:
         raise FavorError(name, st)
     return o
+
+
+def attn_noalloc(q, k, v, w, out, causal: bool = False, eps: float = 1e-6):
+    """favor_attn_noalloc: attention into the caller's `out` with the
+    library's static device scratch as workspace (no allocation by the call;
+    calls on one device must not overlap).  Raises FavorError (status 4) when
+    the shape needs more workspace than the scratch holds."""
+    lib = load()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, L, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, H, L, d = q.shape
+    w, hw = _proj(w, H, (w.shape[-2], d))
+    m = int(w.shape[1])
+    _check_device(q, k, v, w)
+    if k.device != q.device or v.device != q.device or w.device != q.device:
+        raise ValueError("q, k, v and W must live on one device")
+    _check_out(out, q.shape, q.dtype, q.device)
+    st = lib.favor_attn_noalloc(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(w.data_ptr()), hw,
+                                ctypes.c_void_p(out.data_ptr()), B, H, L, d, m, float(eps), int(bool(causal)),
+                                _dtype_code(q), _stream())
+    if st != 0:
+        raise FavorError("favor_attn_noalloc", st)
+    return out
 
 
 def attn_noncausal(q, k, v, w, eps: float = 1e-6, **kw):

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 namespace favor {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -215,6 +217,29 @@ void timing_end(favor_kernel k, hipStream_t s) {
     ++t.used;
     t.open = false;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for favor_attn_noalloc: one array per device (each device
+// that loads the library holds its own copy until the process ends).  The
+// array's name is only a host-side handle; kernels get the device address
+// that hipGetSymbolAddress returns, looked up once per device with that
+// device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[FAVOR_NOALLOC_SCRATCH_BYTES];
+static void* g_scratch_addr[64];
+static std::mutex g_scratch_mu;
+
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_addr[dev] = p;
+  }
+  return g_scratch_addr[dev];
 }
 
 }  // namespace favor
@@ -487,6 +512,20 @@ favor_status favor_attn(const void* Q, const void* K, const void* V, const float
                         int L, int d, int m, float eps, int causal, favor_dtype dtype, void* ws, size_t ws_bytes,
                         void* stream) {
   return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, causal, dtype, ws, ws_bytes, stream);
+}
+
+favor_status favor_attn_noalloc(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O,
+                                int B, int H, int L, int d, int m, float eps, int causal, favor_dtype dtype,
+                                void* stream) {
+  if (!Q || !K || !V || !W || !O) return FAVOR_ERR_NULL;
+  favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
+  if (st != FAVOR_OK) return st;
+  Plan p;
+  if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count())) return FAVOR_ERR_HIP;
+  if (p.total > FAVOR_NOALLOC_SCRATCH_BYTES) return FAVOR_ERR_WORKSPACE;    // nothing launched
+  void* ws = scratch_address();
+  if (!ws) return FAVOR_ERR_HIP;
+  return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, causal, dtype, ws, FAVOR_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 favor_status favor_attn_fmap(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
