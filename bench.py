@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 METRIC = "FAVOR+ fwd tokens/sec (B·H·L/s) causal & non-causal; % of MFMA/HBM roofline"
 PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks
-KERNEL_SOURCES = ["favor_device.hpp", "favor_tiles.hpp", "favor_nc.hip", "favor_causal.hip"]   # forward kernels
+KERNEL_SOURCES = ["favor_device.hpp", "favor_tiles.hpp", "favor_nc.hip", "favor_causal.hip",
+                  "favor_causal3.hip"]   # forward kernels
 BWD_KERNELS = ["k_bprep", "k_bred", "k_bcombine", "k_bside_q", "k_bside_k"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -252,61 +253,11 @@ def fmap_leg(favor, torch, wl, q, k, v, w, outs, K: int, warmup: int) -> dict:
     return out
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the default warmup (about 20 ms of back-to-back steps) outlasts the
-    # shader clock's settling after a burst of work begins: a few ms in, the
-    # clock falls from about 2.0 to about 1.5 GHz and climbs back over the
-    # next ~10 ms, so a short warmup puts that dip into the timed steps
-    ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--workload", default="long", choices=["t1", "encoder", "causal_lm", "long", "wide"])
-    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time budget per path (0 = skip)")
-    ap.add_argument("--paths", default="", help="comma-separated subset of the workload's paths to run "
-                                                "(default: all; used to attribute profiler counters to a path)")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
-    ap.add_argument("--no-fmaps", action="store_true", help="skip the feature-map variant measurement")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB mebibytes 5 times (the reference "
-                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
-        return 0
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): heads are independent, so several "
-              "GPUs would each run this library on their own heads; nothing here runs on more than one",
-              file=sys.stderr)
-        return 2
-    if int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py is a single-process benchmark; do not launch it with several ranks", file=sys.stderr)
-        return 2
-
-    import numpy as np
-    import torch
-    import random_feature_approx_amd as favor
-    import synth
-
-    favor.load()
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        return 1
-    wl = synth.WORKLOADS[args.workload]
-    if args.paths:
-        keep = [p for p in args.paths.split(",") if p]
-        bad = [p for p in keep if p not in wl.paths]
-        if bad:
-            print(f"workload {wl.name} has no path {bad}", file=sys.stderr)
-            return 2
-        wl = dataclasses.replace(wl, paths=tuple(keep))
+def measure(favor, torch, np, synth, wl, K: int, warmup: int, settle_ms: float, with_traffic: bool) -> dict:
+    """One workload: settle the clock, W warmup steps, K timed steps (no
+    other events on the stream), then K more steps with per-path events and
+    the library's per-launch kernel events for the per-path and per-kernel
+    figures and the dominant kernel's roofline."""
     log(f"workload {wl.name}: B={wl.B} H={wl.H} L={wl.L} d={wl.d} m={wl.m} {wl.dtype} paths={wl.paths}")
     x = synth.make_inputs(wl, with64=False)
     dev = torch.device("cuda", 0)
@@ -328,13 +279,18 @@ def main() -> int:
     def run(path):
         favor.attn(q, k, v, w, causal=(path == "causal"), eps=wl.eps, out=outs[path], workspace=wss[path])
 
-    for _ in range(args.warmup):
+    if settle_ms > 0:
+        t_end = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for p in wl.paths:
+                run(p)
+            torch.cuda.synchronize()
+    for _ in range(warmup):
         for p in wl.paths:
             run(p)
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
+    log(f"clock settle {settle_ms:.0f} ms, warmup {warmup} steps done")
 
-    K = args.steps
     # the timed steps carry no per-kernel or per-path events: events between
     # launches add idle time to the stream
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -380,22 +336,114 @@ def main() -> int:
             per_kernel[f"{p}/{kname}"] = {"avg_ms": sum(mine) / len(mine), "launches": len(mine)}
     dom_key = max(per_kernel, key=lambda k: per_kernel[k]["avg_ms"])
     dom_path, dom_kernel = dom_key.split("/")
-    roof = roofline_entry(dom_kernel, dom_path, wl, per_kernel[dom_key]["avg_ms"],
-                          stored_traffic(dom_kernel, dom_path, wl.name))
+    traffic = stored_traffic(dom_kernel, dom_path, wl.name) if with_traffic else None
+    roof = roofline_entry(dom_kernel, dom_path, wl, per_kernel[dom_key]["avg_ms"], traffic)
     kern_report = {}
     for key, val in per_kernel.items():
         p, kn = key.split("/")
         r = roofline_entry(kn, p, wl, val["avg_ms"], None) if algorithmic(kn, p, wl)["bytes"] else {}
         kern_report[key] = {"avg_ms": round(val["avg_ms"], 5), "launches": val["launches"],
                             "hbm_frac_alg": r.get("hbm_frac_alg"), "mfma_frac_alg": r.get("mfma_frac_alg")}
+    paths_report = {p: {"ms": round(path_ms[p], 5), "tokens_per_s": round(wl.tokens / (path_ms[p] * 1e-3), 1)}
+                    for p in wl.paths}
+    return {"ms_per_step": round(ms_step, 5), "roofline": roof, "kernels": kern_report, "paths": paths_report,
+            "_inputs": (x, q, k, v, w, outs, to_dev)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    # the default warmup (about 20 ms of back-to-back steps) outlasts the
+    # shader clock's settling after a burst of work begins: a few ms in, the
+    # clock falls from about 2.0 to about 1.5 GHz and climbs back over the
+    # next ~10 ms, so a short warmup puts that dip into the timed steps
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--workload", default="long", choices=["t1", "encoder", "causal_lm", "long", "wide"])
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time budget per path (0 = skip)")
+    ap.add_argument("--paths", default="", help="comma-separated subset of the workload's paths to run "
+                                                "(default: all; used to attribute profiler counters to a path)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-fmaps", action="store_true", help="skip the feature-map variant measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workload configurations")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps per other configuration")
+    ap.add_argument("--config-warmup", type=int, default=5, help="warmup steps per other configuration")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="back-to-back steps run for this long before the warmup steps of each workload, "
+                         "so that the shader clock has left its dip at the start of a burst (0 = none)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes 5 times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): heads are independent, so several "
+              "GPUs would each run this library on their own heads; nothing here runs on more than one",
+              file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py is a single-process benchmark; do not launch it with several ranks", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import random_feature_approx_amd as favor
+    import synth
+
+    favor.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.WORKLOADS[args.workload]
+    if args.paths:
+        keep = [p for p in args.paths.split(",") if p]
+        bad = [p for p in keep if p not in wl.paths]
+        if bad:
+            print(f"workload {wl.name} has no path {bad}", file=sys.stderr)
+            return 2
+        wl = dataclasses.replace(wl, paths=tuple(keep))
+    res = measure(favor, torch, np, synth, wl, args.steps, args.warmup, args.settle_ms, with_traffic=True)
+    x, q, k, v, w, outs, to_dev = res.pop("_inputs")
+    ms_step = res["ms_per_step"]
+    roof = res["roofline"]
+    kern_report = res["kernels"]
+    path_ms = {p: res["paths"][p]["ms"] for p in wl.paths}
+    K = args.steps
 
     bwd = None if args.no_backward else backward_leg(favor, torch, wl, q, k, v, w, to_dev, K, args.warmup)
     fmaps = None if args.no_fmaps else fmap_leg(favor, torch, wl, q, k, v, w, outs, K, args.warmup)
 
     tokens = wl.tokens
     value = tokens / (ms_step * 1e-3)
-    paths_report = {p: {"ms": round(path_ms[p], 5), "tokens_per_s": round(tokens / (path_ms[p] * 1e-3), 1)}
-                    for p in wl.paths}
+    paths_report = res["paths"]
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for name in ("t1", "encoder", "causal_lm", "wide"):
+            if name == wl.name:
+                continue
+            other = synth.WORKLOADS[name]
+            r = measure(favor, torch, np, synth, other, args.config_steps, args.config_warmup, args.settle_ms,
+                        with_traffic=False)
+            r.pop("_inputs")
+            configs[name] = {"workload": f"{other.name}: B={other.B} H={other.H} L={other.L} d={other.d} "
+                                         f"m={other.m} {other.dtype}, {' + '.join(other.paths)}",
+                             "ms_per_step": r["ms_per_step"],
+                             "tokens_per_s": round(other.tokens / (r["ms_per_step"] * 1e-3), 1),
+                             "steps": args.config_steps, "paths": r["paths"], "roofline": r["roofline"],
+                             "kernels": r["kernels"]}
+            if name == "t1":
+                configs[name]["latency_ms"] = r["ms_per_step"]
+            torch.cuda.empty_cache()
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(wl, x, args.cpu_seconds)
@@ -419,7 +467,9 @@ def main() -> int:
                    "chunk": causal_chunk(wl), "eps": wl.eps},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "clock_settle_ms": args.settle_ms,
         "paths": paths_report,
+        "configs": configs,
         "kernels": kern_report,
         "backward": bwd,
         "feature_maps": fmaps,
