@@ -53,8 +53,11 @@ struct Causal3Args {
 template <int D>
 struct Causal3Lds {
   static constexpr int C = 32;                           // tokens per chunk
-  // fp16 rows of Q and K: D values, then 16 bias columns ([hi, lo, 0, ...])
-  static constexpr int RSX = (D + 16) * 2;
+  // fp16 rows of Q and K: D values, then 16 bias columns ([hi, lo, 0, ...]),
+  // padded to an odd number of 16-byte chunks so that 16 consecutive rows
+  // start in 16 different LDS bank groups (fragment reads: lane = row)
+  static constexpr int RSX0 = (D + 16) * 2;
+  static constexpr int RSX = (RSX0 / 16) % 2 ? RSX0 : RSX0 + 16;
   static constexpr int RS = Rows<D, 2>::RS;              // raw V rows (padded)
   static constexpr int kQh = 0, kKh = C * RSX, kV = 2 * C * RSX, kVT = kV + C * RS;
   static constexpr int BUF = kVT + C * D * 2;            // one chunk buffer
@@ -146,8 +149,10 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
   // Q, K rows converted to fp16 with their bias columns; V raw.  The bias
   // is split as hi = fp16(b), lo = fp16(b - hi); rows past the span get
   // hi = -inf, lo = 0, so their features are exactly zero.  Each row's bias
-  // chunk [hi, lo, 0 x 6] and zero chunk are written by alternate lanes of
-  // the row (identical values from every writer).
+  // chunk [hi, lo, 0 x 6] is written by the row's lane 0 and its zero chunk
+  // by lane 1; the other lanes write their own data chunk a second time
+  // (same value, own address), so that no two lanes of one write touch the
+  // same address.
   auto store_chunk = [&](int ci) {
     char* buf = buf_of(ci);
     const bool valid = t0 + ci * C + srow < t1;
@@ -172,12 +177,15 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
     // |w| exceeds ~200)
     const float bqh = (float)(_Float16)fmaxf(bq, -65504.f), bkh = (float)(_Float16)fmaxf(bk, -65504.f);
     // bitwise selects: computed for every lane, so no branch is formed
-    const unsigned mv = 0u - (unsigned)valid, mb = (scc & 1) - 1u;    // all ones: valid row / bias chunk
-    const unsigned cq = ((pack_f16(bqh, fmaxf(bq - bqh, -65504.f)) & mv) | (0xFC00u & ~mv)) & mb;   // pad: -inf, 0
-    const unsigned ck = ((pack_f16(bkh, fmaxf(bk - bkh, -65504.f)) & mv) | (0xFC00u & ~mv)) & mb;
-    const int boff = D * 2 + (scc & 1) * 16;
-    *(u32x4*)(buf + LY::kQh + srow * RSX + boff) = u32x4{cq, 0u, 0u, 0u};
-    *(u32x4*)(buf + LY::kKh + srow * RSX + boff) = u32x4{ck, 0u, 0u, 0u};
+    const unsigned mv = 0u - (unsigned)valid;                          // all ones: valid row
+    const unsigned cq = (pack_f16(bqh, fmaxf(bq - bqh, -65504.f)) & mv) | (0xFC00u & ~mv);   // pad: -inf, 0
+    const unsigned ck = (pack_f16(bkh, fmaxf(bk - bkh, -65504.f)) & mv) | (0xFC00u & ~mv);
+    const unsigned m0 = scc == 0 ? ~0u : 0u, m1 = scc <= 1 ? ~0u : 0u;  // bias chunk / bias or zero chunk
+    const int boff = scc <= 1 ? D * 2 + scc * 16 : scc * 16;
+    *(u32x4*)(buf + LY::kQh + srow * RSX + boff) =
+        u32x4{(cq & m0) | (hq[0] & ~m1), hq[1] & ~m1, hq[2] & ~m1, hq[3] & ~m1};
+    *(u32x4*)(buf + LY::kKh + srow * RSX + boff) =
+        u32x4{(ck & m0) | (hk[0] & ~m1), hk[1] & ~m1, hk[2] & ~m1, hk[3] & ~m1};
   };
   // V^T fragment (s2, db): lane (d, hh) holds V[crow(8 s2 + j, hh)][32 db + d]
   auto vt_at = [&](const char* buf, int s2, int db) -> const char* {
@@ -206,25 +214,41 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
       kf[s] = row_frag<Tr, D>(krow, hh, s);
     }
     const F qb = *(const F*)(qrow + D * 2 + 16 * hh), kb = *(const F*)(krow + D * 2 + 16 * hh);
+    const f32x16 bq = Tr::pmma(wbias, qb, zero16());      // the row biases
+    const f32x16 bk = Tr::pmma(wbias, kb, zero16());
+    f32x16 aq[FBW], ak[FBW];
 #pragma unroll
     for (int i = 0; i < FBW; ++i) {
-      f32x16 aq = Tr::pmma(wbias, qb, zero16());          // the row bias
-      f32x16 ak = Tr::pmma(wbias, kb, zero16());
+      aq[i] = bq;
+      ak[i] = bk;
 #pragma unroll
       for (int s = 0; s < NKD; ++s) {
-        aq = Tr::pmma(wf[i][s], qf[s], aq);               // + P^T[f][t]
-        ak = Tr::pmma(wf[i][s], kf[s], ak);
+        aq[i] = Tr::pmma(wf[i][s], qf[s], aq[i]);         // + P^T[f][t]
+        ak[i] = Tr::pmma(wf[i][s], kf[s], ak[i]);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        aq[r] = exp2_fast(aq[r]);
-        ak[r] = exp2_fast(ak[r]);
+        aq[i][r] = exp2_fast(aq[i][r]);
+        ak[i][r] = exp2_fast(ak[i][r]);
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        pq[i][s2] = CFrag<Tr>::make(aq, s2);
-        pk[i][s2] = CFrag<Tr>::make(ak, s2);
+        pq[i][s2] = CFrag<Tr>::make(aq[i], s2);
+        pk[i][s2] = CFrag<Tr>::make(ak[i], s2);
       }
+    }
+    // Issue order: the dependent projection chains of the first feature
+    // block, then the second block's chains with the first block's
+    // exponentials between their matrix instructions (a wave issues in
+    // order, so exponentials placed after a chain would wait for all of it)
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 + 2 * NKD, 0);   // biases, block 0
+#pragma unroll
+    for (int s = 0; s < NKD; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);           // block 1, k-step s
+      __builtin_amdgcn_sched_group_barrier(0x400, 32 / NKD, 0);    // block 0 exponentials
     }
   };
 
