@@ -72,7 +72,15 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.rfgroups = (nfb + p.rnw * p.rfbw - 1) / (p.rnw * p.rfbw);
   // the causal scan for bf16 FAVOR+ with d <= 64 and m = 256 (k_causal3)
   p.scan3 = (causal && dt == FAVOR_BF16 && fmap == FAVOR_FMAP_POSITIVE && p.mt == 256 && (d == 32 || d == 64)) ? 1 : 0;
-  const int target = 2 * num_cus;
+  // the float32 FAVOR+ scan for d = 128 on split 16-bit products
+  // (k_causal_x3, one workgroup per compute unit); FAVOR_F32_MFMA=1 keeps
+  // the float32 matrix-core scan instead (comparisons and tuning)
+  {
+    const char* env = getenv("FAVOR_F32_MFMA");
+    const bool f32_mfma = env && atoi(env) > 0;
+    p.x3 = (causal && dt == FAVOR_F32 && fmap == FAVOR_FMAP_POSITIVE && d == 128 && !f32_mfma) ? 1 : 0;
+  }
+  const int target = p.x3 ? num_cus : 2 * num_cus;
   // non-causal: reduction workgroups = BH * splits * rfgroups; causal: the
   // chunk scan runs one workgroup per (span, head) and walks feature groups
   // in turn, so spans alone fill the device.
@@ -136,7 +144,8 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.off_num = off;
   if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * d * sizeof(float));
   p.off_den = off;
-  if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * sizeof(float));
+  // (k_causal_x3: one copy per wave)
+  if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * sizeof(float) * (p.x3 ? 4 : 1));
   p.total = off;
   // backward: 4 feature blocks per reduction workgroup, about two
   // workgroups per compute unit; the causal backward reduces over the spans

@@ -106,22 +106,6 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
   }
 }
 
-struct CausalArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* w;
-  void* o;
-  const float* prefix;    // [BH][spans][M][D] exclusive prefixes of S
-  const float* prefixz;   // [BH][spans][M]
-  float* num;             // [BH][L][D] partial numerators (fgroups > 1)
-  float* den;             // [BH][L]
-  int L, M, H, Hw, spans, span_len, fgroups;
-  float eps;
-  int Mw;                 // feature rows per head (M, or M/2 for the trig map), a multiple of 32
-  int mt;                 // rows of W per head as given; features of rows >= mt are padding
-};
-
 // LDS layout (bytes), computed identically on host and device.
 // Tokens per chunk of the generic scan.  32: the per-wave numerators
 // (NDB x chunk/32 accumulator tiles) and feature fragments of a 64-token
@@ -914,6 +898,7 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.scan3) return launch_causal3(p, t, s);
+  if (p.x3) return launch_causal_x3(p, t, s);
   switch (p.fmap) {
     case FM_POS: return causal_fmap<FM_POS>(p, t, s);
     case FM_ELU1: return causal_fmap<FM_ELU1>(p, t, s);

@@ -65,6 +65,7 @@ __device__ __forceinline__ unsigned pack_f16(float lo, float hi) {
 // __builtin_bit_cast applied directly to a vector subscript has been seen to
 // read element 0 whatever the subscript.
 __device__ __forceinline__ float as_f32(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned as_u32(float x) { return __builtin_bit_cast(unsigned, x); }
 
 __device__ __forceinline__ float bf16_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }

@@ -33,6 +33,7 @@ struct Plan {
   int rfgroups;         // reduction feature groups per head (workgroups sharing K, V tiles)
   // causal chunk scan
   int scan3;            // the pipelined one-workgroup-per-CU scan (bf16, d <= 64, m = 256, FAVOR+)
+  int x3;               // float32 FAVOR+ with d = 128: the scan on split 16-bit products (k_causal_x3)
   int fgroups;          // feature groups walked in turn by one workgroup
   int fbw;              // 32-feature blocks per wave
   // Q-side apply (non-causal)
@@ -77,6 +78,23 @@ struct BwdTensors {
   char* ws;
 };
 
+// Arguments of the causal chunk scans (k_causal, k_causal2, k_causal_x3).
+struct CausalArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* w;
+  void* o;
+  const float* prefix;    // [BH][spans][M][D] exclusive prefixes of S
+  const float* prefixz;   // [BH][spans][M]
+  float* num;             // [BH][L][D] partial numerators (fgroups > 1)
+  float* den;             // [BH][L]
+  int L, M, H, Hw, spans, span_len, fgroups;
+  float eps;
+  int Mw;                 // feature rows per head (M, or M/2 for the trig map), a multiple of 32
+  int mt;                 // rows of W per head as given; features of rows >= mt are padding
+};
+
 // Kernel timing hooks (see favor_timing_start): record the next free event
 // pair of kernel k around a launch on stream s.
 void timing_begin(favor_kernel k, hipStream_t s);
@@ -86,6 +104,7 @@ hipError_t launch_features(const Plan& p, const void* x, const float* w, float* 
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal3(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_causal_x3(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t gather_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int width, int n,
                        hipStream_t s);
 hipError_t scatter_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int n, int srow,

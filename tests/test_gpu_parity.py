@@ -245,6 +245,10 @@ def test_noncausal_constant_values(gpu):
     ("f32", 64, 256, 1, 2, 1000),       # several spans, two feature groups (two workgroups per CU build)
     ("f32", 32, 512, 1, 2, 700),        # several spans, four feature groups
     ("bf16", 32, 256, 1, 2, 1000),      # the m = 256 scan at d = 32, several spans
+    ("f32", 128, 512, 1, 2, 1000),      # split-product scan: several spans, four feature groups
+    ("f32", 128, 128, 2, 2, 777),       # split-product scan: one feature group, ragged last chunk
+    ("f32", 128, 200, 1, 1, 333),       # split-product scan: ragged m, a feature block past m
+    ("f32", 128, 256, 1, 1, 1),         # split-product scan: one token
 ])
 def test_causal_parity(gpu, dtype, d, m, B, H, L):
     x = synth.random_case(3000 + d + m + L, B, H, L, d, m, dtype)
