@@ -59,6 +59,15 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   p.B = B; p.H = H; p.L = L; p.D = d; p.M = m; p.Hw = Hw; p.causal = causal ? 1 : 0; p.dt = dt;
   p.BH = B * H;
   p.esize = dt == FAVOR_BF16 ? 2 : 4;
+  // the float32 FAVOR+ scan for d = 128 on split 16-bit products
+  // (k_causal_x3, one workgroup per compute unit, and its span
+  // aggregates k_reduce_x3, eight waves); FAVOR_F32_MFMA=1 keeps
+  // the float32 matrix-core scan instead (comparisons and tuning)
+  {
+    const char* env = getenv("FAVOR_F32_MFMA");
+    const bool f32_mfma = env && atoi(env) > 0;
+    p.x3 = (causal && dt == FAVOR_F32 && fmap == FAVOR_FMAP_POSITIVE && d == 128 && !f32_mfma) ? 1 : 0;
+  }
   // reduction split: about two workgroups per compute unit, ranges of at
   // least 256 tokens, whole 64-token tiles (two 32-token chunks of the
   // causal scans).
@@ -68,18 +77,10 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   const int nfb = m / 32;
   p.fgroups = (nfb + 4 * p.fbw - 1) / (4 * p.fbw);
   p.rfbw = 1;   // two blocks per wave (4 waves) measured slower: fewer waves to hide latency
-  p.rnw = (dt == FAVOR_F32 && d == 128) ? 4 : 8;
+  p.rnw = (dt == FAVOR_F32 && d == 128 && !p.x3) ? 4 : 8;
   p.rfgroups = (nfb + p.rnw * p.rfbw - 1) / (p.rnw * p.rfbw);
   // the causal scan for bf16 FAVOR+ with d <= 64 and m = 256 (k_causal3)
   p.scan3 = (causal && dt == FAVOR_BF16 && fmap == FAVOR_FMAP_POSITIVE && p.mt == 256 && (d == 32 || d == 64)) ? 1 : 0;
-  // the float32 FAVOR+ scan for d = 128 on split 16-bit products
-  // (k_causal_x3, one workgroup per compute unit); FAVOR_F32_MFMA=1 keeps
-  // the float32 matrix-core scan instead (comparisons and tuning)
-  {
-    const char* env = getenv("FAVOR_F32_MFMA");
-    const bool f32_mfma = env && atoi(env) > 0;
-    p.x3 = (causal && dt == FAVOR_F32 && fmap == FAVOR_FMAP_POSITIVE && d == 128 && !f32_mfma) ? 1 : 0;
-  }
   const int target = p.x3 ? num_cus : 2 * num_cus;
   // non-causal: reduction workgroups = BH * splits * rfgroups; causal: the
   // chunk scan runs one workgroup per (span, head) and walks feature groups

@@ -78,6 +78,18 @@ struct BwdTensors {
   char* ws;
 };
 
+// Arguments of the K-side reductions (k_reduce, k_reduce_x3).
+struct RedArgs {
+  const void* k;
+  const void* v;
+  const float* w;
+  float* part;   // [BH][splits][M][D]
+  float* partz;  // [BH][splits][M]
+  int L, M, H, Hw, splits, split_len;
+  int Mw;        // feature rows per head (M, or M/2 for the trig map), a multiple of 32
+  int mt;        // rows of W per head as given; features of rows >= mt are padding, set to 0
+};
+
 // Arguments of the causal chunk scans (k_causal, k_causal2, k_causal_x3).
 struct CausalArgs {
   const void* q;
@@ -105,6 +117,8 @@ hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal3(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal_x3(const Plan& p, const Tensors& t, hipStream_t s);
+hipError_t launch_reduce_x3(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
+                            hipStream_t s);
 hipError_t gather_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int width, int n,
                        hipStream_t s);
 hipError_t scatter_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int n, int srow,

@@ -105,17 +105,6 @@ __global__ __launch_bounds__(256) void k_features(FeatArgs a) {
 // Wave w of the workgroup owns FBW blocks of 32 features; all four waves
 // share the K and V tiles staged in LDS.
 // ===========================================================================
-struct RedArgs {
-  const void* k;
-  const void* v;
-  const float* w;
-  float* part;   // [BH][splits][M][D]
-  float* partz;  // [BH][splits][M]
-  int L, M, H, Hw, splits, split_len;
-  int Mw;        // feature rows per head (M, or M/2 for the trig map), a multiple of 32
-  int mt;        // rows of W per head as given; features of rows >= mt are padding, set to 0
-};
-
 // Pipeline shape of the K-side kernels: tiles of TT tokens copied into a
 // ring of STAGES raw K|V tiles; each tile is prepared once (K in the
 // projection type with its row biases, and for bf16 V rearranged into
@@ -969,6 +958,7 @@ hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const fl
 
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
                          hipStream_t s) {  // also used for the causal span aggregates
+  if (p.x3) return launch_reduce_x3(p, k, v, w, part, partz, s);
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
       case 32: return launch_reduce_t<TrBF16, 32>(p, k, v, w, part, partz, s);

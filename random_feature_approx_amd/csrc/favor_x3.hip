@@ -85,6 +85,27 @@ __device__ __forceinline__ f32x16 mma3_bf16(u32x4 ah, u32x4 al, u32x4 bh, u32x4 
   return mma_bf16(ah, bh, c);
 }
 
+// k-steps of one W row (lane = feature, d-major slots) as fp16 halves of
+// W log2 e, clamped to fp16's range; zero when !ok
+template <int D>
+__device__ __forceinline__ void w_frags_f16(const float* wrow, int hh, bool ok, u32x4 (&fh)[D / 16], u32x4 (&fl)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const int d0 = (D / 2) * hh + 8 * s;
+    const f32x4 p0 = ok ? *(const f32x4*)(wrow + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 p1 = ok ? *(const f32x4*)(wrow + d0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      unsigned h, l;
+      split_f16(fminf(fmaxf(v[2 * k] * kLog2e, -65504.f), 65504.f),
+                fminf(fmaxf(v[2 * k + 1] * kLog2e, -65504.f), 65504.f), h, l);
+      fh[s][k] = h;
+      fl[s][k] = l;
+    }
+  }
+}
+
 }  // namespace x3
 using namespace x3;
 
@@ -242,22 +263,7 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
     {
       const int wr = fb * 32 + l32;
       const bool wok = fvalid && wr < a.mt;
-      const float* wrow = wh + (size_t)(wok ? wr : 0) * D;
-#pragma unroll
-      for (int s = 0; s < NKD; ++s) {
-        const int d0 = (D / 2) * hh + 8 * s;
-        const f32x4 p0 = wok ? *(const f32x4*)(wrow + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 p1 = wok ? *(const f32x4*)(wrow + d0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const float v[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          unsigned h, l;
-          split_f16(fminf(fmaxf(v[2 * k] * kLog2e, -65504.f), 65504.f),
-                    fminf(fmaxf(v[2 * k + 1] * kLog2e, -65504.f), 65504.f), h, l);
-          wfh[s][k] = h;
-          wfl[s][k] = l;
-        }
-      }
+      w_frags_f16<D>(wh + (size_t)(wok ? wr : 0) * D, hh, wok, wfh, wfl);
     }
     // ---- this wave's column block of S (all features of the group) and the
     // key sums of its own features, from the span's prefix ----
@@ -469,6 +475,206 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
       }
     }
   }
+}
+
+// ===========================================================================
+// Span aggregates for the float32 scan on the same split products:
+//   part[f][d] = sum_t phi(k_t)[f] v_t[d],  partz[f] = sum_t phi(k_t)[f]
+// over the tokens of a span (the K-side reduction of the Performer page's
+// linear-attention form, restricted to the span).  Eight waves each own 32
+// features; 32-token tiles of K and V are copied into LDS (two slots), and
+// each tile is prepared once for all waves: K as fp16 halves with its row
+// biases, V as bf16-half V^T fragments.  Per tile a wave issues 24 fp16
+// products (projection, lane = feature, so phi(K)^T needs no transpose) and
+// 24 bf16 products (state update).
+// ===========================================================================
+template <int D>
+struct RedX3Lds {
+  static constexpr int TT = 32;                         // tokens per tile
+  static constexpr int NW = 8;
+  static constexpr int NDB = D / 32;
+  static constexpr int RAW = TT * D * 4;                // one dense float32 tile
+  static constexpr int RSX = D * 2 + 16;                // fp16 rows of K (odd number of 16-byte chunks)
+  static constexpr int FRAG = 64 * 16;
+  static constexpr int kKh = 0, kKl = TT * RSX;
+  static constexpr int kVT = 2 * TT * RSX;              // [d block][k-step][hi, lo][lane] fragments
+  static constexpr int kBias = kVT + NDB * 2 * 2 * FRAG;
+  static constexpr int PREP = kBias + TT * 4;
+  static constexpr int kRaw = 2 * PREP;                 // two prepared tiles, then two raw K|V slots
+  static constexpr int kTotal = kRaw + 2 * 2 * RAW;
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void k_reduce_x3(RedArgs a) {
+  using LY = RedX3Lds<D>;
+  constexpr int TT = LY::TT, NW = LY::NW, NT = NW * 64, NKD = D / 16, NDB = LY::NDB, RSX = LY::RSX;
+  constexpr int CPR = D * 4 / 16;                       // 16-byte chunks per float32 row
+  static_assert(D == 128 && TT * CPR == 2 * NT && NDB * 2 == NW, "tile split over the threads");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int split = blockIdx.x, fg = blockIdx.y, bh = blockIdx.z;
+  const int head = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nfb = a.M >> 5;
+  const int fb = fg * NW + w;
+  const bool fvalid = fb < nfb;
+  const float* K = (const float*)a.k + (size_t)bh * a.L * D;
+  const float* V = (const float*)a.v + (size_t)bh * a.L * D;
+  const float* wh = a.w + (size_t)(a.Hw == 1 ? 0 : head) * a.mt * D;
+  const float half_ln_m = 0.5f * logf((float)a.mt);
+  const int f = fb * 32 + l32;                          // this lane's feature
+  const bool wok = fvalid && f < a.mt;
+
+  u32x4 wfh[NKD], wfl[NKD];
+  w_frags_f16<D>(wh + (size_t)(wok ? f : 0) * D, hh, wok, wfh, wfl);
+  f32x16 st[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) st[db] = zero16();
+  float zs = 0.f;
+
+  const int t0 = split * a.split_len;
+  const int t1 = min(a.L, t0 + a.split_len);
+  const int ntiles = t0 < t1 ? (t1 - t0 + TT - 1) / TT : 0;
+
+  // copies of tile tt into raw slot tt & 1 (rows past the span re-read the
+  // tile's first row); each wave issues 2 of the 16 1-KB blocks of K and of V
+  auto copy = [&](int tt) {
+    const int r0 = t0 + tt * TT, nvalid = t1 - r0;
+    char* slot = smem + LY::kRaw + (tt & 1) * 2 * LY::RAW;
+#pragma unroll
+    for (int i = 0; i < LY::RAW / 1024 / NW; ++i) {
+      const int blk = i * NW + w;
+      const int P = blk * 64 + lane, row = P / CPR;
+      const size_t off = (size_t)(r0 + (row < nvalid ? row : 0)) * D + (P % CPR) * 4;
+      __builtin_amdgcn_global_load_lds(FAVOR_GLB(K + off), LDS_PTR(void, slot + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(FAVOR_GLB(V + off), LDS_PTR(void, slot + LY::RAW + blk * 1024), 16, 0, 0);
+    }
+  };
+  // raw slot tt & 1 -> prepared buffer tt & 1
+  auto prepare = [&](int tt) {
+    const char* raw = smem + LY::kRaw + (tt & 1) * 2 * LY::RAW;
+    char* pb = smem + (tt & 1) * LY::PREP;
+    float* bias = (float*)(pb + LY::kBias);
+    const int nvalid = t1 - (t0 + tt * TT);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {                       // K: chunks (tid / 32 + 16 i, tid % 32)
+      const int row = tid / CPR + (NT / CPR) * i, cc = tid % CPR;
+      f32x4 x = *(const f32x4*)(raw + row * D * 4 + cc * 16);
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss = fmaf(x[j], x[j], ss);
+      ss = group_sum<CPR>(ss);
+      const bool big = ss > 1048576.f;
+      if (__builtin_amdgcn_ballot_w64(big)) {          // rare: zero such rows
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = big ? 0.f : x[j];
+      }
+      u32x2 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        unsigned h, l;
+        split_f16(x[2 * j], x[2 * j + 1], h, l);
+        hi[j] = h;
+        lo[j] = l;
+      }
+      *(u32x2*)(pb + LY::kKh + row * RSX + cc * 8) = hi;
+      *(u32x2*)(pb + LY::kKl + row * RSX + cc * 8) = lo;
+      if (cc == 0) bias[row] = (row < nvalid && !big) ? -(0.5f * ss + half_ln_m) * kLog2e : -INFINITY;
+    }
+    {                                                   // V^T fragment w (d block w / 2, k-step w % 2), lane
+      const int db = w >> 1, s2 = w & 1;
+      const float* rv = (const float*)(raw + LY::RAW);
+      float vv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vv[j] = rv[(16 * s2 + 8 * (j >> 2) + 4 * hh + (j & 3)) * D + db * 32 + l32];
+      u32x4 vh, vl;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        unsigned h, l;
+        split_bf16(vv[2 * k], vv[2 * k + 1], h, l);
+        vh[k] = h;
+        vl[k] = l;
+      }
+      *(u32x4*)(pb + LY::kVT + (w * 2 + 0) * LY::FRAG + lane * 16) = vh;
+      *(u32x4*)(pb + LY::kVT + (w * 2 + 1) * LY::FRAG + lane * 16) = vl;
+    }
+  };
+
+  if (ntiles > 0) {
+    copy(0);
+    wait_vmcnt<0>();
+    raw_barrier();
+    prepare(0);
+    if (ntiles > 1) copy(1);
+  }
+  for (int tt = 0; tt < ntiles; ++tt) {
+    wait_vmcnt<0>();                          // this wave's copies of tile tt + 1 landed
+    wait_lgkm0();                             // this wave's preparation of tile tt written
+    raw_barrier();                            // ... everywhere; tile tt - 1 fully consumed
+    if (tt + 1 < ntiles) prepare(tt + 1);
+    if (fvalid) {
+      const char* pb = smem + (tt & 1) * LY::PREP;
+      const float* sb = (const float*)(pb + LY::kBias);
+      // P[t][f] + bias[t]: lane = feature, values = tokens (c-row order)
+      f32x16 acc;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 b4 = *(const f32x4*)(sb + 8 * g + 4 * hh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * g + j] = b4[j];
+      }
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) {
+        const int xo = l32 * RSX + ((D / 2) * hh + 8 * s) * 2;
+        const u32x4 kh = *(const u32x4*)(pb + LY::kKh + xo), kl = *(const u32x4*)(pb + LY::kKl + xo);
+        acc = mma_f16(kl, wfh[s], acc);
+        acc = mma_f16(kh, wfl[s], acc);
+        acc = mma_f16(kh, wfh[s], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = wok ? exp2_fast(acc[r]) : 0.f;
+      u32x4 ph[2], pl[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        split_frag(acc, s2, ph[s2], pl[s2]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) zs = dot2_bf16(pl[s2][k], 0x3f803f80u, dot2_bf16(ph[s2][k], 0x3f803f80u, zs));
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const u32x4 vh = *(const u32x4*)(pb + LY::kVT + ((db * 2 + s2) * 2 + 0) * LY::FRAG + lane * 16);
+          const u32x4 vl = *(const u32x4*)(pb + LY::kVT + ((db * 2 + s2) * 2 + 1) * LY::FRAG + lane * 16);
+          st[db] = mma3_bf16(ph[s2], pl[s2], vh, vl, st[db]);   // S[f][d]
+        }
+    }
+    if (tt + 2 < ntiles) copy(tt + 2);        // raw slot tt & 1 was prepared before the barrier
+  }
+
+  if (fvalid) {
+    float* P = a.part + ((size_t)bh * a.splits + split) * a.M * D;
+    float* Pz = a.partz + ((size_t)bh * a.splits + split) * a.M;
+    const int f0 = fb * 32;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) P[(size_t)(f0 + crow(r, hh)) * D + db * 32 + l32] = st[db][r];
+    const float z = half_sum(zs);
+    if (hh == 0) Pz[f0 + l32] = z;
+  }
+}
+
+hipError_t launch_reduce_x3(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
+                            hipStream_t s) {
+  if (!p.x3 || p.D != 128 || p.rnw != RedX3Lds<128>::NW || p.rfbw != 1) return kErrPlan;
+  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw, p.mt};
+  timing_begin(FAVOR_KERNEL_REDUCE, s);
+  hipLaunchKernelGGL(k_reduce_x3<128>, dim3(p.splits, p.rfgroups, p.BH), dim3(RedX3Lds<128>::NW * 64),
+                     (size_t)RedX3Lds<128>::kTotal, s, a);
+  timing_end(FAVOR_KERNEL_REDUCE, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_causal_x3(const Plan& p, const Tensors& t, hipStream_t s) {
