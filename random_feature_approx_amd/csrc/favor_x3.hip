@@ -279,14 +279,20 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
     float zown = fvalid ? a.prefixz[((size_t)bh * a.spans + span) * a.M + fb * 32 + l32] : 0.f;
     if (hh == 0) sZ[l32] = zown;
 
+    // A wave stages exactly the Q and K rows it copies (rows 2 w + 8 i and
+    // 2 w + 8 i + 1), so the copies of chunk ci + 2 are issued as soon as the
+    // wave has staged chunk ci + 1, a whole chunk before they are needed;
+    // the V tile of a chunk is read by every wave and has two slots.
     copy_chunk(0);
     wait_vmcnt<0>();
-    raw_barrier();                            // every wave's copies of chunk 0 landed
     stage_chunk(0);
+    if (nch > 1) {
+      wait_lgkm0();                           // the staging reads of chunk 0 done
+      copy_chunk(1);
+    }
     for (int ci = 0; ci < nch; ++ci) {
       wait_lgkm0();
-      raw_barrier();                          // chunk ci staged; last chunk's step 2 done everywhere
-      if (ci + 1 < nch) copy_chunk(ci + 1);
+      raw_barrier();                          // chunk ci staged, its V landed; last chunk's step 2 done
       const float* sV = (const float*)(smem + LY::kRawV + (ci & 1) * LY::RAW);
 
       // ---- step 1: own features --------------------------------------------
@@ -391,13 +397,17 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
       zown += half_sum(zc);
       if (hh == 0) sZ[l32] = zown;           // read again only by this wave, after this chunk
 
-      wait_vmcnt<0>();                        // this wave's copies of chunk ci + 1 landed
       wait_lgkm0();
-      raw_barrier();                          // every wave's step 1 published, every copy landed
+      raw_barrier();                          // every wave's step 1 published
 
       // ---- step 2: own column block over the group's features ----------------
-      if (ci + 1 < nch) stage_chunk(ci + 1);  // the staging area is no longer read this chunk
+      if (ci + 1 < nch) {
+        wait_vmcnt<0>();                      // this wave's copies of chunk ci + 1 (and older stores)
+        stage_chunk(ci + 1);                  // the staging area is no longer read this chunk
+      }
       // earlier feature groups' numerators and denominators of these rows
+      // (loaded before the next copies, so waiting for them does not wait
+      // for the copies)
       const unsigned orow = (unsigned)(ci * C + l32) * D * 4u;
       u32x4 prev[4];
       float prevd = 0.f;
@@ -407,6 +417,10 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
         for (int g = 0; g < 4; ++g)
           prev[g] = __builtin_amdgcn_raw_buffer_load_b128(rn, (int)(orow + (w * 32 + 8 * g + 4 * hh) * 4u), 0, 0);
         prevd = as_f32(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)((ci * C + l32) * 4u), 0, 0));
+      }
+      if (ci + 2 < nch) {
+        wait_lgkm0();                         // own staging reads done before the copies overwrite them
+        copy_chunk(ci + 2);                   // V slot ci & 1: chunk ci's V was read before the barrier
       }
       f32x16 af = zero16();
 #pragma unroll
