@@ -6,8 +6,9 @@
 //
 // L is cut into spans (one workgroup each) and spans into chunks
 // of 32 tokens in every scan (a chunk of 64 is carried as two 32-token steps).
-//   1. k_reduce (shared with the non-causal path) computes every span's
-//      aggregate [sum phi(k) v^T | sum phi(k)] in float32.
+//   1. k_reduce (shared with the non-causal path) computes the aggregate
+//      [sum phi(k) v^T | sum phi(k)] of every span but the last (whose sum
+//      only a prefix past the end would use) in float32.
 //   2. k_span_scan turns the aggregates into exclusive prefixes in place, in
 //      a fixed order of additions (deterministic).
 //   3. k_causal3 (bf16 FAVOR+, d <= 64, m = 256), k_causal2 (other bf16,
@@ -31,6 +32,7 @@ namespace favor {
 
 // ---------------------------------------------------------------------------
 // exclusive prefix of the span aggregates, in place:  a[s] <- sum_{s'<s} a[s']
+// (the last span's aggregate is neither computed nor read).
 // The m*d + m values of a head are handled in quads of 4 floats.  A block is
 // kScanGroups groups of threads; group g owns spans [g*per, (g+1)*per) of its
 // quad: it first sums them, the groups' sums give each group its starting
@@ -58,6 +60,7 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
   }
   const int per = (spans + kScanGroups - 1) / kScanGroups;
   const int s0 = min(spans, g * per), s1 = min(spans, s0 + per);
+  const int s1a = min(s1, spans - 1);                   // the last span's aggregate is not computed
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 sum = zero;
   // at most 8 spans per group (up to 64 spans): the values stay in registers
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
     for (int s = s0; s < s1; s += 8) {
       f32x4 v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = s + j < s1 ? p[(size_t)(s + j) * stride] : zero;
+      for (int j = 0; j < 8; ++j) v[j] = s + j < s1a ? p[(size_t)(s + j) * stride] : zero;
 #pragma unroll
       for (int j = 0; j < 8; ++j) sum += v[j];
       if (kept) {
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
   for (int s = s0; s < s1; s += 8) {
     f32x4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = s + j < s1 ? p[(size_t)(s + j) * stride] : zero;
+    for (int j = 0; j < 8; ++j) v[j] = s + j < s1a ? p[(size_t)(s + j) * stride] : zero;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (s + j < s1) {
@@ -103,6 +106,38 @@ __global__ __launch_bounds__(256) void k_span_scan(float* part, float* partz, in
         run += v[j];
       }
     }
+  }
+}
+
+
+// The same prefix for at most kScanSmall spans (the usual case): one thread
+// per quad loads the span aggregates together and writes the running sums,
+// added in span order.
+constexpr int kScanSmall = 16;
+
+__global__ __launch_bounds__(256) void k_span_scan_small(float* part, float* partz, int spans, int M, int D) {
+  const int bh = blockIdx.y;
+  const int quad = blockIdx.x * 256 + threadIdx.x;
+  const int md4 = M * D / 4, nq = md4 + M / 4;
+  if (quad >= nq) return;
+  f32x4* p;
+  size_t stride;
+  if (quad < md4) {
+    p = (f32x4*)(part + (size_t)bh * spans * M * D) + quad;
+    stride = md4;
+  } else {
+    p = (f32x4*)(partz + (size_t)bh * spans * M) + (quad - md4);
+    stride = M / 4;
+  }
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 v[kScanSmall];
+#pragma unroll
+  for (int s = 0; s < kScanSmall; ++s) v[s] = s + 1 < spans ? p[(size_t)s * stride] : zero;
+  f32x4 run = zero;
+#pragma unroll
+  for (int s = 0; s < kScanSmall; ++s) {
+    if (s < spans) p[(size_t)s * stride] = run;
+    run += v[s];
   }
 }
 
@@ -888,12 +923,17 @@ static hipError_t causal2_t(const Plan& p, const Tensors& t, hipStream_t s) {
 hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s) {
   float* part = (float*)(t.ws + p.off_part);
   float* partz = (float*)(t.ws + p.off_partz);
-  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
+  // the last span's aggregate would only feed a prefix past the end
+  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s, p.splits - 1);
   if (e != hipSuccess) return e;
   const int nq = (p.M * p.D + p.M) / 4;
   timing_begin(FAVOR_KERNEL_SPAN_SCAN, s);
-  hipLaunchKernelGGL(k_span_scan, dim3((nq + kScanQuads - 1) / kScanQuads, p.BH), dim3(256), 0, s, part, partz,
-                     p.splits, p.M, p.D);
+  if (p.splits <= kScanSmall)
+    hipLaunchKernelGGL(k_span_scan_small, dim3((nq + 255) / 256, p.BH), dim3(256), 0, s, part, partz, p.splits, p.M,
+                       p.D);
+  else
+    hipLaunchKernelGGL(k_span_scan, dim3((nq + kScanQuads - 1) / kScanQuads, p.BH), dim3(256), 0, s, part, partz,
+                       p.splits, p.M, p.D);
   timing_end(FAVOR_KERNEL_SPAN_SCAN, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -118,7 +118,7 @@ hipError_t launch_causal(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal3(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_causal_x3(const Plan& p, const Tensors& t, hipStream_t s);
 hipError_t launch_reduce_x3(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                            hipStream_t s);
+                            hipStream_t s, int nsplit);
 hipError_t gather_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int width, int n,
                        hipStream_t s);
 hipError_t scatter_rows(const void* src, void* dst, const Plan& p, const long long* strides, int c0, int n, int srow,
@@ -129,7 +129,9 @@ hipError_t launch_softmax(const Plan& p, const void* q, const void* k, const voi
                           int causal, hipStream_t s);
 hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
 hipError_t launch_causal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
+// nsplit: how many token ranges to reduce (the first nsplit of p.splits;
+// -1: all).  The causal scans never read the last span's aggregate.
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                         hipStream_t s);
+                         hipStream_t s, int nsplit = -1);
 
 }  // namespace favor

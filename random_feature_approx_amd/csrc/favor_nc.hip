@@ -938,7 +938,7 @@ hipError_t launch_features(const Plan& p, const void* x, const float* w, float* 
 
 template <class Tr, int D>
 hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                           hipStream_t s) {
+                           hipStream_t s, int nsplit) {
   RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw, p.mt};
   // 8 waves of one feature block each, or 4 where a wave's registers exceed
   // half a SIMD's (two blocks per wave, sharing each K/V fragment read, ran
@@ -946,7 +946,7 @@ hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const fl
   constexpr int FBW = 1;
   constexpr int NW = (Tr::VPS == 1 && D == 128) ? 4 : 8;
   if (p.rnw != NW || p.rfbw != FBW) return kErrPlan;
-  dim3 grid(p.splits, p.rfgroups, p.BH);
+  dim3 grid(nsplit, p.rfgroups, p.BH);
   const size_t lds = RedLds<Tr, D, NW * 64>::kTotal;
   return with_fmap(p.fmap, [&]<int FM>() {
     timing_begin(FAVOR_KERNEL_REDUCE, s);
@@ -957,19 +957,21 @@ hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const fl
 }
 
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                         hipStream_t s) {  // also used for the causal span aggregates
-  if (p.x3) return launch_reduce_x3(p, k, v, w, part, partz, s);
+                         hipStream_t s, int nsplit) {  // also used for the causal span aggregates
+  if (nsplit < 0 || nsplit > p.splits) nsplit = p.splits;
+  if (nsplit == 0) return hipSuccess;
+  if (p.x3) return launch_reduce_x3(p, k, v, w, part, partz, s, nsplit);
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
-      case 32: return launch_reduce_t<TrBF16, 32>(p, k, v, w, part, partz, s);
-      case 64: return launch_reduce_t<TrBF16, 64>(p, k, v, w, part, partz, s);
-      case 128: return launch_reduce_t<TrBF16, 128>(p, k, v, w, part, partz, s);
+      case 32: return launch_reduce_t<TrBF16, 32>(p, k, v, w, part, partz, s, nsplit);
+      case 64: return launch_reduce_t<TrBF16, 64>(p, k, v, w, part, partz, s, nsplit);
+      case 128: return launch_reduce_t<TrBF16, 128>(p, k, v, w, part, partz, s, nsplit);
     }
   } else {
     switch (p.D) {
-      case 32: return launch_reduce_t<TrF32, 32>(p, k, v, w, part, partz, s);
-      case 64: return launch_reduce_t<TrF32, 64>(p, k, v, w, part, partz, s);
-      case 128: return launch_reduce_t<TrF32, 128>(p, k, v, w, part, partz, s);
+      case 32: return launch_reduce_t<TrF32, 32>(p, k, v, w, part, partz, s, nsplit);
+      case 64: return launch_reduce_t<TrF32, 64>(p, k, v, w, part, partz, s, nsplit);
+      case 128: return launch_reduce_t<TrF32, 128>(p, k, v, w, part, partz, s, nsplit);
     }
   }
   return kErrPlan;

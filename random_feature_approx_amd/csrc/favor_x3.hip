@@ -131,7 +131,8 @@ struct X3Lds {
   static constexpr int kA = kPhiK + NW * 2 * 2 * FRAG;
   static constexpr int kDen = kA + NW * 16 * 64 * 4;
   static constexpr int kZ = kDen + NW * C * 4;
-  static constexpr int kTotal = kZ + NW * 32 * 4;
+  static constexpr int kIdent = kZ + NW * 32 * 4;       // [k-step][lane] permutation fragments
+  static constexpr int kTotal = kIdent + 2 * FRAG;
 };
 
 // The scan.  CausalArgs as for the other scans; `den` holds one copy of the
@@ -237,18 +238,19 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
 
   // permutation matrix taking phi(K) (lane = token, k-slots = features in
   // c-row order) to phi(K)^T (lane = feature): k-step s2, slot j of lane half
-  // h holds feature crow(8 s2 + j, h); lane f gets a 1 where that equals f
-  u32x4 ident[2];
-  {
-    const bool mine = hh == ((l32 >> 2) & 1);
-    const int j = 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  // h holds feature crow(8 s2 + j, h); lane f gets a 1 where that equals f.
+  // Kept in LDS (two fragments) and read where it is used.
+  if (tid < 128) {
+    const int s2 = tid >> 6;
+    u32x4 id;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        ident[s2][k] = (mine && s2 == (l32 >> 4) && (j >> 1) == k) ? (0x3F80u << (16 * (j & 1))) : 0u;
+    for (int k = 0; k < 4; ++k) {
+      const unsigned lo = crow(8 * s2 + 2 * k, hh) == l32 ? 0x3f80u : 0u;
+      const unsigned hi = crow(8 * s2 + 2 * k + 1, hh) == l32 ? 0x3f80u : 0u;
+      id[k] = lo | (hi << 16);
+    }
+    *(u32x4*)(smem + LY::kIdent + tid * 16) = id;
   }
-
   char* phiq = smem + LY::kPhiQ;
   char* phik = smem + LY::kPhiK;
   float* sA = (float*)(smem + LY::kA);
@@ -296,22 +298,6 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
       const float* sV = (const float*)(smem + LY::kRawV + (ci & 1) * LY::RAW);
 
       // ---- step 1: own features --------------------------------------------
-      // V^T fragments of this wave's column block, as bf16 halves: lane = d,
-      // k-slots = tokens in c-row order
-      u32x4 vth[2], vtl[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        float vv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vv[j] = sV[(16 * s2 + 8 * (j >> 2) + 4 * hh + (j & 3)) * D + w * 32 + l32];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          unsigned h, l;
-          split_bf16(vv[2 * k], vv[2 * k + 1], h, l);
-          vth[s2][k] = h;
-          vtl[s2][k] = l;
-        }
-      }
       // projections P^T[f][t] (lane = token), started at the row biases
       f32x16 aq = splat16(sBq[l32]), ak = splat16(sBk[l32]);
 #pragma unroll
@@ -355,48 +341,66 @@ __global__ __launch_bounds__(256, 1) void k_causal_x3(CausalArgs a) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         split_frag(aq, s2, pqh[s2], pql[s2]);
-        split_frag(ak, s2, pkh[s2], pkl[s2]);
         *(u32x4*)(phiq + ((2 * w + s2) * 2 + 0) * LY::FRAG + lane * 16) = pqh[s2];
         *(u32x4*)(phiq + ((2 * w + s2) * 2 + 1) * LY::FRAG + lane * 16) = pql[s2];
       }
-      // phi(K)^T on the matrix cores (exact: one nonzero product per value)
-      f32x16 th = zero16(), tl = zero16();
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        th = mma_bf16(pkh[s2], ident[s2], th);
-        tl = mma_bf16(pkl[s2], ident[s2], tl);
-      }
+      for (int s2 = 0; s2 < 2; ++s2) split_frag(ak, s2, pkh[s2], pkl[s2]);
       // partial scores A^T[tk][tq] over own features (lane = tq), causal mask
-      f32x16 at = zero16();
+      {
+        f32x16 at = zero16();
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) at = mma3_bf16(pkh[s2], pkl[s2], pqh[s2], pql[s2], at);
+        for (int s2 = 0; s2 < 2; ++s2) at = mma3_bf16(pkh[s2], pkl[s2], pqh[s2], pql[s2], at);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (crow(r, hh) > l32) at[r] = 0.f;
-      float zc = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 kth, ktl;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          kth[k] = pack_bf16(th[8 * s2 + 2 * k], th[8 * s2 + 2 * k + 1]);
-          ktl[k] = pack_bf16(tl[8 * s2 + 2 * k], tl[8 * s2 + 2 * k + 1]);
+        for (int r = 0; r < 16; ++r) {
+          if (crow(r, hh) > l32) at[r] = 0.f;
+          dq += at[r];
         }
-        *(u32x4*)(phik + ((w * 2 + s2) * 2 + 0) * LY::FRAG + lane * 16) = kth;
-        *(u32x4*)(phik + ((w * 2 + s2) * 2 + 1) * LY::FRAG + lane * 16) = ktl;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) zc = dot2_bf16(ktl[k], 0x3f803f80u, dot2_bf16(kth[k], 0x3f803f80u, zc));
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(sA + ((w * 4 + g) * 64 + lane) * 4) = f32x4{at[4 * g], at[4 * g + 1], at[4 * g + 2], at[4 * g + 3]};
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dq += at[r];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(f32x4*)(sA + ((w * 4 + g) * 64 + lane) * 4) = f32x4{at[4 * g], at[4 * g + 1], at[4 * g + 2], at[4 * g + 3]};
       dq = half_sum(dq);
       if (hh == 0) sDen[w * C + l32] = dq;
+      // phi(K)^T on the matrix cores (exact: one nonzero product per value),
+      // the hi halves, then the lo halves; their sums update z
+      float zc = 0.f;
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        f32x16 tt = zero16();
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          tt = mma_bf16(part == 0 ? pkh[s2] : pkl[s2], *(const u32x4*)(smem + LY::kIdent + (s2 * 64 + lane) * 16), tt);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 kt;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            kt[k] = pack_bf16(tt[8 * s2 + 2 * k], tt[8 * s2 + 2 * k + 1]);
+            zc = dot2_bf16(kt[k], 0x3f803f80u, zc);
+          }
+          *(u32x4*)(phik + ((w * 2 + s2) * 2 + part) * LY::FRAG + lane * 16) = kt;
+        }
+      }
       zown += half_sum(zc);
       if (hh == 0) sZ[l32] = zown;           // read again only by this wave, after this chunk
 
+      // V^T fragments of this wave's column block, as bf16 halves: lane = d,
+      // k-slots = tokens in c-row order
+      u32x4 vth[2], vtl[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float vv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vv[j] = sV[(16 * s2 + 8 * (j >> 2) + 4 * hh + (j & 3)) * D + w * 32 + l32];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          unsigned h, l;
+          split_bf16(vv[2 * k], vv[2 * k + 1], h, l);
+          vth[s2][k] = h;
+          vtl[s2][k] = l;
+        }
+      }
       wait_lgkm0();
       raw_barrier();                          // every wave's step 1 published
 
@@ -681,11 +685,11 @@ __global__ __launch_bounds__(512, 1) void k_reduce_x3(RedArgs a) {
 }
 
 hipError_t launch_reduce_x3(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                            hipStream_t s) {
+                            hipStream_t s, int nsplit) {
   if (!p.x3 || p.D != 128 || p.rnw != RedX3Lds<128>::NW || p.rfbw != 1) return kErrPlan;
   RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw, p.mt};
   timing_begin(FAVOR_KERNEL_REDUCE, s);
-  hipLaunchKernelGGL(k_reduce_x3<128>, dim3(p.splits, p.rfgroups, p.BH), dim3(RedX3Lds<128>::NW * 64),
+  hipLaunchKernelGGL(k_reduce_x3<128>, dim3(nsplit, p.rfgroups, p.BH), dim3(RedX3Lds<128>::NW * 64),
                      (size_t)RedX3Lds<128>::kTotal, s, a);
   timing_end(FAVOR_KERNEL_REDUCE, s);
   return hipGetLastError();

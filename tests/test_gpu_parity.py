@@ -264,7 +264,8 @@ def test_causal_shared_projection(gpu, dtype, d, m):
     assert row_rel_err(out, _ref(x, True)) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,d,m", [("bf16", 64, 256), ("bf16", 32, 256), ("bf16", 64, 96), ("f32", 64, 128)])
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 64, 256), ("bf16", 32, 256), ("bf16", 64, 96), ("f32", 64, 128),
+                                     ("f32", 128, 256)])
 def test_causal_independent_of_span_count(gpu, dtype, d, m, monkeypatch):
     """The causal result does not depend on how the sequence is cut into
     spans (the cross-span prefix is exact): forced span counts of 1, 3, 7
@@ -280,6 +281,17 @@ def test_causal_independent_of_span_count(gpu, dtype, d, m, monkeypatch):
     monkeypatch.delenv("FAVOR_SPANS")
     for out in outs[1:]:
         assert row_rel_err(out, outs[0]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 64, 256), ("f32", 128, 256)])
+def test_causal_many_spans(gpu, dtype, d, m, monkeypatch):
+    """More than 16 spans per head take the two-level prefix scan (groups of
+    spans summed, then the groups' offsets); 19 spans of 320 tokens."""
+    x = synth.random_case(4150 + d, 1, 2, 6000, d, m, dtype)
+    monkeypatch.setenv("FAVOR_SPANS", "20")
+    out = _run_attn(gpu, x, dtype, causal=True)
+    monkeypatch.delenv("FAVOR_SPANS")
+    assert row_rel_err(out, _ref(x, True)) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
