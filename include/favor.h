@@ -25,12 +25,20 @@
  *    2^-25) and W log2(e) is rounded to fp16 (nearest even).  Features phi
  *    and the m x d states enter the other products as bf16 (nearest even);
  *    every product accumulates in float32, and states and sums are float32.
- *    FAVOR_F32: everything is float32.
+ *    FAVOR_F32: float32 storage, sums and states; products on the float32
+ *    matrix cores, except in the causal FAVOR+ path at d = 128, where each
+ *    product is three 16-bit products with float32 accumulation: operands
+ *    split into hi + lo halves (fp16 for the projection W x, bf16 for
+ *    features, scores, states and V), hi*hi + hi*lo + lo*hi, about 2^-16
+ *    of each product's size for bf16 halves and 2^-21 for fp16 halves;
+ *    rows with |x|^2 > 2^20 get phi = 0 there (exactly what float32 gives
+ *    when every row of W is shorter than 256).  The environment variable
+ *    FAVOR_F32_MFMA=1 selects float32 products for that path as well.
  *  - Supported shapes: d in {32, 64, 128}; 1 <= m <= 512 (the kernels work
  *    in blocks of 32 features; for m not a multiple of 32 the missing
  *    features are padding whose key-side features are set to exactly 0, so
- *    they add nothing to any sum; the backward entry points need m a
- *    multiple of 32); L >= 1; B, H >= 1; B*H <= 65534 and
+ *    they add nothing to any sum, forward and backward); L >= 1;
+ *    B, H >= 1; B*H <= 65534 and
  *    L*max(d,m) < 2^30 (offsets between heads are 64-bit, offsets inside
  *    one head 32-bit); otherwise FAVOR_ERR_SHAPE.
  *  - stream is a hipStream_t passed as void* (NULL = default stream).  Calls

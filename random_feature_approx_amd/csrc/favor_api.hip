@@ -339,7 +339,6 @@ static void timer_free(Timer& t) {
 }
 
 size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype) {
-  if (m % 32 != 0) return 0;
   Plan p;
   if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count())) return 0;
   return p.btotal;
@@ -442,7 +441,6 @@ static favor_status bwd_common(const void* Q, const void* K, const void* V, cons
   if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
   if (st != FAVOR_OK) return st;
-  if (m % 32 != 0) return FAVOR_ERR_UNSUPPORTED;     // the backward needs whole 32-feature blocks
   Plan p;
   if (!make_plan(p, B, H, L, d, m, Hw, causal, dtype, device_cu_count())) return FAVOR_ERR_HIP;
   if (!ws || ws_bytes < p.btotal || ((uintptr_t)ws & 255) != 0) return FAVOR_ERR_WORKSPACE;

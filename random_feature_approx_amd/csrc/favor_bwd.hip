@@ -71,7 +71,7 @@ template <> struct Bw<TrF32> {
 // ---------------------------------------------------------------------------
 template <class Tr>
 __global__ __launch_bounds__(256) void k_bprep(const float* w, void* wph, void* wpl, void* wt, void* wtl, int nrows,
-                                               int D) {
+                                               int D, int M, int mt) {
   using E = typename Tr::elem;
   constexpr int WES = Tr::VPS == 8 ? 2 : 4;
   constexpr int PER = 16 / WES;
@@ -85,12 +85,15 @@ __global__ __launch_bounds__(256) void k_bprep(const float* w, void* wph, void* 
     if (idx < nproj) {
       const int f = idx & 31, h = (idx >> 5) & 1, rest = idx >> 6;
       const int g = rest % nkg, blk = rest / nkg;
-      const float* src = w + (size_t)(blk * 32 + f) * D + (D / 2) * h + PER * g;
+      const int R = blk * 32 + f;                      // row of the padded operand (Hw * M rows)
+      const bool real = R % M < mt;
+      const float* src = w + ((size_t)(R / M) * mt + (real ? R % M : 0)) * D + (D / 2) * h + PER * g;
+      const float keep = real ? kLog2e : 0.f;          // rows past m: zero
       if constexpr (WES == 2) {
         unsigned hi[4], lo[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float a = src[2 * k] * kLog2e, b = src[2 * k + 1] * kLog2e;
+          const float a = src[2 * k] * keep, b = src[2 * k + 1] * keep;
           hi[k] = pack_f16(a, b);
           const f16x2 hv = __builtin_bit_cast(f16x2, hi[k]);
           lo[k] = pack_f16(a - (float)hv[0], b - (float)hv[1]);
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(256) void k_bprep(const float* w, void* wph, void* 
         ((u32x4*)wph)[idx] = u32x4{hi[0], hi[1], hi[2], hi[3]};
         ((u32x4*)wpl)[idx] = u32x4{lo[0], lo[1], lo[2], lo[3]};
       } else {
-        ((f32x4*)wph)[idx] = *(const f32x4*)src * kLog2e;
+        ((f32x4*)wph)[idx] = *(const f32x4*)src * keep;
       }
     } else {
       const int i = idx - nproj;                       // = ((((fbg*NKT + s)*NDB + db)*2 + h)*32 + c)
@@ -111,7 +114,8 @@ __global__ __launch_bounds__(256) void k_bprep(const float* w, void* wph, void* 
       E* dstl = (E*)wtl + (size_t)i * VPS;
 #pragma unroll
       for (int j = 0; j < VPS; ++j) {
-        const float x = w[(size_t)(fbg * 32 + crow(VPS * s + j, h)) * D + db * 32 + c];
+        const int R = fbg * 32 + crow(VPS * s + j, h);
+        const float x = R % M < mt ? w[((size_t)(R / M) * mt + R % M) * D + db * 32 + c] : 0.f;
         const E hi = (E)x;
         dst[j] = hi;
         if (wtl) dstl[j] = (E)(x - (float)hi);         // lo part (bf16)
@@ -139,6 +143,7 @@ struct BRedArgs {
   float* part;           // [BH][splits][M][D]
   float* partz;          // [BH][splits][M]
   int L, M, H, Hw, splits, split_len;
+  int mt;                // rows of W per head as given; features past them are padding, phi = 0
 };
 
 template <class Tr, int D>
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(256) void k_bred(BRedArgs a) {
   const bool active = fb < nfb;
   const E* X = (const E*)a.x + (size_t)bh * a.L * D;
   const E* Y = (const E*)a.y + (size_t)bh * a.L * D;
-  const float half_ln_m = 0.5f * logf((float)a.M);
+  const float half_ln_m = 0.5f * logf((float)a.mt);
 
   // projection operand of this wave's feature block (lane = feature f)
   F wf[SP::NS][NKD];
@@ -283,6 +288,7 @@ __global__ __launch_bounds__(256) void k_bred(BRedArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = exp2_fast(acc[r]);
+      if (fb * 32 + 32 > a.mt && fb * 32 + l32 >= a.mt) acc = zero16();   // padding feature (lane)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 w4 = *(const f32x4*)(sw + 8 * g + 4 * hh);
@@ -410,6 +416,7 @@ struct BSideArgs {
   float* cw;              // [BH][L] (Q side)
   int L, M, H, Hw, tiles_per_head, total;
   float eps;
+  int mt;                 // rows of W per head as given; features past them are padding, phi = 0
 };
 
 // Waves per SIMD the compiler must fit: two for the bf16 query side at d <= 64
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
   const int bh = g / a.tiles_per_head, tile = g % a.tiles_per_head;
   const int head = bh % a.H;
   const int nfb = a.M >> 5;
-  const float half_ln_m = 0.5f * logf((float)a.M);
+  const float half_ln_m = 0.5f * logf((float)a.mt);
 
   // this lane's half of its tokens' rows of X (projection type) and of Y
   int tok[TB];
@@ -513,8 +520,9 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       }
     }
   };
-  // phi^T[f][t] of block fb for token block tb (rows f = 32 fb + crow(r, h))
-  auto features = [&](const F (&wfr)[SP::NS][NKD], int tb) -> f32x16 {
+  // phi^T[f][t] of block fb for token block tb (rows f = 32 fb + crow(r, h));
+  // padding features (rows of W past m) are zero
+  auto features = [&](const F (&wfr)[SP::NS][NKD], int tb, int fb) -> f32x16 {
     f32x16 p = zero16();
 #pragma unroll
     for (int s = 0; s < NKD; ++s)
@@ -522,6 +530,11 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       for (int pp = 0; pp < SP::NS; ++pp) p = Tr::pmma(wfr[pp][s], xf[tb][s], p);
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = exp2_fast(p[r] + bias[tb]);
+    if (fb * 32 + 32 > a.mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (fb * 32 + crow(r, hh) >= a.mt) p[r] = 0.f;
+    }
     return p;
   };
   auto rows_times_y = [&](const F (&rf)[SP::NS][NKD], int tb, f32x16 acc) -> f32x16 {
@@ -597,7 +610,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       const f32x16 zr = zrows(fb);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        const f32x16 phi = features(wfr, tb);
+        const f32x16 phi = features(wfr, tb, fb);
         const f32x16 y = rows_times_y(rf, tb, zero16());
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -625,7 +638,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       f32x16 gq[TB];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        gq[tb] = features(wfr, tb);
+        gq[tb] = features(wfr, tb, fb);
         const f32x16 y = rows_times_y(rf, tb, zero16());
 #pragma unroll
         for (int r = 0; r < 16; ++r) gq[tb][r] *= y[r] - zr[r] * ratio[tb];
@@ -666,7 +679,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       const f32x16 zr = zrows(fb);
       f32x16 gk[TB];
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) gk[tb] = features(wfr, tb);
+      for (int tb = 0; tb < TB; ++tb) gk[tb] = features(wfr, tb, fb);
       // dv^T[d][t] += dM^T phi^T: the state operand in the apply's order
       if constexpr (VPS == 8) {
 #pragma unroll
@@ -766,7 +779,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
     timing_begin(FAVOR_KERNEL_BWD_PREP, s);
     hipLaunchKernelGGL((k_bprep<Tr>), dim3(blocks), dim3(256), 0, s, t.w, b.wph, b.wpl, b.wt,
-                       Tr::VPS == 8 ? b.wtl : nullptr, nrows, D);
+                       Tr::VPS == 8 ? b.wtl : nullptr, nrows, D, p.M, p.mt);
     timing_end(FAVOR_KERNEL_BWD_PREP, s);
   }
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
@@ -781,7 +794,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   const dim3 sgrid((total + 3) / 4);
   // state M, z from K, V
   {
-    BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len};
+    BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
     hipLaunchKernelGGL((k_bred<Tr, D, false>), rgrid, dim3(256), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
@@ -793,14 +806,14 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   // query side: dQ, and the per-token scale and weight of the next reduction
   {
     BSideArgs a{t.q, t.g, b.rows_hi, b.rows_lo, nullptr, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dq, nullptr, b.lg, b.cw,
-                p.L, p.M, p.H, p.Hw, tph, total, t.eps};
+                p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_Q, s);
     hipLaunchKernelGGL((k_bside<Tr, D, true, TB>), sgrid, dim3(256), 0, s, a);
     timing_end(FAVOR_KERNEL_BWD_Q, s);
   }
   // dM, dz from Q, G
   {
-    BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len};
+    BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
     hipLaunchKernelGGL((k_bred<Tr, D, true>), rgrid, dim3(256), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
@@ -812,7 +825,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   // key side: dK, dV
   {
     BSideArgs a{t.k, t.v, b.rows_hi, b.rows_lo, b.op, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dk, t.dv, nullptr, nullptr,
-                p.L, p.M, p.H, p.Hw, tph, total, t.eps};
+                p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_K, s);
     hipLaunchKernelGGL((k_bside<Tr, D, false, TB>), sgrid, dim3(256), 0, s, a);
     timing_end(FAVOR_KERNEL_BWD_K, s);
@@ -907,6 +920,7 @@ struct BCausalArgs {
   float* acc;            // [BH][L][2D+2] sums carried between feature groups
   int L, M, H, Hw, spans, span_len, fgroups;
   float eps;
+  int mt;                // rows of W per head as given; features past them are padding, phi = 0
 };
 
 template <class Tr, int D>
@@ -1042,7 +1056,7 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
   const E* Vg = (const E*)a.v + hoff;
   const E* Gg = (const E*)a.g + hoff;
   const int hw = a.Hw == 1 ? 0 : head;
-  const float half_ln_m = 0.5f * logf((float)a.M);
+  const float half_ln_m = 0.5f * logf((float)a.mt);
   const int t0 = span * a.span_len;
   const int t1 = min(a.L, t0 + a.span_len);
   const int nch = t0 < t1 ? (t1 - t0 + C - 1) / C : 0;
@@ -1173,6 +1187,12 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
             pq[r] = exp2_fast(pq[r] + bq);
             pk[r] = exp2_fast(pk[r]);
           }
+          if (fb * 32 + 32 > a.mt) {                     // padding features: phi = 0
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (fb * 32 + crow(r, hh) >= a.mt) pq[r] = 0.f;
+            if (fb * 32 + l32 >= a.mt) pk = zero16();
+          }
           // B[j][i] = v_j . g_i for j <= i (rows j, lane i)
           f32x16 bm = zero16();
 #pragma unroll
@@ -1254,6 +1274,14 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
           for (int r = 0; r < 16; ++r) {
             pqt[r] = exp2_fast(pqt[r] + bq);
             pk[r] = exp2_fast(pk[r] + bk);
+          }
+          if (fb * 32 + 32 > a.mt) {                     // padding features: phi = 0
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (fb * 32 + crow(r, hh) >= a.mt) {
+                pqt[r] = 0.f;
+                pk[r] = 0.f;
+              }
           }
           f32x16 pq = zero16();
 #pragma unroll
@@ -1446,7 +1474,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
     const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
     timing_begin(FAVOR_KERNEL_BWD_PREP, s);
     hipLaunchKernelGGL((k_bprep<Tr>), dim3(blocks), dim3(256), 0, s, t.w, b.wph, b.wpl, b.wt,
-                       Tr::VPS == 8 ? b.wtl : nullptr, nrows, D);
+                       Tr::VPS == 8 ? b.wtl : nullptr, nrows, D, p.M, p.mt);
     timing_end(FAVOR_KERNEL_BWD_PREP, s);
   }
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
@@ -1457,10 +1485,10 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   const int fgroups = (p.M / 32 + 3) / 4;
   if (fgroups > 1 && p.boff_acc == p.btotal) return kErrPlan;   // no room for the sums
   BCausalArgs ca{t.q, t.k, t.v, t.g, b.wph, b.wpl, b.wt, b.wtl, b.part, b.partz, b.lg, b.cw, b.lg, b.cw,
-                 t.dq, nullptr, b.acc, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, fgroups, t.eps};
+                 t.dq, nullptr, b.acc, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, fgroups, t.eps, p.mt};
   // span aggregates of phi(K) V^T, phi(K) -> exclusive prefixes
   {
-    BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len};
+    BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
     hipLaunchKernelGGL((k_bred<Tr, D, false>), rgrid, dim3(256), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
@@ -1475,7 +1503,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   timing_end(FAVOR_KERNEL_BWD_Q, s);
   // span aggregates of phi'(Q) G^T, phi'(Q) c -> exclusive suffixes
   {
-    BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len};
+    BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
     hipLaunchKernelGGL((k_bred<Tr, D, true>), rgrid, dim3(256), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);

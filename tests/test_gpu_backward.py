@@ -127,6 +127,21 @@ def test_causal_backward_parity(gpu, dtype, d, m, B, H, L):
     _check(gpu, 6000 + d + m + L, B, H, L, d, m, dtype, causal=True)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d,m,L,heads_w", [
+    ("bf16", 64, 100, 300, None),
+    ("bf16", 32, 40, 130, None),
+    ("bf16", 64, 200, 257, 1),          # one W for both heads
+    ("f32", 64, 33, 129, None),
+    ("f32", 128, 250, 100, None),
+])
+def test_backward_ragged_feature_count(gpu, causal, dtype, d, m, L, heads_w):
+    """m not a multiple of 32: the padding features of the last 32-feature
+    block are zero in every backward kernel (phi of rows past m), the padded
+    W operands are zero there, and 1/sqrt(m) uses the true m."""
+    _check(gpu, 7000 + d + m + L, 1, 2, L, d, m, dtype, heads_w=heads_w, causal=causal)
+
+
 def test_causal_backward_shared_projection_and_large_eps(gpu):
     _check(gpu, 6100, 1, 3, 300, 64, 256, "bf16", heads_w=1, causal=True)
     _check(gpu, 6101, 1, 2, 200, 64, 128, "f32", eps=5.0, causal=True)
