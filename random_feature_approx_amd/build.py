@@ -63,6 +63,50 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(outdir: str) -> str:
+    """Host-only build of every source, instrumented with AddressSanitizer and
+    UndefinedBehaviorSanitizer, and the argument-checking driver
+    tests/abi_check.c linked against it.  The device code is compiled as
+    usual (the host objects register it) but never runs: the driver only
+    makes calls that are rejected before anything is launched.  Returns the
+    path of the driver executable (outdir/abi_check)."""
+    os.makedirs(outdir, exist_ok=True)
+    # each sanitizer flag goes to the host compilation only
+    san = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer"):
+        san += ["-Xarch_host", f]
+    srcs = sources()
+    objs = [os.path.join(outdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+
+    def compile_one(src, obj):
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++20", "-fPIC",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *san, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host build failed for {os.path.basename(src)}:\n{r.stderr}")
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        list(ex.map(compile_one, srcs, objs))
+    lib = os.path.join(outdir, "libfavor_host_san.so")
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, *objs, "-o", lib],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host link failed:\n{r.stderr}")
+    root = os.path.dirname(HERE)
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    exe = os.path.join(outdir, "abi_check")
+    cmd = [clang, "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-I", os.path.join(root, "include"), os.path.join(root, "tests", "abi_check.c"),
+           lib, f"-Wl,-rpath,{outdir}", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"driver build failed:\n{r.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

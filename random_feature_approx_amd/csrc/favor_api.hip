@@ -4,6 +4,7 @@
 
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -256,11 +257,37 @@ static void* scratch_address() {
 
 using namespace favor;
 
+// Enumeration arguments at the boundary.  A C caller may pass any int; C++
+// may only load values inside an enumeration's range, so every exported
+// function reads its enumeration arguments through their object
+// representation and rejects values outside the declared ones before any
+// other use.
+template <class E>
+static int enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enumerations are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+static bool dtype_ok(const favor_dtype& dt) {
+  const int v = enum_bits(dt);
+  return v == FAVOR_F32 || v == FAVOR_BF16;
+}
+static bool fmap_ok(const favor_feature_map& f) {
+  const int v = enum_bits(f);
+  return v >= FAVOR_FMAP_POSITIVE && v <= FAVOR_FMAP_TRIG;
+}
+static bool kernel_ok(const favor_kernel& k) {
+  const int v = enum_bits(k);
+  return v >= 0 && v < FAVOR_KERNEL_COUNT;
+}
+
 extern "C" {
 
 int favor_abi_version(void) { return 1; }
 
 const char* favor_status_string(favor_status s) {
+  if (enum_bits(s) < FAVOR_OK || enum_bits(s) > FAVOR_ERR_INTERNAL) return "unknown status";
   switch (s) {
     case FAVOR_OK: return "ok";
     case FAVOR_ERR_NULL: return "null pointer argument";
@@ -274,6 +301,7 @@ const char* favor_status_string(favor_status s) {
 }
 
 size_t favor_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype) {
+  if (!dtype_ok(dtype)) return 0;
   Plan p;
   if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count())) return 0;
   return p.total;
@@ -281,6 +309,8 @@ size_t favor_workspace_bytes(int B, int H, int L, int d, int m, int causal, favo
 
 size_t favor_workspace_bytes_fmap(int B, int H, int L, int d, int m, int causal, favor_feature_map fmap,
                                   favor_dtype dtype) {
+  if (!fmap_ok(fmap)) return 0;
+  if (!dtype_ok(dtype)) return 0;
   Plan p;
   if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count(), (int)fmap)) return 0;
   return p.total;
@@ -288,6 +318,8 @@ size_t favor_workspace_bytes_fmap(int B, int H, int L, int d, int m, int causal,
 
 favor_status favor_features_fmap(const void* X, const float* W, int Hw, float* Phi, int B, int H, int L, int d,
                                  int m, favor_feature_map fmap, favor_dtype dtype, void* stream) {
+  if (!fmap_ok(fmap)) return FAVOR_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   if (!X || !W || !Phi) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
   if (st != FAVOR_OK) return st;
@@ -300,6 +332,7 @@ favor_status favor_features_fmap(const void* X, const float* W, int Hw, float* P
 
 favor_status favor_features(const void* X, const float* W, int Hw, float* Phi, int B, int H, int L, int d, int m,
                             favor_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   return favor_features_fmap(X, W, Hw, Phi, B, H, L, d, m, FAVOR_FMAP_POSITIVE, dtype, stream);
 }
 
@@ -321,12 +354,14 @@ static favor_status attn_common(const void* Q, const void* K, const void* V, con
 favor_status favor_attn_noncausal(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
                                   int H, int L, int d, int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes,
                                   void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, 0, dtype, ws, ws_bytes, stream);
 }
 
 favor_status favor_attn_causal(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
                                int H, int L, int d, int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes,
                                void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, 1, dtype, ws, ws_bytes, stream);
 }
 
@@ -339,6 +374,7 @@ static void timer_free(Timer& t) {
 }
 
 size_t favor_bwd_workspace_bytes(int B, int H, int L, int d, int m, int causal, favor_dtype dtype) {
+  if (!dtype_ok(dtype)) return 0;
   Plan p;
   if (!make_plan(p, B, H, L, d, m, 1, causal, dtype, device_cu_count())) return 0;
   return p.btotal;
@@ -351,6 +387,8 @@ static size_t strided_extra(const Plan& p) { return align256((size_t)p.BH * p.L 
 
 size_t favor_workspace_bytes_strided(int B, int H, int L, int dk, int dv, int m, int causal, favor_feature_map fmap,
                                      favor_dtype dtype) {
+  if (!fmap_ok(fmap)) return 0;
+  if (!dtype_ok(dtype)) return 0;
   Plan p;
   if (dv < 1 || !make_plan(p, B, H, L, dk, m, 1, causal, dtype, device_cu_count(), (int)fmap)) return 0;
   return align256(p.total) + 4 * strided_extra(p);
@@ -365,6 +403,8 @@ favor_status favor_attn_strided(const void* Q, const long long* q_strides, const
                                 const long long* o_strides, int B, int H, int L, int dk, int dv, int m, float eps,
                                 int causal, favor_feature_map fmap, favor_dtype dtype, void* ws, size_t ws_bytes,
                                 void* stream) {
+  if (!fmap_ok(fmap)) return FAVOR_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !W || !O || !q_strides || !k_strides || !v_strides || !o_strides) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, dk, m, Hw, dtype);
   if (st != FAVOR_OK) return st;
@@ -425,6 +465,7 @@ favor_status favor_draw_projection(unsigned long long seed, int Hw, int m, int d
 
 favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, void* O, int B, int H, int L, int d,
                                 float scale, int causal, favor_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !O) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, d, 32, 1, dtype);
   if (st != FAVOR_OK) return st;
@@ -452,17 +493,20 @@ static favor_status bwd_common(const void* Q, const void* K, const void* V, cons
 favor_status favor_attn_noncausal_bwd(const void* Q, const void* K, const void* V, const float* W, int Hw,
                                       const void* dO, void* dQ, void* dK, void* dV, int B, int H, int L, int d,
                                       int m, float eps, favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   return bwd_common(Q, K, V, W, Hw, dO, dQ, dK, dV, B, H, L, d, m, eps, 0, dtype, ws, ws_bytes, stream);
 }
 
 favor_status favor_attn_causal_bwd(const void* Q, const void* K, const void* V, const float* W, int Hw,
                                    const void* dO, void* dQ, void* dK, void* dV, int B, int H, int L, int d, int m,
                                    float eps, favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   return bwd_common(Q, K, V, W, Hw, dO, dQ, dK, dV, B, H, L, d, m, eps, 1, dtype, ws, ws_bytes, stream);
 }
 
 favor_status favor_timing_start(favor_kernel k, int capacity) {
-  if ((int)k < 0 || k >= FAVOR_KERNEL_COUNT || capacity < 1) return FAVOR_ERR_SHAPE;
+  if (!kernel_ok(k)) return FAVOR_ERR_SHAPE;
+  if (capacity < 1) return FAVOR_ERR_SHAPE;
   Timer& t = g_timers[k];
   timer_free(t);
   t.ev = new hipEvent_t[2 * (size_t)capacity];
@@ -479,7 +523,7 @@ favor_status favor_timing_start(favor_kernel k, int capacity) {
 }
 
 favor_status favor_timing_stop(favor_kernel k, double* ms, int max_launches, int* launches) {
-  if ((int)k < 0 || k >= FAVOR_KERNEL_COUNT) return FAVOR_ERR_SHAPE;
+  if (!kernel_ok(k)) return FAVOR_ERR_SHAPE;
   if (!launches || (max_launches > 0 && !ms)) return FAVOR_ERR_NULL;
   Timer& t = g_timers[k];
   favor_status st = FAVOR_OK;
@@ -498,6 +542,7 @@ favor_status favor_timing_stop(favor_kernel k, double* ms, int max_launches, int
 }
 
 const char* favor_kernel_name(favor_kernel k) {
+  if (!kernel_ok(k)) return "unknown";
   switch (k) {
     case FAVOR_KERNEL_FEATURES: return "k_features";
     case FAVOR_KERNEL_REDUCE: return "k_reduce";
@@ -519,12 +564,14 @@ const char* favor_kernel_name(favor_kernel k) {
 favor_status favor_attn(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B, int H,
                         int L, int d, int m, float eps, int causal, favor_dtype dtype, void* ws, size_t ws_bytes,
                         void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, causal, dtype, ws, ws_bytes, stream);
 }
 
 favor_status favor_attn_noalloc(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O,
                                 int B, int H, int L, int d, int m, float eps, int causal, favor_dtype dtype,
                                 void* stream) {
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !W || !O) return FAVOR_ERR_NULL;
   favor_status st = check_shapes(B, H, L, d, m, Hw, dtype);
   if (st != FAVOR_OK) return st;
@@ -539,6 +586,8 @@ favor_status favor_attn_noalloc(const void* Q, const void* K, const void* V, con
 favor_status favor_attn_fmap(const void* Q, const void* K, const void* V, const float* W, int Hw, void* O, int B,
                              int H, int L, int d, int m, float eps, int causal, favor_feature_map fmap,
                              favor_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!fmap_ok(fmap)) return FAVOR_ERR_UNSUPPORTED;
+  if (!dtype_ok(dtype)) return FAVOR_ERR_UNSUPPORTED;
   return attn_common(Q, K, V, W, Hw, O, B, H, L, d, m, eps, causal, dtype, ws, ws_bytes, stream, (int)fmap);
 }
 
