@@ -20,9 +20,12 @@
  *    given: the library samples nothing and applies no 1/sqrt(d) temperature;
  *    a caller who wants one pre-scales Q and K.
  *  - dtype FAVOR_BF16: Q, K, V, X and O are bfloat16.  The projection x W^T
- *    runs on fp16 matrix-core operands: x is converted exactly (|x| must stay
- *    below 65504; magnitudes under 2^-14 keep an absolute error below
- *    2^-25) and W log2(e) is rounded to fp16 (nearest even).  Features phi
+ *    runs on fp16 matrix-core operands: x is converted exactly (magnitudes
+ *    under 2^-14 keep an absolute error below 2^-25; entries past fp16's
+ *    65504 saturate there, and since the row bias -|x|^2/2 is taken from
+ *    the unsaturated values, FAVOR+ features of such rows come out 0, as in
+ *    exact arithmetic; the other feature maps see the saturated entries) and
+ *    W log2(e) is rounded to fp16 (nearest even).  Features phi
  *    and the m x d states enter the other products as bf16 (nearest even);
  *    every product accumulates in float32, and states and sums are float32.
  *    FAVOR_F32: float32 storage, sums and states; products on the float32

@@ -176,10 +176,14 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
     // below that every feature underflows to zero in float32 anyway unless
     // |w| exceeds ~200)
     const float bqh = (float)(_Float16)fmaxf(bq, -65504.f), bkh = (float)(_Float16)fmaxf(bk, -65504.f);
-    // bitwise selects: computed for every lane, so no branch is formed
-    const unsigned mv = 0u - (unsigned)valid;                          // all ones: valid row
-    const unsigned cq = (pack_f16(bqh, fmaxf(bq - bqh, -65504.f)) & mv) | (0xFC00u & ~mv);   // pad: -inf, 0
-    const unsigned ck = (pack_f16(bkh, fmaxf(bk - bkh, -65504.f)) & mv) | (0xFC00u & ~mv);
+    // bitwise selects: computed for every lane, so no branch is formed.
+    // Rows with |x|^2 > 2^20 (entries may have saturated at the fp16 range)
+    // take the padding rows' -inf as well: their features are exactly what
+    // float32 gives, zero, whenever every row of W is shorter than 256.
+    const unsigned mvq = 0u - (unsigned)(valid && !(ssq > 1048576.f));   // all ones: a real row
+    const unsigned mvk = 0u - (unsigned)(valid && !(ssk > 1048576.f));
+    const unsigned cq = (pack_f16(bqh, fmaxf(bq - bqh, -65504.f)) & mvq) | (0xFC00u & ~mvq);   // pad: -inf, 0
+    const unsigned ck = (pack_f16(bkh, fmaxf(bk - bkh, -65504.f)) & mvk) | (0xFC00u & ~mvk);
     const unsigned m0 = scc == 0 ? ~0u : 0u, m1 = scc <= 1 ? ~0u : 0u;  // bias chunk / bias or zero chunk
     const int boff = scc <= 1 ? D * 2 + scc * 16 : scc * 16;
     *(u32x4*)(buf + LY::kQh + srow * RSX + boff) =

@@ -70,10 +70,18 @@ __device__ __forceinline__ unsigned as_u32(float x) { return __builtin_bit_cast(
 __device__ __forceinline__ float bf16_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 
+// Two floats as fp16 (nearest even), saturated at +-65504 rather than
+// rounded to infinity: an input row of the projection with entries past
+// fp16's range keeps a finite projection, and its float32 row bias
+// -|x|^2/2 (taken from the unsaturated values) sends FAVOR+ features to 0.
+__device__ __forceinline__ unsigned pack_f16_sat(float lo, float hi) {
+  return pack_f16(__builtin_amdgcn_fmed3f(lo, -65504.f, 65504.f), __builtin_amdgcn_fmed3f(hi, -65504.f, 65504.f));
+}
+
 // A dword of two bf16 values re-encoded as two fp16 values.  Exact for
 // magnitudes in fp16's normal range [2^-14, 65504]; smaller values keep an
-// absolute error below 2^-25.
-__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned u) { return pack_f16(bf16_lo(u), bf16_hi(u)); }
+// absolute error below 2^-25; larger ones saturate at +-65504.
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned u) { return pack_f16_sat(bf16_lo(u), bf16_hi(u)); }
 
 // Sum of the two bf16 halves of a dword plus acc (exact products with 1.0).
 __device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float acc) {

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
           const float lo = bf16_lo(v[j]), hi = bf16_hi(v[j]);
           ss = fmaf(lo, lo, ss);
           ss = fmaf(hi, hi, ss);
-          v[j] = pack_f16(lo, hi);
+          v[j] = pack_f16_sat(lo, hi);
         } else {
           const float x = as_f32(v[j]);
           ss = fmaf(x, x, ss);

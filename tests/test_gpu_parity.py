@@ -294,6 +294,31 @@ def test_causal_many_spans(gpu, dtype, d, m, monkeypatch):
     assert row_rel_err(out, _ref(x, True)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 64, 256), ("bf16", 32, 256), ("bf16", 64, 96), ("bf16", 128, 256),
+                                     ("f32", 128, 256)])
+def test_entries_beyond_fp16_range(gpu, causal, dtype, d, m):
+    """Query and key rows with one entry of 3e5, past fp16's 65504 (the
+    projection's operand type for bf16): their FAVOR+ features
+    exp(w.x - |x|^2/2)/sqrt(m) are 0 in float64 as well, so such a query row's
+    output is exactly 0 and such a key adds nothing; every other row matches
+    the oracle."""
+    L = 300
+    x = synth.random_case(4300 + d + m, 1, 2, L, d, m, dtype)
+    rows_q, rows_k = [5, 77, L - 1], [10, 150]
+    for name, rows in (("q", rows_q), ("k", rows_k)):
+        arr = x[name + "64"].copy()
+        arr[0, :, rows, 3] = 3e5
+        x[name] = synth.bf16_round(arr.astype(np.float32)) if dtype == "bf16" else arr.astype(np.float32)
+        x[name + "64"] = synth.as_f64(x[name], dtype)
+    out = _run_attn(gpu, x, dtype, causal=causal)
+    ref = _ref(x, causal)
+    assert np.all(ref[0, :, rows_q] == 0)
+    assert np.all(out[0, :, rows_q] == 0), out[0, :, rows_q]
+    keep = np.setdiff1d(np.arange(L), rows_q)
+    assert row_rel_err(out[:, :, keep], ref[:, :, keep]) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_noncausal_key_value_permutation_invariance(gpu, dtype):
     """Non-causal attention sums over keys: permuting the rows of K and V
