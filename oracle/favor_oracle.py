@@ -46,16 +46,17 @@ def favor_features(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     """Positive random features, phi(x) = exp(-|x|^2/2) / sqrt(m) *
     [exp(omega_1 . x), ..., exp(omega_m . x)].
 
-    Follows the feature-map equation of P1 (and P3 section 4): the projection
-    x W^T, minus half the squared norm of x, exponentiated, divided by sqrt(m).
-    x: (..., d), w: (m, d).  Returns (..., m) float64.
+    Written in the general form of P3 section 4 (and P1's feature-map
+    equation), phi(x) = h(x)/sqrt(m) (f(omega_1 . x), ..., f(omega_m . x))
+    with h(x) = exp(-|x|^2/2) and f = exp, evaluated in the log domain so
+    that h and f never overflow separately: log phi_i = log h(x) +
+    omega_i . x - log(m)/2.  x: (..., d), w: (m, d).  Returns (..., m) float64.
     """
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
-    m = w.shape[0]
-    proj = x @ w.T
-    half_sq_norm = 0.5 * np.sum(x * x, axis=-1, keepdims=True)
-    return np.exp(proj - half_sq_norm) / np.sqrt(m)
+    log_h = -0.5 * np.einsum("...d,...d->...", x, x)            # log h(x)
+    log_f = np.einsum("...d,md->...m", x, w)                    # log f(omega_i . x) = omega_i . x
+    return np.exp(log_h[..., None] + log_f - 0.5 * np.log(w.shape[0]))
 
 
 FEATURE_MAPS = ("positive", "elu1", "relu", "trig")
@@ -111,18 +112,18 @@ def attn_quadratic(q, k, v, w, eps: float = 1e-6, causal: bool = False, kind: st
 
 
 def attn_noncausal(q, k, v, w, eps: float = 1e-6, kind: str = "positive") -> np.ndarray:
-    """Reassociated non-causal attention, in the order of P1 In[25] and the
-    right-hand side of P2's 换顺序 diagram: first the m x d state
-    M = phi(K)^T V and the key sum z = phi(K)^T 1, then
-    O = (phi(Q) M) / (phi(Q) z + eps)."""
+    """Reassociated non-causal attention, the right-hand side of P2's 换顺序
+    diagram: phi(K)^T is contracted once with the values augmented by a
+    column of ones, [V | 1], giving the m x (d+1) block [M | z] (the state
+    M = phi(K)^T V and the key sum z = phi(K)^T 1 of P2's key points); then
+    phi(Q) [M | z] holds the numerators in its first d columns and the
+    normaliser phi(Q) z in its last, and O = numerator / (normaliser + eps)."""
     fq = feature_map(q, w, kind)
     fk = feature_map(k, w, kind)
     v = np.asarray(v, dtype=np.float64)
-    state = fk.T @ v
-    key_sum = fk.sum(axis=0)
-    num = fq @ state
-    den = fq @ key_sum + eps
-    return num / den[:, None]
+    v_aug = np.concatenate([v, np.ones((v.shape[0], 1))], axis=1)      # [V | 1]
+    r = fq @ (fk.T @ v_aug)                                           # phi(Q) [M | z]
+    return r[:, :-1] / (r[:, -1:] + eps)
 
 
 def attn_causal(q, k, v, w, eps: float = 1e-6, kind: str = "positive") -> np.ndarray:
