@@ -41,7 +41,10 @@ METRIC = "FAVOR+ fwd tokens/sec (B·H·L/s) causal & non-causal; % of MFMA/HBM r
 PEAK_HBM_GBS = 8000.0                      # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks
 KERNEL_SOURCES = ["favor_device.hpp", "favor_tiles.hpp", "favor_nc.hip", "favor_causal.hip",
-                  "favor_causal3.hip"]   # forward kernels
+                  "favor_causal3.hip", "favor_x3.hip"]   # forward kernels
+SPLIT_ARITHMETIC = ("float32 storage, sums and states; each product as three 16-bit matrix-core products "
+                    "(hi*hi + hi*lo + lo*hi of fp16 halves for the projection, bf16 halves elsewhere), "
+                    "float32 accumulation")
 BWD_KERNELS = ["k_bprep", "k_bred", "k_bcombine", "k_bside_q", "k_bside_k"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -100,27 +103,45 @@ def algorithmic(kernel: str, path: str, wl) -> dict:
     return {"bytes": 0, "flops": 0}
 
 
+def split_products(wl, path: str, kernel: str) -> bool:
+    """True for the kernels the library runs on split 16-bit products: the
+    causal scan and its span sums for float32 FAVOR+ at d = 128, unless
+    FAVOR_F32_MFMA=1 selects float32 products."""
+    forced = int(os.environ.get("FAVOR_F32_MFMA", "0") or 0) > 0
+    return (wl.dtype == "f32" and wl.d == 128 and path == "causal" and kernel in ("k_causal", "k_reduce")
+            and not forced)
+
+
 def roofline_entry(kernel: str, path: str, wl, avg_ms: float, traffic) -> dict:
     a = algorithmic(kernel, path, wl)
     t = avg_ms * 1e-3
-    peak_mfma = PEAK_MFMA_TFLOPS[wl.dtype]
-    intensity = a["flops"] / a["bytes"] if a["bytes"] else float("inf")
+    split = split_products(wl, path, kernel)
+    # split products: the matrix cores execute three bf16/fp16 products per
+    # float32 one, against the bf16 dense peak
+    peak_mfma = PEAK_MFMA_TFLOPS["bf16" if split else wl.dtype]
+    executed = 3 * a["flops"] if split else a["flops"]
+    intensity = executed / a["bytes"] if a["bytes"] else float("inf")
     ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
     if intensity <= ridge:
         achieved = a["bytes"] / t / 1e9
         entry = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
-        achieved = a["flops"] / t / 1e12
+        achieved = executed / t / 1e12
         entry = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_mfma, "unit": "TFLOP/s",
                  "frac": round(achieved / peak_mfma, 4)}
+    if split:
+        entry["arithmetic"] = "split: 3 bf16/fp16 products per float32 product"
+        entry["executed_flops_per_launch"] = executed
+        entry["f32_equivalent_tflops"] = round(a["flops"] / t / 1e12, 2)
+        entry["f32_equivalent_frac"] = round(a["flops"] / t / 1e12 / PEAK_MFMA_TFLOPS["f32"], 4)
     entry["traffic"] = traffic
     entry["kernel"] = kernel
     entry["path"] = path
     entry["avg_launch_ms"] = round(avg_ms, 5)
     entry["alg_bytes_per_launch"] = a["bytes"]
     entry["alg_flops_per_launch"] = a["flops"]
-    entry["mfma_frac_alg"] = round(a["flops"] / t / 1e12 / peak_mfma, 4)
+    entry["mfma_frac_alg"] = round(executed / t / 1e12 / peak_mfma, 4)
     entry["hbm_frac_alg"] = round(a["bytes"] / t / 1e9 / PEAK_HBM_GBS, 4)
     return entry
 
@@ -439,8 +460,11 @@ def main() -> int:
                                          f"m={other.m} {other.dtype}, {' + '.join(other.paths)}",
                              "ms_per_step": r["ms_per_step"],
                              "tokens_per_s": round(other.tokens / (r["ms_per_step"] * 1e-3), 1),
+                             "dtype": other.dtype,
                              "steps": args.config_steps, "paths": r["paths"], "roofline": r["roofline"],
                              "kernels": r["kernels"]}
+            if any(split_products(other, p, "k_causal") for p in other.paths):
+                configs[name]["arithmetic"] = SPLIT_ARITHMETIC
             if name == "t1":
                 configs[name]["latency_ms"] = r["ms_per_step"]
             torch.cuda.empty_cache()

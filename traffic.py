@@ -98,7 +98,7 @@ def main() -> int:
         for c in COUNTERS:
             rows, cmd = run_pass(c, os.path.join(args.out, f"{wl.name}_{path}_{c}_{stamp}"),
                                  [bench_py, "--workload", wl.name, "--paths", path, "--steps", "3", "--warmup", "1", "--no-backward", "--no-fmaps",
-                                  "--cpu-seconds", "0"], run)
+                                  "--no-configs", "--settle-ms", "0", "--cpu-seconds", "0"], run)
             commands.append(cmd)
             acc = {}
             for r in rows:
