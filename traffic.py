@@ -78,6 +78,7 @@ def main() -> int:
     args = ap.parse_args()
     wl = synth.WORKLOADS[args.workload]
     bench_py = os.path.join(ROOT, "bench.py")
+    args.out = os.path.abspath(args.out)      # rocprofv3 runs from /tmp
     stamp = args.resummarise or time.strftime("%Y%m%d-%H%M%S")
     run = args.resummarise is None
 
