@@ -26,18 +26,20 @@ def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
-def grad_err(out: np.ndarray, ref: np.ndarray, floor_frac: float = 2.0 ** -7) -> float:
-    """Per-row infinity-norm error of a gradient, relative to the row's own
-    infinity norm or, for rows smaller than floor_frac times the largest row
-    of their head, to that floor.  Such small rows are differences of nearly
-    equal terms (the first causal query's dq is proportional to eps, its
-    terms are of ordinary size): their error scales with the terms, not with
-    the result, at any float precision.  Leading axes other than the last
-    two are heads."""
+def grad_err(out: np.ndarray, ref: np.ndarray, floored: bool = False, floor_frac: float = 2.0 ** -7) -> float:
+    """Per-row infinity-norm error of a gradient relative to the row's own
+    infinity norm, or (floored=True, used for dQ) relative to max(own norm,
+    floor_frac times the largest row of its head).  dq_i is formed from the
+    per-feature difference y - z s_i/D_i, which nearly cancels in some rows
+    (the first causal query's dq is proportional to eps: its one key gives
+    o_0 = v_0 a/(a + eps)); in such a row the error scales with the terms,
+    not with the result, at any float precision.  dK and dV are held to
+    their own size row by row.  Leading axes other than the last two are
+    heads."""
     num = np.abs(out - ref).max(axis=-1)
     row = np.abs(ref).max(axis=-1)
-    floor = floor_frac * row.max(axis=-1, keepdims=True)
-    return float((num / np.maximum(row, floor)).max())
+    den = np.maximum(row, floor_frac * row.max(axis=-1, keepdims=True)) if floored else row
+    return float((num / den).max())
 
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}

@@ -2,8 +2,9 @@
 Q, K, V) against the float64 oracle's gradients on the same seeded inputs,
 W and upstream gradient G, with the tolerances of the forward (1e-4
 float32, 2e-2 bfloat16) on the per-row metric of _util.grad_err: each row
-relative to its own size, rows below 1/128 of their head's largest row
-relative to that floor (see grad_err for why)."""
+relative to its own size, except that dQ rows smaller than 1/128 of their
+head's largest row are measured against that floor (dQ is formed from a
+per-feature difference that nearly cancels in some rows; see grad_err)."""
 import numpy as np
 import pytest
 
@@ -31,9 +32,9 @@ def _check(gpu, seed, B, H, L, d, m, dtype, heads_w=None, eps=1e-6, causal=False
     torch.cuda.synchronize()
     fn = oracle.attn_causal_grad if causal else oracle.attn_noncausal_grad
     ref = oracle.per_head_grad(fn, x["q64"], x["k64"], x["v64"], x["w64"], g64, eps=eps)
-    errs = [grad_err(to_f64(t), r) for t, r in zip((dq, dk, dv), ref)]
+    errs = [grad_err(to_f64(t), r, floored=name == "dq") for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref)]
     strict = [row_rel_err(to_f64(t), r) for t, r in zip((dq, dk, dv), ref)]
-    print(f"[bwd]   floor-metric {errs}  per-row {strict}", flush=True)
+    print(f"[bwd]   metric {errs}  strict per-row {strict}", flush=True)
     assert max(errs) <= TOL[dtype], dict(zip(("dq", "dk", "dv"), errs))
     return errs
 
@@ -101,8 +102,9 @@ def test_noncausal_backward_long_sampled(gpu):
     for h in (0, wl.H - 1):
         q64, k64, v64, g64 = (synth.as_f64(a[0, h], "bf16") for a in (x["q"], x["k"], x["v"], g))
         ref = oracle.attn_noncausal_grad(q64, k64, v64, x["w64"][h], g64, wl.eps)
-        errs = [grad_err(to_f64(t[0, h]), r) for t, r in zip((dq, dk, dv), ref)]
-        print(f"[bwd]   floor-metric {errs}", flush=True)
+        errs = [grad_err(to_f64(t[0, h]), r, floored=name == "dq")
+                for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref)]
+        print(f"[bwd]   metric {errs}", flush=True)
         assert max(errs) <= TOL["bf16"]
 
 
@@ -176,6 +178,7 @@ def test_causal_backward_long_full_heads(gpu):
         print(f"[bwd] long causal head {h}", flush=True)
         q64, k64, v64, g64 = (synth.as_f64(a[0, h], "bf16") for a in (x["q"], x["k"], x["v"], g))
         ref = oracle.attn_causal_grad(q64, k64, v64, x["w64"][h], g64, wl.eps)
-        errs = [grad_err(to_f64(t[0, h]), r) for t, r in zip((dq, dk, dv), ref)]
-        print(f"[bwd]   floor-metric {errs}", flush=True)
+        errs = [grad_err(to_f64(t[0, h]), r, floored=name == "dq")
+                for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref)]
+        print(f"[bwd]   metric {errs}", flush=True)
         assert max(errs) <= TOL["bf16"]
