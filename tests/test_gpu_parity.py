@@ -283,6 +283,18 @@ def test_causal_independent_of_span_count(gpu, dtype, d, m, monkeypatch):
         assert row_rel_err(out, outs[0]) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("f32_mfma", ["0", "1"])
+def test_float32_causal_both_product_forms(gpu, f32_mfma, monkeypatch):
+    """Float32 FAVOR+ causal at d = 128 runs on split 16-bit products by
+    default and on float32 products with FAVOR_F32_MFMA=1; both match the
+    oracle at the float32 tolerance, on several spans and feature groups."""
+    monkeypatch.setenv("FAVOR_F32_MFMA", f32_mfma)
+    x = synth.random_case(4170, 1, 3, 1500, 128, 384, "f32")
+    out = _run_attn(gpu, x, "f32", causal=True)
+    monkeypatch.delenv("FAVOR_F32_MFMA")
+    assert row_rel_err(out, _ref(x, True)) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("dtype,d,m", [("bf16", 64, 256), ("f32", 128, 256)])
 def test_causal_many_spans(gpu, dtype, d, m, monkeypatch):
     """More than 16 spans per head take the two-level prefix scan (groups of
