@@ -31,9 +31,24 @@ def test_roofline_bound_follows_the_ridge_point():
     assert e["bound"] == "hbm" and e["unit"] == "GB/s"
     assert e["achieved"] == pytest.approx(4 * 64 * 2 * 524288 / 1e-4 / 1e9, rel=1e-3)
     assert e["frac"] == pytest.approx(e["achieved"] / 8000.0, rel=1e-3)
-    # float32 wide state: 256 flops per byte against a ridge of 157.3/8 -> MFMA-bound
+    # float32 wide causal scan on split 16-bit products: three products per
+    # float32 product, 768 executed flops per byte against the bf16 ridge
+    # 312.5 -> MFMA-bound at the bf16 peak, with the float32-equivalent rate
+    wl = synth.WORKLOADS["wide"]
+    flops = bench.algorithmic("k_causal", "causal", wl)["flops"]
+    e = bench.roofline_entry("k_causal", "causal", wl, 30.0, None)
+    assert e["bound"] == "mfma" and e["peak"] == 2500.0 and e["unit"] == "TFLOP/s"
+    assert e["executed_flops_per_launch"] == 3 * flops
+    assert e["achieved"] == pytest.approx(3 * flops / 30e-3 / 1e12, rel=1e-2)
+    assert e["f32_equivalent_frac"] == pytest.approx(flops / 30e-3 / 1e12 / 157.3, rel=1e-2)
+
+
+def test_roofline_of_float32_products(monkeypatch):
+    # FAVOR_F32_MFMA=1: float32 products, 256 flops per byte against the
+    # float32 ridge 157.3/8 -> MFMA-bound at the float32 peak
+    monkeypatch.setenv("FAVOR_F32_MFMA", "1")
     e = bench.roofline_entry("k_causal", "causal", synth.WORKLOADS["wide"], 30.0, None)
-    assert e["bound"] == "mfma" and e["peak"] == 157.3
+    assert e["bound"] == "mfma" and e["peak"] == 157.3 and "arithmetic" not in e
 
 
 def test_source_hash_covers_the_forward_kernels():
