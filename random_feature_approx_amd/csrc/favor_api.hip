@@ -91,8 +91,10 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   // run as a second, mostly empty round
   int splits = target / per_head;
   const int max_splits = (L + 255) / 256;
-  // the causal backward keeps two span workgroups per compute unit
-  int bwd_splits = (2 * num_cus) / per_head;
+  // the causal backward's query walks run one span workgroup of eight waves
+  // per compute unit (bf16, d <= 64) or two of four waves
+  p.bqnw = (dt == FAVOR_BF16 && d <= 64) ? 8 : 4;
+  int bwd_splits = ((p.bqnw == 8 ? 1 : 2) * num_cus) / per_head;
   // FAVOR_SPANS (testing and tuning): the number of causal spans per head
   if (causal) {
     const char* env = getenv("FAVOR_SPANS");

@@ -864,7 +864,8 @@ hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t 
 //   R_j = sum_{i>=j} phi(q_i) g_i^T / D_i,  r_j = sum_{i>=j} phi(q_i) c_i / D_i,
 //   c_i = -s_i/D_i,  dv_j = R_j^T phi(k_j),  dphi(k_j) = R_j v_j + r_j.
 // Both sides walk 32-token chunks of a span (one workgroup per span and
-// head, four waves, one 32-feature block per wave, feature groups in turn),
+// head, one 32-feature block per wave -- eight waves for the bf16 query walks
+// at d <= 64, four otherwise -- feature groups in turn),
 // starting from the span's exclusive prefix (query side) or suffix (key side)
 // of the span aggregates.  Inside a chunk the masked token-by-token terms are
 // matrix products with the chunk's 32 x 32 score-like tiles.  The query side
@@ -923,7 +924,7 @@ struct BCausalArgs {
   int mt;                // rows of W per head as given; features past them are padding, phi = 0
 };
 
-template <class Tr, int D>
+template <class Tr, int D, int NW>
 struct BCLds {
   using E = typename Tr::elem;
   static constexpr int C = 32;
@@ -932,9 +933,9 @@ struct BCLds {
   static constexpr int kQ = 0, kK = C * RS, kV = 2 * C * RS, kG = 3 * C * RS;
   static constexpr int kBq = 4 * C * RS, kBk = kBq + C * 4, kC = kBk + C * 4;
   static constexpr int kZ = kC + C * 4;                 // per wave: 32 floats (z or r of its features)
-  static constexpr int kRed = kZ + 4 * 32 * 4;          // per wave: C x RSR floats
-  static constexpr int kRedS = kRed + 4 * C * RSR * 4;  // per wave: C x 2 floats
-  static constexpr int kTotal = kRedS + 4 * C * 2 * 4;
+  static constexpr int kRed = kZ + NW * 32 * 4;         // per wave: C x RSR floats
+  static constexpr int kRedS = kRed + NW * C * RSR * 4; // per wave: C x 2 floats
+  static constexpr int kTotal = kRedS + NW * C * 2 * 4;
 };
 
 // B operand over d in c-row order (k-step s2 of d block db) from one row of
@@ -1013,17 +1014,24 @@ constexpr int kQ1 = 0, kQ2 = 1, kK = 2;
 
 // Two waves per SIMD for the bf16 query walks at d <= 64 (the second walk
 // spills a few registers and runs 30% faster than at one wave), one for the
-// key walk, whose state would spill inside the chunk loop.
+// key walk, whose state would spill inside the chunk loop.  NW waves per
+// workgroup, each owning one 32-feature block: the bf16 query walks at
+// d <= 64 run eight (one workgroup per compute unit, all 256 features of
+// m = 256 in one walk, so nothing is carried between feature groups), the
+// others four.
 template <class Tr, int D, int MODE>
 constexpr int bcausal_waves() { return (Tr::VPS == 8 && D <= 64 && MODE != kK) ? 2 : 1; }
-
 template <class Tr, int D, int MODE>
-__global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal(BCausalArgs a) {
+constexpr int bcausal_nw() { return (Tr::VPS == 8 && D <= 64 && MODE != kK) ? 8 : 4; }
+
+template <class Tr, int D, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bcausal(BCausalArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
   using SP = Bw<Tr>;
-  using LY = BCLds<Tr, D>;
+  using LY = BCLds<Tr, D, NW>;
   constexpr bool QSIDE = MODE != kK;
+  constexpr int NT = NW * 64;
   constexpr int C = LY::C;
   constexpr int NKD = D / Tr::KS;
   constexpr int NDB = D / 32;
@@ -1081,7 +1089,7 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
   };
 
   for (int fg = 0; fg < a.fgroups; ++fg) {
-    const int fb = fg * 4 + w;
+    const int fb = fg * NW + w;
     const bool valid = fb < nfb;
     const int fbs = valid ? fb : 0;
     // projection operand of this wave's block (lane = feature)
@@ -1115,7 +1123,7 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
     float zreg = valid ? a.prez[((size_t)bh * a.spans + span) * a.M + fbs * 32 + l32] : 0.f;
     sZ[l32] = zreg;
 
-    TileLoader<E, D, C, 256> lq, lk, lv, lg_;
+    TileLoader<E, D, C, NT> lq, lk, lv, lg_;
     auto chunk0 = [&](int ci) { return t0 + ci * C; };
     auto prefetch = [&](int ci) {
       const int c0 = chunk0(ci);
@@ -1367,7 +1375,9 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
       // carried sums per token: [0, D) first output, [D, 2D) second, 2D and
       // 2D+1 the two scalars
       float* accrow = a.acc + ((size_t)bh * a.L + c0) * AW;
-      const int tq = tid >> 3, d0 = (tid & 7) * DP;
+      // threads 0..255: eight per token of the chunk
+      const bool rt = tid < 8 * C;
+      const int tq = rt ? tid >> 3 : 0, d0 = (tid & 7) * DP;
       constexpr int NROUND = MODE == kQ1 ? 0 : (MODE == kQ2 ? 1 : 2);
       float v1[DP], v2[DP], sc1 = 0.f, sc2 = 0.f;
       {
@@ -1392,7 +1402,7 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
 #pragma unroll
         for (int j = 0; j < DP; ++j) vv[j] = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < NW; ++ww) {
           const float* src = sRed + (size_t)ww * C * RSR + tq * RSR + d0;
 #pragma unroll
           for (int j = 0; j < DP; j += 4) {
@@ -1403,7 +1413,7 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
             vv[j + 3] += x[3];
           }
         }
-        if (a.fgroups > 1 && tq < nv) {
+        if (a.fgroups > 1 && rt && tq < nv) {
           float* ar = accrow + (size_t)tq * AW + round * D + d0;
           if (fg > 0) {
 #pragma unroll
@@ -1418,11 +1428,11 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
       }
       if constexpr (NROUND == 0) __syncthreads();        // the scalars are in LDS
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         sc1 += sRedS[(ww * C + tq) * 2];
         sc2 += sRedS[(ww * C + tq) * 2 + 1];
       }
-      if (a.fgroups > 1 && tq < nv && MODE != kQ2) {
+      if (a.fgroups > 1 && rt && tq < nv && MODE != kQ2) {
         float* as = accrow + (size_t)tq * AW + 2 * D;
         if (fg > 0) {
           sc1 += as[0];
@@ -1433,7 +1443,7 @@ __global__ __launch_bounds__(256, (bcausal_waves<Tr, D, MODE>())) void k_bcausal
           as[1] = sc2;
         }
       }
-      if (fg + 1 == a.fgroups && tq < nv) {
+      if (fg + 1 == a.fgroups && rt && tq < nv) {
         const size_t tok = (size_t)c0 + tq;
         if constexpr (MODE == kQ1) {
           if ((tid & 7) == 0) {
@@ -1481,11 +1491,14 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   const size_t rlds = BRedLds<Tr, D>::kTotal;
   const int nq = (p.M * D + p.M) / 4;
   const dim3 sgrid((nq + 255) / 256, p.BH);
-  const size_t clds = BCLds<Tr, D>::kTotal;
-  const int fgroups = (p.M / 32 + 3) / 4;
-  if (fgroups > 1 && p.boff_acc == p.btotal) return kErrPlan;   // no room for the sums
+  constexpr int NWQ = bcausal_nw<Tr, D, kQ1>(), NWK = bcausal_nw<Tr, D, kK>();
+  static_assert(bcausal_nw<Tr, D, kQ2>() == NWQ, "one wave count for both query walks");
+  const int nfb = p.M / 32;
+  const int fgq = (nfb + NWQ - 1) / NWQ, fgk = (nfb + NWK - 1) / NWK;
+  if ((fgq > 1 || fgk > 1) && p.boff_acc == p.btotal) return kErrPlan;   // no room for the sums
+  if (p.bqnw != NWQ) return kErrPlan;
   BCausalArgs ca{t.q, t.k, t.v, t.g, b.wph, b.wpl, b.wt, b.wtl, b.part, b.partz, b.lg, b.cw, b.lg, b.cw,
-                 t.dq, nullptr, b.acc, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, fgroups, t.eps, p.mt};
+                 t.dq, nullptr, b.acc, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, fgq, t.eps, p.mt};
   // span aggregates of phi(K) V^T, phi(K) -> exclusive prefixes
   {
     BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
@@ -1498,8 +1511,9 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   }
   // query side: log2 D_i and c_i (the lg and cw arrays), then dQ
   timing_begin(FAVOR_KERNEL_BWD_Q, s);
-  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ1>), dim3(p.bsplits, p.BH), dim3(256), clds, s, ca);
-  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ2>), dim3(p.bsplits, p.BH), dim3(256), clds, s, ca);
+  const size_t qlds = BCLds<Tr, D, NWQ>::kTotal;
+  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ1, NWQ>), dim3(p.bsplits, p.BH), dim3(NWQ * 64), qlds, s, ca);
+  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ2, NWQ>), dim3(p.bsplits, p.BH), dim3(NWQ * 64), qlds, s, ca);
   timing_end(FAVOR_KERNEL_BWD_Q, s);
   // span aggregates of phi'(Q) G^T, phi'(Q) c -> exclusive suffixes
   {
@@ -1514,8 +1528,10 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   // key side
   ca.dx = t.dk;
   ca.dy = t.dv;
+  ca.fgroups = fgk;
+  const size_t klds = BCLds<Tr, D, NWK>::kTotal;
   timing_begin(FAVOR_KERNEL_BWD_K, s);
-  hipLaunchKernelGGL((k_bcausal<Tr, D, kK>), dim3(p.bsplits, p.BH), dim3(256), clds, s, ca);
+  hipLaunchKernelGGL((k_bcausal<Tr, D, kK, NWK>), dim3(p.bsplits, p.BH), dim3(NWK * 64), klds, s, ca);
   timing_end(FAVOR_KERNEL_BWD_K, s);
   return hipGetLastError();
 }

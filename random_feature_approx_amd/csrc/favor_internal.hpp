@@ -47,6 +47,7 @@ struct Plan {
   // backward pass: its reductions (4 waves of one feature block each) and
   // its workspace (a separate layout, sized by favor_bwd_workspace_bytes)
   int bsplits, bsplit_len, bfgroups;
+  int bqnw;              // causal backward: waves of a query-walk workgroup
   size_t boff_part, boff_partz, boff_zf, boff_lg, boff_cw, boff_wph, boff_wpl, boff_wt, boff_wtl, boff_rows_hi,
       boff_rows_lo, boff_op, boff_acc, btotal;
 };
