@@ -89,6 +89,8 @@ struct RedArgs {
   int L, M, H, Hw, splits, split_len;
   int Mw;        // feature rows per head (M, or M/2 for the trig map), a multiple of 32
   int mt;        // rows of W per head as given; features of rows >= mt are padding, set to 0
+  void* wp;      // non-causal: the apply's projection operand, written by the split-0
+                 // workgroups from the W fragments they load (nullptr: not written)
 };
 
 // Arguments of the causal chunk scans (k_causal, k_causal2, k_causal_x3).
@@ -132,7 +134,9 @@ hipError_t launch_noncausal_bwd(const Plan& p, const BwdTensors& t, hipStream_t 
 hipError_t launch_causal_bwd(const Plan& p, const BwdTensors& t, hipStream_t s);
 // nsplit: how many token ranges to reduce (the first nsplit of p.splits;
 // -1: all).  The causal scans never read the last span's aggregate.
+// wp: non-causal only, the apply's projection operand (written by the
+// reduction; nullptr for the causal span aggregates)
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                         hipStream_t s, int nsplit = -1);
+                         hipStream_t s, int nsplit = -1, void* wp = nullptr);
 
 }  // namespace favor

@@ -177,6 +177,32 @@ __global__ __launch_bounds__(NW * 64) void k_reduce(RedArgs a) {
 #pragma unroll
     for (int s = 0; s < NKD; ++s) wf[i][s] = w_frag<Tr, D, FM>(wrow, hh, s, wok[i]);
   }
+  // Non-causal: these fragments are also the apply's projection operand, in
+  // its operand order [Hw*M/32 feature blocks][k-group g][lane half h][feature
+  // f][16 bytes] (lane (f, h) of k-group g holds d = (D/2) h + (16/size) g + 0..,
+  // the d-major k order of the projection; rows of W past mt are zero); the
+  // first split's workgroup of each head stores them.
+  if (a.wp != nullptr && split == 0 && (a.Hw == 1 ? bh == 0 : bh < a.H)) {
+    constexpr int NKG = Tr::VPS == 8 ? NKD : NKD / 4;   // 16-byte chunks per lane and block
+    const size_t hw = a.Hw == 1 ? 0 : head;
+#pragma unroll
+    for (int i = 0; i < FBW; ++i) {
+      if (fb0 + i < nfb) {
+        const size_t blk = hw * nfb + fb0 + i;
+#pragma unroll
+        for (int g = 0; g < NKG; ++g) {
+          u32x4 c;
+          if constexpr (Tr::VPS == 8) {
+            c = wf[i][g];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = as_u32(wf[i][4 * g + j]);
+          }
+          ((u32x4*)a.wp)[((blk * NKG + g) * 2 + hh) * 32 + l32] = c;
+        }
+      }
+    }
+  }
   f32x16 st[FBW][NDB];
   float zs[FBW];
 #pragma unroll
@@ -393,57 +419,21 @@ struct OperandOrder {
 };
 
 // The m*d + m values of a head's state are handled in quads of 4 floats;
-// a block is kSplitGroups groups of threads, group g summing splits
-// [g*per, (g+1)*per) of its quad in order, and the groups' sums are added in
-// group order.
-constexpr int kSplitGroups = 8;
-constexpr int kQuadsPerBlock = 256 / kSplitGroups;
+// a block is NG groups of threads, group g summing splits [g*per, (g+1)*per)
+// of its quad in order (per = ceil(splits / NG)), and the groups' sums are
+// added in group order.  NG grows with the split count (1 up to 8 splits, 8
+// from 33 on), so that a thread has up to 8 loads in flight and a block
+// covers 256 / NG quads; the order of additions depends only on the split
+// count.
+constexpr int combine_groups(int splits) { return splits <= 8 ? 1 : splits <= 16 ? 2 : splits <= 32 ? 4 : 8; }
 
-// Projection operand for the apply: W log2(e) in the operand type of the
-// projection (fp16 for bf16 inputs, float otherwise), in operand order
-// [Hw*M/32 feature blocks][NKG][half h][feature f][16 bytes]: the 16 bytes of
-// lane (f, h) at k-group g hold d = (D/2) h + (16/WES) g + 0.. (the d-major
-// k order of the projection), so a wave reads 1 KB of contiguous memory.
-// The operand covers M features per head; for the trig map feature f uses
-// W row f mod Mw (its sine and its cosine share a row); rows past the mt
-// rows of W (padding up to a multiple of 32) are zero.
-template <class E, int FM>
-__device__ __forceinline__ void wprep_chunk(const float* w, void* out, int idx, int D, int M, int Mw, int mt) {
-  constexpr int WES = sizeof(E);
-  constexpr int PER = 16 / WES;                      // d values per 16 bytes
-  constexpr float sc = FMap<FM>::kWScale;
-  const int nkg = D * WES / 32;
-  const int f = idx & 31, h = (idx >> 5) & 1, rest = idx >> 6;
-  const int g = rest % nkg, blk = rest / nkg;
-  const int nb = M >> 5;                             // feature blocks per head
-  const int lf = (blk % nb) * 32 + f;                // feature within the head
-  const int wr = FM == FM_TRIG ? lf % Mw : lf;       // its row of W
-  const bool ok = wr < mt;
-  const float* src = w + ((size_t)(blk / nb) * mt + (ok ? wr : 0)) * D + (D / 2) * h + PER * g;
-  if constexpr (WES == 2) {
-    f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
-    if (!ok) x0 = x1 = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 v = {pack_f16(x0[0] * sc, x0[1] * sc), pack_f16(x0[2] * sc, x0[3] * sc),
-               pack_f16(x1[0] * sc, x1[1] * sc), pack_f16(x1[2] * sc, x1[3] * sc)};
-    ((u32x4*)out)[idx] = v;
-  } else {
-    ((f32x4*)out)[idx] = ok ? *(const f32x4*)src * sc : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-// grid.y = BH + 1: slices 0..BH-1 combine a head's partial states, the last
-// slice prepares the projection operand from W (n16w 16-byte chunks).
-template <class E, int FM>
+// grid.y = BH: slice bh combines head bh's partial states.
+template <class E, int NG>
 __global__ __launch_bounds__(256) void k_combine(const float* part, const float* partz, E* mstate, E* zstate,
-                                                 int splits, int M, int D, int BH, const float* w, void* wp,
-                                                 int n16w, int Mw, int mt) {
-  __shared__ f32x4 red[kSplitGroups][kQuadsPerBlock];
+                                                 int splits, int M, int D) {
+  constexpr int kQuadsPerBlock = 256 / NG;
+  __shared__ f32x4 red[NG][kQuadsPerBlock];
   const int bh = blockIdx.y;
-  if (bh == BH) {
-    for (int idx = blockIdx.x * 256 + threadIdx.x; idx < n16w; idx += gridDim.x * 256)
-      wprep_chunk<E, FM>(w, wp, idx, D, M, Mw, mt);
-    return;
-  }
   const int g = threadIdx.x / kQuadsPerBlock, qi = threadIdx.x % kQuadsPerBlock;
   const int quad = blockIdx.x * kQuadsPerBlock + qi;
   const int md4 = M * D / 4, nq = md4 + M / 4;
@@ -457,7 +447,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* part, const float*
     src = (const f32x4*)(partz + (size_t)bh * splits * M) + (active ? quad - md4 : 0);
     stride = M / 4;
   }
-  const int per = (splits + kSplitGroups - 1) / kSplitGroups;
+  const int per = (splits + NG - 1) / NG;
   const int s0 = min(splits, g * per), s1 = min(splits, s0 + per);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (active) {
@@ -469,11 +459,14 @@ __global__ __launch_bounds__(256) void k_combine(const float* part, const float*
       for (int j = 0; j < 8; ++j) acc += v[j];
     }
   }
-  red[g][qi] = acc;
-  __syncthreads();
-  if (g != 0 || !active) return;
+  if constexpr (NG > 1) {
+    red[g][qi] = acc;
+    __syncthreads();
+    if (g != 0) return;
 #pragma unroll
-  for (int gg = 1; gg < kSplitGroups; ++gg) acc += red[gg][qi];
+    for (int gg = 1; gg < NG; ++gg) acc += red[gg][qi];
+  }
+  if (!active) return;
   using OO = OperandOrder<E>;
   if (quad < md4) {
     const int f = quad * 4 / D, d0 = quad * 4 % D;
@@ -500,7 +493,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* part, const float*
 // ===========================================================================
 struct ApplyArgs {
   const void* q;
-  const void* wp;       // projection operand (prepared by k_combine)
+  const void* wp;       // projection operand (written by the first split of k_reduce)
   const void* mstate;   // [BH] x operand-ordered M (m x d), operand type
   const void* zstate;   // [BH] x operand-ordered z (m), operand type
   void* o;
@@ -938,8 +931,8 @@ hipError_t launch_features(const Plan& p, const void* x, const float* w, float* 
 
 template <class Tr, int D>
 hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                           hipStream_t s, int nsplit) {
-  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw, p.mt};
+                           hipStream_t s, int nsplit, void* wp) {
+  RedArgs a{k, v, w, part, partz, p.L, p.M, p.H, p.Hw, p.splits, p.split_len, p.Mw, p.mt, wp};
   // 8 waves of one feature block each, or 4 where a wave's registers exceed
   // half a SIMD's (two blocks per wave, sharing each K/V fragment read, ran
   // slower: half as many waves to hide the latency of each block's chain)
@@ -957,21 +950,21 @@ hipError_t launch_reduce_t(const Plan& p, const void* k, const void* v, const fl
 }
 
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, const float* w, float* part, float* partz,
-                         hipStream_t s, int nsplit) {  // also used for the causal span aggregates
+                         hipStream_t s, int nsplit, void* wp) {  // also used for the causal span aggregates
   if (nsplit < 0 || nsplit > p.splits) nsplit = p.splits;
   if (nsplit == 0) return hipSuccess;
   if (p.x3) return launch_reduce_x3(p, k, v, w, part, partz, s, nsplit);
   if (p.dt == FAVOR_BF16) {
     switch (p.D) {
-      case 32: return launch_reduce_t<TrBF16, 32>(p, k, v, w, part, partz, s, nsplit);
-      case 64: return launch_reduce_t<TrBF16, 64>(p, k, v, w, part, partz, s, nsplit);
-      case 128: return launch_reduce_t<TrBF16, 128>(p, k, v, w, part, partz, s, nsplit);
+      case 32: return launch_reduce_t<TrBF16, 32>(p, k, v, w, part, partz, s, nsplit, wp);
+      case 64: return launch_reduce_t<TrBF16, 64>(p, k, v, w, part, partz, s, nsplit, wp);
+      case 128: return launch_reduce_t<TrBF16, 128>(p, k, v, w, part, partz, s, nsplit, wp);
     }
   } else {
     switch (p.D) {
-      case 32: return launch_reduce_t<TrF32, 32>(p, k, v, w, part, partz, s, nsplit);
-      case 64: return launch_reduce_t<TrF32, 64>(p, k, v, w, part, partz, s, nsplit);
-      case 128: return launch_reduce_t<TrF32, 128>(p, k, v, w, part, partz, s, nsplit);
+      case 32: return launch_reduce_t<TrF32, 32>(p, k, v, w, part, partz, s, nsplit, wp);
+      case 64: return launch_reduce_t<TrF32, 64>(p, k, v, w, part, partz, s, nsplit, wp);
+      case 128: return launch_reduce_t<TrF32, 128>(p, k, v, w, part, partz, s, nsplit, wp);
     }
   }
   return kErrPlan;
@@ -1030,22 +1023,29 @@ hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
   void* wp = t.ws + p.off_wprep;
   void* mstate = t.ws + p.off_mstate;
   void* zstate = t.ws + p.off_zstate;
-  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s);
+  // the reduction also writes the apply's projection operand (wp)
+  hipError_t e = launch_reduce(p, t.k, t.v, t.w, part, partz, s, -1, wp);
   if (e != hipSuccess) return e;
   const int nq = (p.M * p.D + p.M) / 4;
-  const int n16w = p.Hw * p.M * p.D * (p.dt == FAVOR_BF16 ? 2 : 4) / 16;   // M features per head
-  dim3 cgrid((nq + kQuadsPerBlock - 1) / kQuadsPerBlock, p.BH + 1);
-  e = with_fmap(p.fmap, [&]<int FM>() {
-    timing_begin(FAVOR_KERNEL_COMBINE, s);
+  const int ng = combine_groups(p.splits);
+  const dim3 cgrid((nq + 256 / ng - 1) / (256 / ng), p.BH);
+  auto launch_combine = [&]<int NG>() {
     if (p.dt == FAVOR_BF16)
-      hipLaunchKernelGGL((k_combine<bf16, FM>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate,
-                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw, p.mt);
+      hipLaunchKernelGGL((k_combine<bf16, NG>), cgrid, dim3(256), 0, s, part, partz, (bf16*)mstate, (bf16*)zstate,
+                         p.splits, p.M, p.D);
     else
-      hipLaunchKernelGGL((k_combine<float, FM>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
-                         p.splits, p.M, p.D, p.BH, t.w, wp, n16w, p.Mw, p.mt);
-    timing_end(FAVOR_KERNEL_COMBINE, s);
-    return hipGetLastError();
-  });
+      hipLaunchKernelGGL((k_combine<float, NG>), cgrid, dim3(256), 0, s, part, partz, (float*)mstate, (float*)zstate,
+                         p.splits, p.M, p.D);
+  };
+  timing_begin(FAVOR_KERNEL_COMBINE, s);
+  switch (ng) {
+    case 1: launch_combine.template operator()<1>(); break;
+    case 2: launch_combine.template operator()<2>(); break;
+    case 4: launch_combine.template operator()<4>(); break;
+    default: launch_combine.template operator()<8>(); break;
+  }
+  timing_end(FAVOR_KERNEL_COMBINE, s);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_apply(p, t, wp, mstate, zstate, s);
 }
