@@ -326,7 +326,7 @@ favor_status favor_softmax_attn(const void* Q, const void* K, const void* V, voi
 typedef enum {
   FAVOR_KERNEL_FEATURES = 0,   /* fused feature map (favor_features)            */
   FAVOR_KERNEL_REDUCE = 1,     /* K-side state reduction / causal span totals    */
-  FAVOR_KERNEL_COMBINE = 2,    /* non-causal combine of the partials + W operand */
+  FAVOR_KERNEL_COMBINE = 2,    /* non-causal combine of the partial states       */
   FAVOR_KERNEL_APPLY = 3,      /* non-causal Q-side apply                         */
   FAVOR_KERNEL_SPAN_SCAN = 4,  /* causal exclusive prefix over spans              */
   FAVOR_KERNEL_CAUSAL = 5,     /* causal chunked scan                             */
