@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 namespace favor {
@@ -13,20 +14,23 @@ namespace favor {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];                 // zero-initialised (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
 // Size limits: every offset between heads is 64-bit; offsets inside one head
 // are 32-bit byte offsets, so L * max(d, m) must stay below 2^30 (a head's
-// float32 features fit 4 GiB); B * H is a grid dimension (plus one slice for
-// the projection operand), at most 65535.
+// float32 features fit 4 GiB); B * H is a grid dimension (y or z, at most
+// 65535 on this device), accepted up to 65534.
 static favor_status check_shapes(int B, int H, int L, int d, int m, int Hw, favor_dtype dt) {
   if (B < 1 || H < 1 || L < 1) return FAVOR_ERR_SHAPE;
   if (Hw != 1 && Hw != H) return FAVOR_ERR_SHAPE;
