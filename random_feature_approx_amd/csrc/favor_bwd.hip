@@ -179,7 +179,8 @@ __global__ __launch_bounds__(256) void k_bred(BRedArgs a) {
 
   const int split = blockIdx.x, fg = blockIdx.y, bh = blockIdx.z;
   const int head = bh % a.H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int nfb = a.M >> 5;
   const int fb = fg * NW + w;
   const bool active = fb < nfb;
@@ -437,7 +438,8 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
   constexpr int ES = (int)sizeof(E);
   constexpr int WES = VPS == 8 ? 2 : 4;
   constexpr int NKG = D * WES / 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = blockIdx.x * 4 + w;                  // group of TB x 32 tokens
   if (g >= a.total) return;                         // no barriers below
   const int bh = g / a.tiles_per_head, tile = g % a.tiles_per_head;
@@ -1055,7 +1057,8 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
 
   const int span = blockIdx.x, bh = blockIdx.y;
   const int head = bh % a.H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hh = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   float* sZ = (float*)(smem + LY::kZ) + w * 32;
   const int nfb = a.M >> 5;
   const size_t hoff = (size_t)bh * a.L * D;

@@ -153,6 +153,12 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
   // by lane 1; the other lanes write their own data chunk a second time
   // (same value, own address), so that no two lanes of one write touch the
   // same address.
+  // per-lane chunk masks of the staging (bias chunk / bias or zero chunk),
+  // held as plain bit masks in registers: the compiler would otherwise turn
+  // the masked words into selects on VCC, which issue several times slower
+  // on gfx950 than bitwise operations
+  unsigned m0 = scc == 0 ? ~0u : 0u, m1 = scc <= 1 ? ~0u : 0u;
+  asm volatile("" : "+v"(m0), "+v"(m1));
   auto store_chunk = [&](int ci) {
     char* buf = buf_of(ci);
     const bool valid = t0 + ci * C + srow < t1;
@@ -180,11 +186,11 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
     // Rows with |x|^2 > 2^20 (entries may have saturated at the fp16 range)
     // take the padding rows' -inf as well: their features are exactly what
     // float32 gives, zero, whenever every row of W is shorter than 256.
-    const unsigned mvq = 0u - (unsigned)(valid && !(ssq > 1048576.f));   // all ones: a real row
-    const unsigned mvk = 0u - (unsigned)(valid && !(ssk > 1048576.f));
+    unsigned mvq = 0u - (unsigned)(valid && !(ssq > 1048576.f));   // all ones: a real row
+    unsigned mvk = 0u - (unsigned)(valid && !(ssk > 1048576.f));
+    asm volatile("" : "+v"(mvq), "+v"(mvk));
     const unsigned cq = (pack_f16(bqh, fmaxf(bq - bqh, -65504.f)) & mvq) | (0xFC00u & ~mvq);   // pad: -inf, 0
     const unsigned ck = (pack_f16(bkh, fmaxf(bk - bkh, -65504.f)) & mvk) | (0xFC00u & ~mvk);
-    const unsigned m0 = scc == 0 ? ~0u : 0u, m1 = scc <= 1 ? ~0u : 0u;  // bias chunk / bias or zero chunk
     const int boff = scc <= 1 ? D * 2 + scc * 16 : scc * 16;
     *(u32x4*)(buf + LY::kQh + srow * RSX + boff) =
         u32x4{(cq & m0) | (hq[0] & ~m1), hq[1] & ~m1, hq[2] & ~m1, hq[3] & ~m1};
