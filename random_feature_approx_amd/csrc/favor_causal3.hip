@@ -163,17 +163,11 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
     char* buf = buf_of(ci);
     const bool valid = t0 + ci * C + srow < t1;
     float ssq = 0.f, ssk = 0.f;
-    u32x4 hq, hk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const unsigned uq = gq[j], uk = gk[j];
-      ssq = dot2_bf16(uq, uq, ssq);
-      ssk = dot2_bf16(uk, uk, ssk);
-      hq[j] = bf16x2_to_f16x2(uq);
-      hk[j] = bf16x2_to_f16x2(uk);
+      ssq = dot2_bf16(gq[j], gq[j], ssq);
+      ssk = dot2_bf16(gk[j], gk[j], ssk);
     }
-    *(u32x4*)(buf + LY::kQh + srow * RSX + scc * 16) = hq;
-    *(u32x4*)(buf + LY::kKh + srow * RSX + scc * 16) = hk;
     *(u32x4*)(buf + LY::kV + srow * RS + scc * 16) = gv;
     ssq = group_sum<CPR>(ssq);
     ssk = group_sum<CPR>(ssk);
@@ -183,12 +177,22 @@ __global__ __launch_bounds__(256, 2) void k_causal3(Causal3Args a) {
     // |w| exceeds ~200)
     const float bqh = (float)(_Float16)fmaxf(bq, -65504.f), bkh = (float)(_Float16)fmaxf(bk, -65504.f);
     // bitwise selects: computed for every lane, so no branch is formed.
-    // Rows with |x|^2 > 2^20 (entries may have saturated at the fp16 range)
-    // take the padding rows' -inf as well: their features are exactly what
-    // float32 gives, zero, whenever every row of W is shorter than 256.
+    // Rows with |x|^2 > 2^20 take the padding rows' -inf as well: their
+    // features are exactly what float32 gives, zero, whenever every row of W
+    // is shorter than 256.  Their data words are zeroed, which also covers
+    // entries past fp16's range (|x|^2 > 2^32 then): the conversion below
+    // does not saturate.
     unsigned mvq = 0u - (unsigned)(valid && !(ssq > 1048576.f));   // all ones: a real row
     unsigned mvk = 0u - (unsigned)(valid && !(ssk > 1048576.f));
     asm volatile("" : "+v"(mvq), "+v"(mvk));
+    u32x4 hq, hk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hq[j] = pack_f16(bf16_lo(gq[j]), bf16_hi(gq[j])) & mvq;
+      hk[j] = pack_f16(bf16_lo(gk[j]), bf16_hi(gk[j])) & mvk;
+    }
+    *(u32x4*)(buf + LY::kQh + srow * RSX + scc * 16) = hq;
+    *(u32x4*)(buf + LY::kKh + srow * RSX + scc * 16) = hk;
     const unsigned cq = (pack_f16(bqh, fmaxf(bq - bqh, -65504.f)) & mvq) | (0xFC00u & ~mvq);   // pad: -inf, 0
     const unsigned ck = (pack_f16(bkh, fmaxf(bk - bkh, -65504.f)) & mvk) | (0xFC00u & ~mvk);
     const int boff = scc <= 1 ? D * 2 + scc * 16 : scc * 16;
