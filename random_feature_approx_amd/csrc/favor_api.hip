@@ -517,7 +517,9 @@ favor_status favor_timing_start(favor_kernel k, int capacity) {
   timer_free(t);
   t.ev = new hipEvent_t[2 * (size_t)capacity];
   for (int i = 0; i < 2 * capacity; ++i) {
-    if (hipEventCreate(&t.ev[i]) != hipSuccess) {
+    // timing only: no system-scope fence at each record (its cache writeback
+    // and invalidate would otherwise be timed with the kernel)
+    if (hipEventCreateWithFlags(&t.ev[i], hipEventDisableSystemFence) != hipSuccess) {
       for (int j = 0; j < i; ++j) hipEventDestroy(t.ev[j]);
       delete[] t.ev;
       t = Timer();
