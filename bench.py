@@ -454,7 +454,7 @@ def main() -> int:
                 continue
             other = synth.WORKLOADS[name]
             r = measure(favor, torch, np, synth, other, args.config_steps, args.config_warmup, args.settle_ms,
-                        with_traffic=False)
+                        with_traffic=True)
             r.pop("_inputs")
             configs[name] = {"workload": f"{other.name}: B={other.B} H={other.H} L={other.L} d={other.d} "
                                          f"m={other.m} {other.dtype}, {' + '.join(other.paths)}",
