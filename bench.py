@@ -274,7 +274,8 @@ def fmap_leg(favor, torch, wl, q, k, v, w, outs, K: int, warmup: int) -> dict:
     return out
 
 
-def measure(favor, torch, np, synth, wl, K: int, warmup: int, settle_ms: float, with_traffic: bool) -> dict:
+def measure(favor, torch, np, synth, wl, K: int, warmup: int, settle_ms: float, with_traffic: bool,
+            graph: bool = False) -> dict:
     """One workload: settle the clock, W warmup steps, K timed steps (no
     other events on the stream), then K more steps with per-path events and
     the library's per-launch kernel events for the per-path and per-kernel
@@ -367,8 +368,31 @@ def measure(favor, torch, np, synth, wl, K: int, warmup: int, settle_ms: float, 
                             "hbm_frac_alg": r.get("hbm_frac_alg"), "mfma_frac_alg": r.get("mfma_frac_alg")}
     paths_report = {p: {"ms": round(path_ms[p], 5), "tokens_per_s": round(wl.tokens / (path_ms[p] * 1e-3), 1)}
                     for p in wl.paths}
-    return {"ms_per_step": round(ms_step, 5), "roofline": roof, "kernels": kern_report, "paths": paths_report,
-            "_inputs": (x, q, k, v, w, outs, to_dev)}
+    res = {"ms_per_step": round(ms_step, 5), "roofline": roof, "kernels": kern_report, "paths": paths_report,
+           "_inputs": (x, q, k, v, w, outs, to_dev)}
+    if graph:
+        # the step captured once as a HIP graph and replayed (no per-call
+        # host work); every replay writes the eager outputs bit for bit (the
+        # calls enqueue kernels only)
+        ref = {p: outs[p].clone() for p in wl.paths}
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for p in wl.paths:
+                run(p)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(K):
+            g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        res["graph_ms_per_step"] = round(start.elapsed_time(stop) / K, 5)
+        res["graph_replays_match_eager"] = all(torch.equal(outs[p], ref[p]) for p in wl.paths)
+        log(f"graph replay: {res['graph_ms_per_step']:.4f} ms/step, outputs equal to eager: "
+            f"{res['graph_replays_match_eager']}")
+    return res
 
 
 def main() -> int:
@@ -454,7 +478,7 @@ def main() -> int:
                 continue
             other = synth.WORKLOADS[name]
             r = measure(favor, torch, np, synth, other, args.config_steps, args.config_warmup, args.settle_ms,
-                        with_traffic=True)
+                        with_traffic=True, graph=(name == "t1"))
             r.pop("_inputs")
             configs[name] = {"workload": f"{other.name}: B={other.B} H={other.H} L={other.L} d={other.d} "
                                          f"m={other.m} {other.dtype}, {' + '.join(other.paths)}",
@@ -466,7 +490,12 @@ def main() -> int:
             if any(split_products(other, p, "k_causal") for p in other.paths):
                 configs[name]["arithmetic"] = SPLIT_ARITHMETIC
             if name == "t1":
+                # latency of one call; beside it the same step captured once
+                # as a HIP graph and replayed (on this stack a replay of so
+                # small a graph is not faster than the eager launches)
                 configs[name]["latency_ms"] = r["ms_per_step"]
+                configs[name]["graph_ms_per_step"] = r["graph_ms_per_step"]
+                configs[name]["graph_replays_match_eager"] = r["graph_replays_match_eager"]
             torch.cuda.empty_cache()
     cpu = None
     if args.cpu_seconds > 0:
