@@ -110,6 +110,11 @@ struct CausalArgs {
   int mt;                 // rows of W per head as given; features of rows >= mt are padding
 };
 
+// Non-causal attention of short heads in one launch (favor_small.hip):
+// L <= 64, m <= 256, d in {32, 64}, FAVOR+.
+bool small_nc_fits(const Plan& p);
+hipError_t launch_small_nc(const Plan& p, const Tensors& t, hipStream_t s);
+
 // Kernel timing hooks (see favor_timing_start): record the next free event
 // pair of kernel k around a launch on stream s.
 void timing_begin(favor_kernel k, hipStream_t s);

@@ -1018,6 +1018,7 @@ static hipError_t launch_apply(const Plan& p, const Tensors& t, const void* wp, 
 }
 
 hipError_t launch_noncausal(const Plan& p, const Tensors& t, hipStream_t s) {
+  if (small_nc_fits(p)) return launch_small_nc(p, t, s);
   float* part = (float*)(t.ws + p.off_part);
   float* partz = (float*)(t.ws + p.off_partz);
   void* wp = t.ws + p.off_wprep;

@@ -131,6 +131,24 @@ def test_noncausal_shared_projection(gpu):
     assert row_rel_err(out, _ref(x, False)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype,d,m,B,H,L,heads_w", [
+    ("f32", 32, 256, 1, 1, 64, None),   # the worked example's shape
+    ("f32", 32, 32, 1, 2, 17, None),
+    ("f32", 64, 96, 2, 2, 33, None),    # second token block holds one token
+    ("f32", 64, 250, 1, 3, 64, 1),      # ragged m, one W for every head
+    ("bf16", 64, 256, 1, 4, 64, None),
+    ("bf16", 32, 200, 3, 1, 31, None),
+    ("bf16", 64, 40, 1, 2, 2, None),
+    ("bf16", 32, 256, 2, 2, 64, 1),
+])
+def test_noncausal_short_heads(gpu, dtype, d, m, B, H, L, heads_w):
+    """Heads of at most 64 tokens (m <= 256, d 32 or 64) take the one-launch
+    kernel: every row against the oracle at the same tolerances."""
+    x = synth.random_case(8100 + d + m + L, B, H, L, d, m, dtype, heads_w=heads_w)
+    out = _run_attn(gpu, x, dtype, causal=False)
+    assert row_rel_err(out, _ref(x, False)) <= TOL[dtype]
+
+
 def test_noncausal_encoder_full_size_sampled(gpu):
     """The full encoder workload (B=8, H=12, L=4096, d=64, m=256, bf16) in the
     launch configuration the benchmark uses; every head is checked on 64
