@@ -327,7 +327,7 @@ typedef enum {
   FAVOR_KERNEL_FEATURES = 0,   /* fused feature map (favor_features)            */
   FAVOR_KERNEL_REDUCE = 1,     /* K-side state reduction / causal span totals    */
   FAVOR_KERNEL_COMBINE = 2,    /* non-causal combine of the partial states       */
-  FAVOR_KERNEL_APPLY = 3,      /* non-causal Q-side apply                         */
+  FAVOR_KERNEL_APPLY = 3,      /* non-causal Q-side apply (heads of <= 64 tokens: the one-launch kernel) */
   FAVOR_KERNEL_SPAN_SCAN = 4,  /* causal exclusive prefix over spans              */
   FAVOR_KERNEL_CAUSAL = 5,     /* causal chunked scan                             */
   FAVOR_KERNEL_BWD_PREP = 6,   /* backward: W operands                            */
