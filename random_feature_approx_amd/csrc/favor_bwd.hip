@@ -903,6 +903,31 @@ __global__ __launch_bounds__(256) void k_bscan(float* part, float* partz, int sp
   }
 }
 
+// DP consecutive values of an output row (16-byte aligned) in 16-byte stores,
+// each value rounded to E as a scalar conversion would
+template <class E, int DP>
+__device__ __forceinline__ void store_row(E* dst, const float (&v)[DP]) {
+  if constexpr (sizeof(E) == 2 && DP == 4) {
+    E h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (E)v[e];
+    *(u32x2*)dst = __builtin_bit_cast(u32x2, h);
+  } else if constexpr (sizeof(E) == 2) {
+    static_assert(DP % 8 == 0, "whole 16-byte groups");
+#pragma unroll
+    for (int j = 0; j < DP; j += 8) {
+      E h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = (E)v[j + e];
+      *(u32x4*)(dst + j) = __builtin_bit_cast(u32x4, h);
+    }
+  } else {
+    static_assert(DP % 4 == 0, "whole 16-byte groups");
+#pragma unroll
+    for (int j = 0; j < DP; j += 4) *(f32x4*)(dst + j) = f32x4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+  }
+}
+
 struct BCausalArgs {
   const void* q;
   const void* k;
@@ -1128,12 +1153,26 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
 
     TileLoader<E, D, C, NT> lq, lk, lv, lg_;
     auto chunk0 = [&](int ci) { return t0 + ci * C; };
+    // per-token scalars of the first query walk (c_i; log2 D_i for the key
+    // side), loaded one chunk ahead with the tiles by the threads that stage them
+    float pcw = 0.f, plg = 0.f;
+    const bool sthr = tid >= 64 && tid < 64 + C;
     auto prefetch = [&](int ci) {
       const int c0 = chunk0(ci);
       lq.load(Qg + (size_t)c0 * D, t1 - c0, tid);
       lk.load(Kg + (size_t)c0 * D, t1 - c0, tid);
       lv.load(Vg + (size_t)c0 * D, t1 - c0, tid);
       lg_.load(Gg + (size_t)c0 * D, t1 - c0, tid);
+      if constexpr (MODE != kQ1) {
+        const int r = tid - 64;
+        if (sthr && r < t1 - c0) {
+          pcw = a.cw[(size_t)bh * a.L + c0 + r];
+          if constexpr (MODE == kK) plg = a.lg[(size_t)bh * a.L + c0 + r];
+        } else {
+          pcw = 0.f;
+          plg = 0.f;
+        }
+      }
     };
     if (nch > 0) prefetch(QSIDE ? 0 : nch - 1);
     for (int it = 0; it < nch; ++it) {
@@ -1150,12 +1189,10 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       if constexpr (MODE != kQ1) {
         // per-token log2 D_i and c_i of the first walk: the key side divides
         // the query features by D_i (bias - log2 D_i) and weights them by c_i;
-        // the second query walk uses s_i/D_i = -c_i
-        if (tid >= 64 && tid < 64 + C) {
-          const int r = tid - 64;
-          const bool ok = r < nv;
-          sC[r] = ok ? a.cw[(size_t)bh * a.L + c0 + r] : 0.f;
-          if constexpr (MODE == kK) sRedS[r] = ok ? a.lg[(size_t)bh * a.L + c0 + r] : 0.f;
+        // the second query walk uses s_i/D_i = -c_i (rows past nv: 0)
+        if (sthr) {
+          sC[tid - 64] = pcw;
+          if constexpr (MODE == kK) sRedS[tid - 64] = plg;
         }
       }
       __syncthreads();
@@ -1374,14 +1411,75 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
         }
       }
 
+      // what the end of this chunk reads from memory, requested before the
+      // sums over the waves so that its latency hides behind them (not
+      // earlier: the values would be live across the products, where the
+      // register file is full): the input row of the token (dq and dk
+      // subtract a multiple of it), the token's log2 D_i and c_i (second query
+      // walk) and the sums carried from earlier feature groups
+      const bool rt = tid < 8 * C;
+      const int tq = rt ? tid >> 3 : 0, d0 = (tid & 7) * DP;
+      const bool own = rt && tq < nv;
+      const size_t tokq = (size_t)c0 + tq;
+      constexpr int NRND = MODE == kQ1 ? 0 : (MODE == kQ2 ? 1 : 2);
+      float xrow[DP], carried[NRND > 0 ? NRND * DP : 1], cs1 = 0.f, cs2 = 0.f, lgq = 0.f, cwq = 0.f;
+      if constexpr (MODE != kQ1) {
+        const E* xr = (MODE == kQ2 ? Qg : Kg) + tokq * D + d0;
+        const bool need = own && fg + 1 == a.fgroups;
+        if constexpr (sizeof(E) == 2 && DP == 4) {
+          u32x2 x2 = {0u, 0u};
+          if (need) x2 = *(const u32x2*)xr;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            xrow[2 * e] = bf16_lo(x2[e]);
+            xrow[2 * e + 1] = bf16_hi(x2[e]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < DP; j += 16 / (int)sizeof(E)) {
+            u32x4 x4 = {0u, 0u, 0u, 0u};
+            if (need) x4 = *(const u32x4*)(xr + j);
+            if constexpr (sizeof(E) == 2) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                xrow[j + 2 * e] = bf16_lo(x4[e]);
+                xrow[j + 2 * e + 1] = bf16_hi(x4[e]);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xrow[j + e] = as_f32(x4[e]);
+            }
+          }
+        }
+        if constexpr (MODE == kQ2) {
+          if (own && fg + 1 == a.fgroups) {
+            lgq = a.lg[(size_t)bh * a.L + tokq];
+            cwq = a.cw[(size_t)bh * a.L + tokq];
+          }
+        }
+      }
+      if constexpr (NRND > 0) {
+#pragma unroll
+        for (int j = 0; j < NRND * DP; ++j) carried[j] = 0.f;
+        if (a.fgroups > 1 && fg > 0 && own) {
+          const float* ar = a.acc + ((size_t)bh * a.L + tokq) * AW;
+#pragma unroll
+          for (int rd = 0; rd < NRND; ++rd)
+#pragma unroll
+            for (int j = 0; j < DP; ++j) carried[rd * DP + j] = ar[rd * D + d0 + j];   // rows 8-byte aligned
+        }
+      }
+      if (a.fgroups > 1 && fg > 0 && own && MODE != kQ2) {
+        const float* as = a.acc + ((size_t)bh * a.L + tokq) * AW + 2 * D;
+        cs1 = as[0];
+        cs2 = as[1];
+      }
       // ---- sums over the waves (fixed order) and the feature groups --------
       // carried sums per token: [0, D) first output, [D, 2D) second, 2D and
       // 2D+1 the two scalars
       float* accrow = a.acc + ((size_t)bh * a.L + c0) * AW;
-      // threads 0..255: eight per token of the chunk
-      const bool rt = tid < 8 * C;
-      const int tq = rt ? tid >> 3 : 0, d0 = (tid & 7) * DP;
-      constexpr int NROUND = MODE == kQ1 ? 0 : (MODE == kQ2 ? 1 : 2);
+      // threads 0..255: eight per token of the chunk (rt, tq, d0 above)
+      constexpr int NROUND = NRND;
       float v1[DP], v2[DP], sc1 = 0.f, sc2 = 0.f;
       {
         const float a1 = half_sum(ps1), a2s = half_sum(ps2);
@@ -1420,7 +1518,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
           float* ar = accrow + (size_t)tq * AW + round * D + d0;
           if (fg > 0) {
 #pragma unroll
-            for (int j = 0; j < DP; ++j) vv[j] += ar[j];
+            for (int j = 0; j < DP; ++j) vv[j] += carried[round * DP + j];
           }
           if (fg + 1 < a.fgroups) {
 #pragma unroll
@@ -1438,8 +1536,8 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       if (a.fgroups > 1 && rt && tq < nv && MODE != kQ2) {
         float* as = accrow + (size_t)tq * AW + 2 * D;
         if (fg > 0) {
-          sc1 += as[0];
-          sc2 += as[1];
+          sc1 += cs1;
+          sc2 += cs2;
         }
         if (fg + 1 < a.fgroups && (tid & 7) == 0) {
           as[0] = sc1;
@@ -1455,21 +1553,18 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
             a.cw_out[(size_t)bh * a.L + tok] = -(sc2 / den);
           }
         } else if constexpr (MODE == kQ2) {
-          E* out = (E*)a.dx + hoff + tok * D + d0;
-          const E* xr = Qg + tok * D + d0;
-          const float inv = exp2f(-a.lg[(size_t)bh * a.L + tok]);
-          const float ratio = -a.cw[(size_t)bh * a.L + tok];
+          const float inv = exp2f(-lgq);
+          const float ratio = -cwq;
+          float o[DP];
 #pragma unroll
-          for (int j = 0; j < DP; ++j) out[j] = (E)((v1[j] - ratio * a.eps * (float)xr[j]) * inv);
+          for (int j = 0; j < DP; ++j) o[j] = (v1[j] - ratio * a.eps * xrow[j]) * inv;
+          store_row<E, DP>((E*)a.dx + hoff + tok * D + d0, o);
         } else {
-          E* out = (E*)a.dx + hoff + tok * D + d0;
-          const E* xr = Kg + tok * D + d0;
-          E* outv = (E*)a.dy + hoff + tok * D + d0;
+          float o[DP];
 #pragma unroll
-          for (int j = 0; j < DP; ++j) {
-            out[j] = (E)(v1[j] - sc1 * (float)xr[j]);
-            outv[j] = (E)v2[j];
-          }
+          for (int j = 0; j < DP; ++j) o[j] = v1[j] - sc1 * xrow[j];
+          store_row<E, DP>((E*)a.dx + hoff + tok * D + d0, o);
+          store_row<E, DP>((E*)a.dy + hoff + tok * D + d0, v2);
         }
       }
     }
