@@ -962,7 +962,17 @@ struct BCLds {
   static constexpr int kZ = kC + C * 4;                 // per wave: 32 floats (z or r of its features)
   static constexpr int kRed = kZ + NW * 32 * 4;         // per wave: C x RSR floats
   static constexpr int kRedS = kRed + NW * C * RSR * 4; // per wave: C x 2 floats
-  static constexpr int kTotal = kRedS + NW * C * 2 * 4;
+  static constexpr int kBase = kRedS + NW * C * 2 * 4;
+  // per wave, where it fits next to the rest: the W^T operand fragments of the
+  // wave's feature block, [NKT k-steps][NDB d blocks][hi, lo][64 lanes],
+  // copied once per feature group, so that the chunk loop reads them from LDS
+  // (global loads there would share the in-order load counter with the next
+  // chunk's tile prefetch, and waiting for them would wait for the prefetch)
+  static constexpr int WTF = (32 / Tr::KS) * (D / 32) * Bw<Tr>::NS;   // fragments per wave
+  static constexpr int WTB = WTF * 64 * (int)sizeof(typename Tr::frag);
+  static constexpr bool kStageWt = kBase + NW * WTB <= 160 * 1024;
+  static constexpr int kWt = kBase;
+  static constexpr int kTotal = kBase + (kStageWt ? NW * WTB : 0);
 };
 
 // B operand over d in c-row order (k-step s2 of d block db) from one row of
@@ -1106,13 +1116,22 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
     tri[s2] = const_frag<Tr>(s2, lane, [](int k, int n) { return k <= n; });   // key k <= query n
   }
   // W^T operand (hi, lo) of block fb, k-step s2, d block db (lane = d)
-  auto wt_frag = [&](int fb, int s2, int db, F (&wt)[SP::NS]) {
+  auto wt_global = [&](int fb, int s2, int db, F (&wt)[SP::NS]) {
     const size_t e = (((((size_t)fb * NKT + s2) * NDB + db) * 2 + hh) * 32 + l32) * VPS;
     if constexpr (VPS == 8) {
       wt[0] = *(const u32x4*)(wth + e);
       if constexpr (SP::NS == 2) wt[1] = *(const u32x4*)(wtl + e);
     } else {
       wt[0] = wth[e];
+    }
+  };
+  F* sWt = (F*)(smem + LY::kWt) + (size_t)w * LY::WTF * 64;   // this wave's staged copy
+  auto wt_frag = [&](int fb, int s2, int db, F (&wt)[SP::NS]) {
+    if constexpr (LY::kStageWt) {
+#pragma unroll
+      for (int p = 0; p < SP::NS; ++p) wt[p] = sWt[((s2 * NDB + db) * SP::NS + p) * 64 + lane];
+    } else {
+      wt_global(fb, s2, db, wt);
     }
   };
 
@@ -1136,6 +1155,19 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
           for (int j = 0; j < 4; ++j) wf[p][4 * gk + j] = v[j];
         }
       }
+    }
+    if constexpr (LY::kStageWt && MODE != kQ1) {
+      // wave-private copy: a wave's LDS accesses complete in program order,
+      // so this overwrites the previous group's copy after its last read
+#pragma unroll
+      for (int s2 = 0; s2 < NKT; ++s2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          F wt[SP::NS];
+          wt_global(fbs, s2, db, wt);
+#pragma unroll
+          for (int p = 0; p < SP::NS; ++p) sWt[((s2 * NDB + db) * SP::NS + p) * 64 + lane] = wt[p];
+        }
     }
     // state of this block from the span prefix (query side: S^T, rows d, lane f;
     // key side: R^T (rows d, lane f) and R (rows f, lane d)) and z or r
