@@ -426,6 +426,30 @@ struct BSideArgs {
 template <class Tr, int D, bool SIDE_Q>
 constexpr int bside_waves() { return (Tr::VPS == 8 && D <= 64 && SIDE_Q) ? 2 : 1; }
 
+// The per-head operands of one 32-feature block, as one workgroup's LDS
+// image (16-byte chunks, each region in the order its fragments are read:
+// chunk q of lane l at q * 64 + l): the projection operand (hi, lo parts),
+// the rows of M or dM (hi, lo), z or dz, dM in the apply's operand order (key
+// side) and the W^T operand (hi, lo).  The four waves of a workgroup work on
+// one head; the image of block fb + 1 is copied (global -> LDS) while block
+// fb is used.
+template <class Tr, int D, bool SIDE_Q>
+struct BSideImg {
+  static constexpr int ES = (int)sizeof(typename Tr::elem);
+  static constexpr int NS = Bw<Tr>::NS;
+  static constexpr int WES = Tr::VPS == 8 ? 2 : 4;
+  static constexpr int NKT = 32 / Tr::KS, NDB = D / 32;
+  static constexpr int CWP = (D * WES / 32) * 64;             // projection operand, per part
+  static constexpr int RQ = (D / 2) * ES / 16;                // row chunks per lane
+  static constexpr int CR = RQ * 64;                          // rows, per part
+  static constexpr int CZ = 8;                                // 32 floats
+  static constexpr int COP = SIDE_Q ? 0 : (Tr::VPS == 8 ? 2 : 4) * 2 * D;
+  static constexpr int CWT = NKT * NDB * 64 * Tr::VPS * ES / 16;   // W^T operand, per part
+  static constexpr int kWp = 0, kR = kWp + NS * CWP, kZ = kR + NS * CR, kOp = kZ + CZ, kWt = kOp + COP;
+  static constexpr int CHUNKS = kWt + NS * CWT;
+  static constexpr int BYTES = CHUNKS * 16;
+};
+
 template <class Tr, int D, bool SIDE_Q, int TB>
 __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(BSideArgs a) {
   using E = typename Tr::elem;
@@ -438,11 +462,15 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
   constexpr int ES = (int)sizeof(E);
   constexpr int WES = VPS == 8 ? 2 : 4;
   constexpr int NKG = D * WES / 32;
-  const int lane = threadIdx.x & 63, hh = lane >> 5, l32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int g = blockIdx.x * 4 + w;                  // group of TB x 32 tokens
-  if (g >= a.total) return;                         // no barriers below
-  const int bh = g / a.tiles_per_head, tile = g % a.tiles_per_head;
+  using IMG = BSideImg<Tr, D, SIDE_Q>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  // workgroup = 4 consecutive groups of TB x 32 tokens of one head; waves
+  // past the head's last group take part in the copies and barriers only
+  const int wgs_per_head = (a.tiles_per_head + 3) / 4;
+  const int bh = blockIdx.x / wgs_per_head, tile = (blockIdx.x % wgs_per_head) * 4 + w;
+  const bool active = tile < a.tiles_per_head;
   const int head = bh % a.H;
   const int nfb = a.M >> 5;
   const float half_ln_m = 0.5f * logf((float)a.mt);
@@ -491,34 +519,77 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
   const E* rlo = (const E*)a.rows_lo + (size_t)bh * a.M * D;
   const float* zf = a.zf + (size_t)bh * a.M;
 
-  // projection operand of block fb (hi, lo)
-  auto wproj = [&](int fb, F (&wfr)[SP::NS][NKD]) {
+  const char* opb = SIDE_Q ? nullptr : (const char*)a.op + (size_t)bh * a.M * D * ES;
+  // ---- the LDS image of feature block fb: copy, then fragment reads --------
+  // image buffers alternate with the step of the walk (not with fb: the
+  // query side walks the blocks twice)
+  auto img = [&](int step) -> char* { return smem + (step & 1) * IMG::BYTES; };
+  auto copy_region = [&](char* dst, int nchunks, auto src_of) {
+    for (int c0 = w * 64; c0 < nchunks; c0 += 256) {
+      const int c = c0 + lane;
+      if (c < nchunks) __builtin_amdgcn_global_load_lds(FAVOR_GLB(src_of(c)), LDS_PTR(void, dst + c0 * 16), 16, 0, 0);
+    }
+  };
+  auto copy_image = [&](int fb, int step, bool with_wt) {
+    char* im = img(step);
 #pragma unroll
     for (int pp = 0; pp < SP::NS; ++pp) {
-      const char* base = (pp == 0 ? wph : wpl) + (size_t)fb * NKG * 2 * 32 * 16;
+      const char* wsrc = (pp == 0 ? wph : wpl) + (size_t)fb * IMG::CWP * 16;
+      copy_region(im + (IMG::kWp + pp * IMG::CWP) * 16, IMG::CWP, [&](int c) { return wsrc + (size_t)c * 16; });
+      const char* rsrc = (const char*)(pp == 0 ? rhi : rlo) + (size_t)fb * 32 * D * ES;
+      copy_region(im + (IMG::kR + pp * IMG::CR) * 16, IMG::CR, [&](int c) {
+        const int q = c >> 6, ln = c & 63;            // chunk q of lane ln = (row, half)
+        return rsrc + (size_t)(ln & 31) * D * ES + (D / 2) * (ln >> 5) * ES + q * 16;
+      });
+    }
+    const char* zsrc = (const char*)(zf + fb * 32);
+    copy_region(im + IMG::kZ * 16, IMG::CZ, [&](int c) { return zsrc + (size_t)c * 16; });
+    if constexpr (!SIDE_Q) {
+      const char* osrc = opb + (size_t)fb * IMG::COP * 16;
+      copy_region(im + IMG::kOp * 16, IMG::COP, [&](int c) { return osrc + (size_t)c * 16; });
+    }
+    if (with_wt) {
+#pragma unroll
+      for (int pp = 0; pp < SP::NS; ++pp) {
+        const char* tsrc = (const char*)(pp == 0 ? wt : wtlo) + (size_t)fb * IMG::CWT * 16;
+        copy_region(im + (IMG::kWt + pp * IMG::CWT) * 16, IMG::CWT, [&](int c) { return tsrc + (size_t)c * 16; });
+      }
+    }
+  };
+  // projection operand of block fb (hi, lo)
+  auto wproj = [&](const char* im, F (&wfr)[SP::NS][NKD]) {
+#pragma unroll
+    for (int pp = 0; pp < SP::NS; ++pp) {
+      const char* base = im + (IMG::kWp + pp * IMG::CWP) * 16;
       if constexpr (WES == 2) {
 #pragma unroll
-        for (int s = 0; s < NKD; ++s) wfr[pp][s] = *(const u32x4*)(base + ((s * 2 + hh) * 32 + l32) * 16);
+        for (int s = 0; s < NKD; ++s) wfr[pp][s] = *(const u32x4*)(base + (s * 64 + lane) * 16);
       } else {
 #pragma unroll
         for (int gk = 0; gk < NKG; ++gk) {
-          const f32x4 v = *(const f32x4*)(base + ((gk * 2 + hh) * 32 + l32) * 16);
+          const f32x4 v = *(const f32x4*)(base + (gk * 64 + lane) * 16);
 #pragma unroll
           for (int j = 0; j < 4; ++j) wfr[pp][4 * gk + j] = v[j];
         }
       }
     }
   };
-  // rows operand (M or dM, hi + lo) of block fb
-  auto rows = [&](int fb, F (&rf)[SP::NS][NKD]) {
-    const size_t rb = (size_t)(fb * 32 + l32) * D + (D / 2) * hh;
+  // rows operand (M or dM, hi + lo) of block fb: lane (f, h) holds row f,
+  // elements (D/2) h + 0 ..
+  auto rows = [&](const char* im, F (&rf)[SP::NS][NKD]) {
 #pragma unroll
-    for (int s = 0; s < NKD; ++s) {
+    for (int pp = 0; pp < SP::NS; ++pp) {
+      const char* base = im + (IMG::kR + pp * IMG::CR) * 16;
       if constexpr (VPS == 8) {
-        rf[0][s] = *(const u32x4*)(rhi + rb + VPS * s);
-        if constexpr (SP::NS == 2) rf[1][s] = *(const u32x4*)(rlo + rb + VPS * s);
+#pragma unroll
+        for (int s = 0; s < NKD; ++s) rf[pp][s] = *(const u32x4*)(base + (s * 64 + lane) * 16);
       } else {
-        rf[0][s] = rhi[rb + s];
+#pragma unroll
+        for (int q = 0; q < IMG::RQ; ++q) {
+          const f32x4 v = *(const f32x4*)(base + (q * 64 + lane) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rf[pp][4 * q + j] = v[j];
+        }
       }
     }
   };
@@ -547,11 +618,12 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
     return acc;
   };
   // z or dz values of the rows of feature block fb, in accumulator order
-  auto zrows = [&](int fb) -> f32x16 {
+  auto zrows = [&](const char* im) -> f32x16 {
     f32x16 zr;
+    const float* zl = (const float*)(im + IMG::kZ * 16);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 v = *(const f32x4*)(zf + fb * 32 + 8 * q4 + 4 * hh);
+      const f32x4 v = *(const f32x4*)(zl + 8 * q4 + 4 * hh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) zr[4 * q4 + j] = v[j];
     }
@@ -559,7 +631,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
   };
   // acc[tb][db] += W^T gacc[tb] (c-row feature order), both operands split
   // into hi + lo (three products: hi hi, hi lo, lo hi)
-  auto wt_times = [&](int fb, const f32x16 (&gacc)[TB], f32x16 (&acc)[TB][NDB]) {
+  auto wt_times = [&](const char* im, const f32x16 (&gacc)[TB], f32x16 (&acc)[TB][NDB]) {
 #pragma unroll
     for (int s2 = 0; s2 < NKT; ++s2) {
       F gfr[TB][SP::NS];
@@ -567,14 +639,11 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       for (int tb = 0; tb < TB; ++tb) SP::split(gacc[tb], s2, gfr[tb]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const size_t e = (((((size_t)fb * NKT + s2) * NDB + db) * 2 + hh) * 32 + l32) * VPS;
+        const int e = ((s2 * NDB + db) * 64 + lane) * VPS;   // element within the part
         F wfr[SP::NS];
-        if constexpr (VPS == 8) {
-          wfr[0] = *(const u32x4*)(wt + e);
-          if constexpr (SP::NS == 2) wfr[1] = *(const u32x4*)(wtlo + e);
-        } else {
-          wfr[0] = wt[e];
-        }
+#pragma unroll
+        for (int pp = 0; pp < SP::NS; ++pp)
+          wfr[pp] = *(const F*)(im + (IMG::kWt + pp * IMG::CWT) * 16 + e * ES);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
           acc[tb][db] = Tr::mma(wfr[0], gfr[tb][0], acc[tb][db]);
@@ -585,6 +654,29 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
         }
       }
     }
+  };
+  // the input row's values at this lane's output columns d = 32 db + 8 i + 4 h
+  // + j, all requested before any output is stored (the stores could alias
+  // the input as far as the compiler knows, so loads between them would each
+  // wait for a full memory round trip)
+  auto x_at_outputs = [&](int tb, float (&xo)[NDB][4][4]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const E* src = xrow[tb] + db * 32 + 8 * i + 4 * hh;
+        if constexpr (ES == 2) {
+          const u32x2 x2 = *(const u32x2*)src;
+          xo[db][i][0] = bf16_lo(x2[0]);
+          xo[db][i][1] = bf16_hi(x2[0]);
+          xo[db][i][2] = bf16_lo(x2[1]);
+          xo[db][i][3] = bf16_hi(x2[1]);
+        } else {
+          const f32x4 x4 = *(const f32x4*)src;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xo[db][i][j] = x4[j];
+        }
+      }
   };
   // store 16 values of a d^T accumulator for token block tb (columns d0..d0+3)
   auto store4 = [&](E* row, int d0, const float (&v)[4]) {
@@ -601,15 +693,28 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dacc[tb][db] = zero16();
 
+  // one step of the block walk: the image of block fb is complete and every
+  // wave is done with the other buffer, whose next image is then requested
+  auto next_image = [&](int it, int nit, auto want_wt) -> const char* {
+    wait_vmcnt<0>();
+    raw_barrier();
+    if (it + 1 < nit) copy_image((it + 1) % nfb, it + 1, want_wt(it + 1));
+    return img(it);
+  };
   if constexpr (SIDE_Q) {
     float den[TB], sy[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) den[tb] = sy[tb] = 0.f;
+    // two walks over the blocks (den and s, then dq); W^T only in the second
+    auto want_wt = [&](int it) { return it >= nfb; };
+    copy_image(0, 0, false);
     for (int fb = 0; fb < nfb; ++fb) {
+      const char* im = next_image(fb, 2 * nfb, want_wt);
+      if (!active) continue;
       F wfr[SP::NS][NKD], rf[SP::NS][NKD];
-      wproj(fb, wfr);
-      rows(fb, rf);
-      const f32x16 zr = zrows(fb);
+      wproj(im, wfr);
+      rows(im, rf);
+      const f32x16 zr = zrows(im);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const f32x16 phi = features(wfr, tb, fb);
@@ -627,16 +732,18 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       den[tb] = half_sum(den[tb]) + a.eps;
       sy[tb] = half_sum(sy[tb]);
       ratio[tb] = sy[tb] / den[tb];
-      if (ok[tb] && hh == 0) {
+      if (active && ok[tb] && hh == 0) {
         a.lg[(size_t)bh * a.L + tok[tb]] = log2f(den[tb]);
         a.cw[(size_t)bh * a.L + tok[tb]] = -ratio[tb];
       }
     }
     for (int fb = 0; fb < nfb; ++fb) {
+      const char* im = next_image(nfb + fb, 2 * nfb, want_wt);
+      if (!active) continue;
       F wfr[SP::NS][NKD], rf[SP::NS][NKD];
-      wproj(fb, wfr);
-      rows(fb, rf);
-      const f32x16 zr = zrows(fb);
+      wproj(im, wfr);
+      rows(im, rf);
+      const f32x16 zr = zrows(im);
       f32x16 gq[TB];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
@@ -645,14 +752,16 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
 #pragma unroll
         for (int r = 0; r < 16; ++r) gq[tb][r] *= y[r] - zr[r] * ratio[tb];
       }
-      wt_times(fb, gq, dacc);
+      wt_times(im, gq, dacc);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      if (!ok[tb]) continue;
+      if (!active || !ok[tb]) continue;
       const float inv = 1.f / den[tb];
       const float rs = sy[tb] * a.eps * inv;           // sum_f phi_f (y_f - z_f s/D)
       E* drow = (E*)a.dx + ((size_t)bh * a.L + tok[tb]) * D;
+      float xo[NDB][4][4];
+      x_at_outputs(tb, xo);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -660,7 +769,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
           const int d0 = db * 32 + 8 * i + 4 * hh;
           float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (dacc[tb][db][4 * i + j] - rs * (float)xrow[tb][d0 + j]) * inv;
+          for (int j = 0; j < 4; ++j) v[j] = (dacc[tb][db][4 * i + j] - rs * xo[db][i][j]) * inv;
           store4(drow, d0, v);
         }
     }
@@ -673,12 +782,15 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vacc[tb][db] = zero16();
     }
-    const char* opb = (const char*)a.op + (size_t)bh * a.M * D * ES;
+    copy_image(0, 0, true);
     for (int fb = 0; fb < nfb; ++fb) {
+      const char* im = next_image(fb, nfb, [](int) { return true; });
+      if (!active) continue;
+      const char* opl = im + IMG::kOp * 16;             // dM, operand order, this block
       F wfr[SP::NS][NKD], rf[SP::NS][NKD];
-      wproj(fb, wfr);
-      rows(fb, rf);
-      const f32x16 zr = zrows(fb);
+      wproj(im, wfr);
+      rows(im, rf);
+      const f32x16 zr = zrows(im);
       f32x16 gk[TB];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) gk[tb] = features(wfr, tb, fb);
@@ -686,10 +798,9 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       if constexpr (VPS == 8) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const int gi = 2 * fb + s2;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const F mf = *(const u32x4*)(opb + ((gi * 2 + hh) * D + db * 32 + l32) * 16);
+            const F mf = *(const u32x4*)(opl + ((s2 * 2 + hh) * D + db * 32 + l32) * 16);
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) vacc[tb][db] = Tr::mma(mf, CFrag<Tr>::make(gk[tb], s2), vacc[tb][db]);
           }
@@ -697,10 +808,9 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
       } else {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          const int gi = 4 * fb + s4;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const f32x4 mf = *(const f32x4*)(opb + ((gi * 2 + hh) * D + db * 32 + l32) * 16);
+            const f32x4 mf = *(const f32x4*)(opl + ((s4 * 2 + hh) * D + db * 32 + l32) * 16);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -717,14 +827,16 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
           rs[tb] += gk[tb][r];
         }
       }
-      wt_times(fb, gk, dacc);
+      wt_times(im, gk, dacc);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const float rsum = half_sum(rs[tb]);
-      if (!ok[tb]) continue;
+      if (!active || !ok[tb]) continue;
       E* drow = (E*)a.dx + ((size_t)bh * a.L + tok[tb]) * D;
       E* vrow = (E*)a.dy + ((size_t)bh * a.L + tok[tb]) * D;
+      float xo[NDB][4][4];
+      x_at_outputs(tb, xo);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -733,7 +845,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
           float v[4], dv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            v[j] = dacc[tb][db][4 * i + j] - rsum * (float)xrow[tb][d0 + j];
+            v[j] = dacc[tb][db][4 * i + j] - rsum * xo[db][i][j];
             dv[j] = vacc[tb][db][4 * i + j];
           }
           store4(drow, d0, v);
@@ -793,7 +905,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   constexpr int TB = (Tr::VPS == 8 && D <= 64) ? 2 : 1;
   const int tph = (p.L + 32 * TB - 1) / (32 * TB);
   const int total = p.BH * tph;
-  const dim3 sgrid((total + 3) / 4);
+  const dim3 sgrid(p.BH * ((tph + 3) / 4));            // four groups of one head per workgroup
   // state M, z from K, V
   {
     BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
@@ -810,7 +922,8 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     BSideArgs a{t.q, t.g, b.rows_hi, b.rows_lo, nullptr, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dq, nullptr, b.lg, b.cw,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_Q, s);
-    hipLaunchKernelGGL((k_bside<Tr, D, true, TB>), sgrid, dim3(256), 0, s, a);
+    constexpr size_t lds = 2 * BSideImg<Tr, D, true>::BYTES;
+    hipLaunchKernelGGL((k_bside<Tr, D, true, TB>), sgrid, dim3(256), lds, s, a);
     timing_end(FAVOR_KERNEL_BWD_Q, s);
   }
   // dM, dz from Q, G
@@ -829,7 +942,8 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     BSideArgs a{t.k, t.v, b.rows_hi, b.rows_lo, b.op, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dk, t.dv, nullptr, nullptr,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_K, s);
-    hipLaunchKernelGGL((k_bside<Tr, D, false, TB>), sgrid, dim3(256), 0, s, a);
+    constexpr size_t lds = 2 * BSideImg<Tr, D, false>::BYTES;
+    hipLaunchKernelGGL((k_bside<Tr, D, false, TB>), sgrid, dim3(256), lds, s, a);
     timing_end(FAVOR_KERNEL_BWD_K, s);
   }
   return hipGetLastError();
