@@ -220,10 +220,26 @@ __global__ __launch_bounds__(256) void k_bred(BRedArgs a) {
   const int ntiles = t0 < t1 ? (t1 - t0 + TT - 1) / TT : 0;
 
   TL xl, yl;
-  if (ntiles > 0) {
-    xl.load(X + (size_t)t0 * D, t1 - t0, tid);
-    yl.load(Y + (size_t)t0 * D, t1 - t0, tid);
-  }
+  // weighted form: the per-token exponent shift and weight of a tile's rows,
+  // loaded with the tile (one tile ahead) by the threads that own the rows
+  float plg[TL::NCH], pcw[TL::NCH];
+  auto load_tile = [&](int r0) {
+    xl.load(X + (size_t)r0 * D, t1 - r0, tid);
+    yl.load(Y + (size_t)r0 * D, t1 - r0, tid);
+    if constexpr (WT) {
+#pragma unroll
+      for (int i = 0; i < TL::NCH; ++i) {
+        const int c = tid + i * NT, row = c / CPR;
+        plg[i] = 0.f;
+        pcw[i] = 0.f;
+        if (c < TT * CPR && (c % CPR) == 0 && row < t1 - r0) {
+          plg[i] = a.lg[(size_t)bh * a.L + r0 + row];
+          pcw[i] = a.cw[(size_t)bh * a.L + r0 + row];
+        }
+      }
+    }
+  };
+  if (ntiles > 0) load_tile(t0);
   for (int tt = 0; tt < ntiles; ++tt) {
     char* buf = smem + (tt & 1) * LY::BUF;
     const int r0 = t0 + tt * TT;
@@ -256,8 +272,8 @@ __global__ __launch_bounds__(256) void k_bred(BRedArgs a) {
             b = -(0.5f * ss + half_ln_m) * kLog2e;
             wt = 1.f;
             if constexpr (WT) {
-              b -= a.lg[(size_t)bh * a.L + r0 + row];
-              wt = a.cw[(size_t)bh * a.L + r0 + row];
+              b -= plg[i];
+              wt = pcw[i];
             }
           }
           sb[row] = b;
@@ -266,11 +282,7 @@ __global__ __launch_bounds__(256) void k_bred(BRedArgs a) {
       }
     }
     __syncthreads();
-    if (tt + 1 < ntiles) {
-      const int n0 = r0 + TT;
-      xl.load(X + (size_t)n0 * D, t1 - n0, tid);
-      yl.load(Y + (size_t)n0 * D, t1 - n0, tid);
-    }
+    if (tt + 1 < ntiles) load_tile(r0 + TT);
     if (active) {
       const float* sb = (const float*)(buf + LY::kBias);
       const float* sw = (const float*)(buf + LY::kW);
@@ -1644,7 +1656,10 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
           for (int g = 0; g < 4; ++g)
             *(f32x4*)(rrow + db * 32 + 8 * g + 4 * hh) =
                 f32x4{rr[db][4 * g], rr[db][4 * g + 1], rr[db][4 * g + 2], rr[db][4 * g + 3]};
-        __syncthreads();
+        // LDS-only barriers from here on: __syncthreads would also wait for
+        // the next chunk's tile prefetch and the loads requested above
+        wait_lgkm0();
+        raw_barrier();
         float* vv = round == 0 ? v1 : v2;
 #pragma unroll
         for (int j = 0; j < DP; ++j) vv[j] = 0.f;
@@ -1671,9 +1686,15 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
             for (int j = 0; j < DP; ++j) ar[j] = vv[j];
           }
         }
-        if (round + 1 < NROUND) __syncthreads();         // before the next round overwrites sRed
+        if (round + 1 < NROUND) {                        // before the next round overwrites sRed
+          wait_lgkm0();
+          raw_barrier();
+        }
       }
-      if constexpr (NROUND == 0) __syncthreads();        // the scalars are in LDS
+      if constexpr (NROUND == 0) {                       // the scalars are in LDS
+        wait_lgkm0();
+        raw_barrier();
+      }
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
         sc1 += sRedS[(ww * C + tq) * 2];
