@@ -1172,8 +1172,12 @@ __device__ __forceinline__ f32x16 rows_of(const float* v, int hh) {
 //            s_i = phi(q_i).y_i, written as log2 D_i and c_i = -s_i/D_i;
 // MODE kQ2: its second walk -- per feature u = y - z s_i/D_i (float32, where
 //            the difference cancels), dq_i = (W^T (phi(q_i) * u) - (s_i eps/D_i) q_i)/D_i;
-// MODE kK:  the key side, walking the chunks of a span in reverse.
-constexpr int kQ1 = 0, kQ2 = 1, kK = 2;
+// MODE kK:  the key side, walking the chunks of a span in reverse;
+// MODE kQF: both query walks in one, where the workgroup's waves hold every
+//            feature block: per chunk, D_i and s_i are summed over the waves
+//            (through LDS, one barrier) before u and dq are formed, with the
+//            same arithmetic and summation order as the two walks.
+constexpr int kQ1 = 0, kQ2 = 1, kK = 2, kQF = 3;
 
 // Two waves per SIMD for the bf16 query walks at d <= 64 (the second walk
 // spills a few registers and runs 30% faster than at one wave), one for the
@@ -1321,7 +1325,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       lk.load(Kg + (size_t)c0 * D, t1 - c0, tid);
       lv.load(Vg + (size_t)c0 * D, t1 - c0, tid);
       lg_.load(Gg + (size_t)c0 * D, t1 - c0, tid);
-      if constexpr (MODE != kQ1) {
+      if constexpr (MODE == kQ2 || MODE == kK) {
         const int r = tid - 64;
         if (sthr && r < t1 - c0) {
           pcw = a.cw[(size_t)bh * a.L + c0 + r];
@@ -1344,7 +1348,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       lg_.store(sG, tid);
       lk.row_bias(sBk, tid, nv, half_ln_m);
       lq.row_bias(sBq, tid, nv, half_ln_m);
-      if constexpr (MODE != kQ1) {
+      if constexpr (MODE == kQ2 || MODE == kK) {
         // per-token log2 D_i and c_i of the first walk: the key side divides
         // the query features by D_i (bias - log2 D_i) and weights them by c_i;
         // the second query walk uses s_i/D_i = -c_i (rows past nv: 0)
@@ -1367,10 +1371,12 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
         r1[db] = zero16();
         r2[db] = zero16();
       }
+      // query side: phi(Q)^T, phi(K), Y^T, Z^T of this wave's block (kept
+      // across the fused walk's exchange of D_i and s_i)
+      f32x16 pq = zero16(), pk = zero16(), y = zero16(), z = zero16();
       if (valid) {
         if constexpr (QSIDE) {
           // phi(Q)^T (rows f, lane i) and phi(K) (rows j, lane f)
-          f32x16 pq = zero16(), pk;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 b4 = *(const f32x4*)(sBk + 8 * g + 4 * hh);
@@ -1408,7 +1414,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
           for (int r = 0; r < 16; ++r)
             if (crow(r, hh) > l32) bm[r] = 0.f;
           // Y^T = S^T-operand x G + phi(K)^T B;  Z^T = z + phi(K)^T T (rows f, lane i)
-          f32x16 y = zero16(), z = rows_of(sZ, hh);
+          z = rows_of(sZ, hh);
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1425,15 +1431,41 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
             y = mma_ss<Tr>(kf, bf, y);
             z = mma_sa<Tr>(kf, tri[s2], z);
           }
-          if constexpr (MODE == kQ1) {
+          if constexpr (MODE == kQ1 || MODE == kQF) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               ps1 = fmaf(pq[r], z[r], ps1);
               ps2 = fmaf(pq[r], y[r], ps2);
             }
-          } else {
+          }
+        }
+      }
+      // fused walk: D_i and s_i over every wave's features, in wave order
+      float fratio = 0.f;
+      if constexpr (MODE == kQF) {
+        {
+          const float a1 = half_sum(ps1), a2s = half_sum(ps2);
+          if (hh == 0) {
+            sRedS[(w * C + l32) * 2] = a1;
+            sRedS[(w * C + l32) * 2 + 1] = a2s;
+          }
+        }
+        wait_lgkm0();
+        raw_barrier();
+        float d1 = 0.f, d2 = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          d1 += sRedS[(ww * C + l32) * 2];
+          d2 += sRedS[(ww * C + l32) * 2 + 1];
+        }
+        const float den = d1 + a.eps;
+        fratio = -(-(d2 / den));                       // as -c_i of the first walk
+      }
+      if (valid) {
+        if constexpr (QSIDE) {
+          if constexpr (MODE == kQ2 || MODE == kQF) {
             // u = y - z s/D in float32, then dq^T += W^T (phi * u) (rows d, lane i)
-            const float ratio = -sC[l32];
+            const float ratio = MODE == kQF ? fratio : -sC[l32];
             f32x16 gq;
 #pragma unroll
             for (int r = 0; r < 16; ++r) gq[r] = pq[r] * (y[r] - z[r] * ratio);
@@ -1579,10 +1611,10 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       const int tq = rt ? tid >> 3 : 0, d0 = (tid & 7) * DP;
       const bool own = rt && tq < nv;
       const size_t tokq = (size_t)c0 + tq;
-      constexpr int NRND = MODE == kQ1 ? 0 : (MODE == kQ2 ? 1 : 2);
+      constexpr int NRND = MODE == kQ1 ? 0 : (MODE == kK ? 2 : 1);
       float xrow[DP], carried[NRND > 0 ? NRND * DP : 1], cs1 = 0.f, cs2 = 0.f, lgq = 0.f, cwq = 0.f;
       if constexpr (MODE != kQ1) {
-        const E* xr = (MODE == kQ2 ? Qg : Kg) + tokq * D + d0;
+        const E* xr = (QSIDE ? Qg : Kg) + tokq * D + d0;
         const bool need = own && fg + 1 == a.fgroups;
         if constexpr (sizeof(E) == 2 && DP == 4) {
           u32x2 x2 = {0u, 0u};
@@ -1627,7 +1659,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
             for (int j = 0; j < DP; ++j) carried[rd * DP + j] = ar[rd * D + d0 + j];   // rows 8-byte aligned
         }
       }
-      if (a.fgroups > 1 && fg > 0 && own && MODE != kQ2) {
+      if (a.fgroups > 1 && fg > 0 && own && (MODE == kQ1 || MODE == kK)) {
         const float* as = a.acc + ((size_t)bh * a.L + tokq) * AW + 2 * D;
         cs1 = as[0];
         cs2 = as[1];
@@ -1639,7 +1671,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       // threads 0..255: eight per token of the chunk (rt, tq, d0 above)
       constexpr int NROUND = NRND;
       float v1[DP], v2[DP], sc1 = 0.f, sc2 = 0.f;
-      {
+      if constexpr (MODE != kQF) {                       // (the fused walk wrote them mid-chunk)
         const float a1 = half_sum(ps1), a2s = half_sum(ps2);
         if (hh == 0) {
           sRedS[(w * C + l32) * 2] = a1;
@@ -1700,7 +1732,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
         sc1 += sRedS[(ww * C + tq) * 2];
         sc2 += sRedS[(ww * C + tq) * 2 + 1];
       }
-      if (a.fgroups > 1 && rt && tq < nv && MODE != kQ2) {
+      if (a.fgroups > 1 && rt && tq < nv && (MODE == kQ1 || MODE == kK)) {
         float* as = accrow + (size_t)tq * AW + 2 * D;
         if (fg > 0) {
           sc1 += cs1;
@@ -1719,9 +1751,19 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
             a.lg_out[(size_t)bh * a.L + tok] = log2f(den);
             a.cw_out[(size_t)bh * a.L + tok] = -(sc2 / den);
           }
-        } else if constexpr (MODE == kQ2) {
-          const float inv = exp2f(-lgq);
-          const float ratio = -cwq;
+        } else if constexpr (MODE == kQ2 || MODE == kQF) {
+          float lgv = lgq, cwv = cwq;
+          if constexpr (MODE == kQF) {                   // the first walk's outputs, formed here
+            const float den = sc1 + a.eps;
+            lgv = log2f(den);
+            cwv = -(sc2 / den);
+            if ((tid & 7) == 0) {
+              a.lg_out[(size_t)bh * a.L + tok] = lgv;
+              a.cw_out[(size_t)bh * a.L + tok] = cwv;
+            }
+          }
+          const float inv = exp2f(-lgv);
+          const float ratio = -cwv;
           float o[DP];
 #pragma unroll
           for (int j = 0; j < DP; ++j) o[j] = (v1[j] - ratio * a.eps * xrow[j]) * inv;
@@ -1757,7 +1799,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   const int nq = (p.M * D + p.M) / 4;
   const dim3 sgrid((nq + 255) / 256, p.BH);
   constexpr int NWQ = bcausal_nw<Tr, D, kQ1>(), NWK = bcausal_nw<Tr, D, kK>();
-  static_assert(bcausal_nw<Tr, D, kQ2>() == NWQ, "one wave count for both query walks");
+  static_assert(bcausal_nw<Tr, D, kQ2>() == NWQ && bcausal_nw<Tr, D, kQF>() == NWQ, "one wave count for the query walks");
   const int nfb = p.M / 32;
   const int fgq = (nfb + NWQ - 1) / NWQ, fgk = (nfb + NWK - 1) / NWK;
   if ((fgq > 1 || fgk > 1) && p.boff_acc == p.btotal) return kErrPlan;   // no room for the sums
@@ -1777,8 +1819,12 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   // query side: log2 D_i and c_i (the lg and cw arrays), then dQ
   timing_begin(FAVOR_KERNEL_BWD_Q, s);
   const size_t qlds = BCLds<Tr, D, NWQ>::kTotal;
-  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ1, NWQ>), dim3(p.bsplits, p.BH), dim3(NWQ * 64), qlds, s, ca);
-  hipLaunchKernelGGL((k_bcausal<Tr, D, kQ2, NWQ>), dim3(p.bsplits, p.BH), dim3(NWQ * 64), qlds, s, ca);
+  if (fgq == 1) {                                         // every feature block in one workgroup
+    hipLaunchKernelGGL((k_bcausal<Tr, D, kQF, NWQ>), dim3(p.bsplits, p.BH), dim3(NWQ * 64), qlds, s, ca);
+  } else {
+    hipLaunchKernelGGL((k_bcausal<Tr, D, kQ1, NWQ>), dim3(p.bsplits, p.BH), dim3(NWQ * 64), qlds, s, ca);
+    hipLaunchKernelGGL((k_bcausal<Tr, D, kQ2, NWQ>), dim3(p.bsplits, p.BH), dim3(NWQ * 64), qlds, s, ca);
+  }
   timing_end(FAVOR_KERNEL_BWD_Q, s);
   // span aggregates of phi'(Q) G^T, phi'(Q) c -> exclusive suffixes
   {
