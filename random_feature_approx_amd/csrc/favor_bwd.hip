@@ -432,11 +432,18 @@ struct BSideArgs {
   int mt;                 // rows of W per head as given; features past them are padding, phi = 0
 };
 
-// Waves per SIMD the compiler must fit: two for the bf16 query side at d <= 64
-// (a few registers spill outside the hot loop; measured 11% faster than one),
-// one elsewhere (forcing two spills dozens of registers inside it).
+// Work split of the per-token side: TB 32-token blocks per wave and NWB
+// waves per workgroup (sharing each LDS image), compiled for bside_waves
+// waves per SIMD.  bf16 at d <= 64: one block per wave, eight waves, two per
+// SIMD on both sides (no spills; measured on the long workload against two
+// blocks per wave in four-wave workgroups: query side 244 -> 226 us, key
+// side 225 -> 193 us); elsewhere the register file holds one wave per SIMD.
 template <class Tr, int D, bool SIDE_Q>
-constexpr int bside_waves() { return (Tr::VPS == 8 && D <= 64 && SIDE_Q) ? 2 : 1; }
+constexpr int bside_waves() { return (Tr::VPS == 8 && D <= 64) ? 2 : 1; }
+template <class Tr, int D>
+constexpr int bside_tb() { return 1; }
+template <class Tr, int D>
+constexpr int bside_nwb() { return (Tr::VPS == 8 && D <= 64) ? 8 : 4; }
 
 // The per-head operands of one 32-feature block, as one workgroup's LDS
 // image (16-byte chunks, each region in the order its fragments are read:
@@ -462,8 +469,8 @@ struct BSideImg {
   static constexpr int BYTES = CHUNKS * 16;
 };
 
-template <class Tr, int D, bool SIDE_Q, int TB>
-__global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(BSideArgs a) {
+template <class Tr, int D, bool SIDE_Q, int TB, int NWB>
+__global__ __launch_bounds__(NWB * 64, (bside_waves<Tr, D, SIDE_Q>() * 4 >= NWB ? bside_waves<Tr, D, SIDE_Q>() * 4 / NWB : 1)) void k_bside(BSideArgs a) {
   using E = typename Tr::elem;
   using F = typename Tr::frag;
   using SP = Bw<Tr>;
@@ -478,10 +485,10 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  // workgroup = 4 consecutive groups of TB x 32 tokens of one head; waves
+  // workgroup = NWB consecutive groups of TB x 32 tokens of one head; waves
   // past the head's last group take part in the copies and barriers only
-  const int wgs_per_head = (a.tiles_per_head + 3) / 4;
-  const int bh = blockIdx.x / wgs_per_head, tile = (blockIdx.x % wgs_per_head) * 4 + w;
+  const int wgs_per_head = (a.tiles_per_head + NWB - 1) / NWB;
+  const int bh = blockIdx.x / wgs_per_head, tile = (blockIdx.x % wgs_per_head) * NWB + w;
   const bool active = tile < a.tiles_per_head;
   const int head = bh % a.H;
   const int nfb = a.M >> 5;
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(256, (bside_waves<Tr, D, SIDE_Q>())) void k_bside(B
   // query side walks the blocks twice)
   auto img = [&](int step) -> char* { return smem + (step & 1) * IMG::BYTES; };
   auto copy_region = [&](char* dst, int nchunks, auto src_of) {
-    for (int c0 = w * 64; c0 < nchunks; c0 += 256) {
+    for (int c0 = w * 64; c0 < nchunks; c0 += NWB * 64) {
       const int c = c0 + lane;
       if (c < nchunks) __builtin_amdgcn_global_load_lds(FAVOR_GLB(src_of(c)), LDS_PTR(void, dst + c0 * 16), 16, 0, 0);
     }
@@ -913,11 +920,12 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   const int nq = (p.M * D + p.M) / 4;
   const dim3 cgrid((nq + kBQuads - 1) / kBQuads, p.BH);
   E* rlo = Tr::VPS == 8 ? (E*)b.rows_lo : nullptr;
-  // per-token side: TB 32-token blocks per wave share each operand read
-  constexpr int TB = (Tr::VPS == 8 && D <= 64) ? 2 : 1;
+  // per-token side: TB 32-token blocks per wave share each operand read,
+  // NWB groups of one head per workgroup
+  constexpr int TB = bside_tb<Tr, D>(), NWB = bside_nwb<Tr, D>();
   const int tph = (p.L + 32 * TB - 1) / (32 * TB);
   const int total = p.BH * tph;
-  const dim3 sgrid(p.BH * ((tph + 3) / 4));            // four groups of one head per workgroup
+  const dim3 sgrid(p.BH * ((tph + NWB - 1) / NWB));
   // state M, z from K, V
   {
     BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
@@ -935,7 +943,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_Q, s);
     constexpr size_t lds = 2 * BSideImg<Tr, D, true>::BYTES;
-    hipLaunchKernelGGL((k_bside<Tr, D, true, TB>), sgrid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_bside<Tr, D, true, TB, NWB>), sgrid, dim3(NWB * 64), lds, s, a);
     timing_end(FAVOR_KERNEL_BWD_Q, s);
   }
   // dM, dz from Q, G
@@ -955,7 +963,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_K, s);
     constexpr size_t lds = 2 * BSideImg<Tr, D, false>::BYTES;
-    hipLaunchKernelGGL((k_bside<Tr, D, false, TB>), sgrid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_bside<Tr, D, false, TB, NWB>), sgrid, dim3(NWB * 64), lds, s, a);
     timing_end(FAVOR_KERNEL_BWD_K, s);
   }
   return hipGetLastError();
