@@ -1325,8 +1325,11 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
     auto chunk0 = [&](int ci) { return t0 + ci * C; };
     // per-token scalars of the first query walk (c_i; log2 D_i for the key
     // side), loaded one chunk ahead with the tiles by the threads that stage them
-    float pcw = 0.f, plg = 0.f;
+    float pcw = 0.f;
     const bool sthr = tid >= 64 && tid < 64 + C;
+    // key side: log2 D_i of the rows whose chunk 0 this thread stages (the
+    // query features enter divided by D_i, as a shift of their row bias)
+    float plgr[decltype(lq)::NCH];
     auto prefetch = [&](int ci) {
       const int c0 = chunk0(ci);
       lq.load(Qg + (size_t)c0 * D, t1 - c0, tid);
@@ -1335,12 +1338,14 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       lg_.load(Gg + (size_t)c0 * D, t1 - c0, tid);
       if constexpr (MODE == kQ2 || MODE == kK) {
         const int r = tid - 64;
-        if (sthr && r < t1 - c0) {
-          pcw = a.cw[(size_t)bh * a.L + c0 + r];
-          if constexpr (MODE == kK) plg = a.lg[(size_t)bh * a.L + c0 + r];
-        } else {
-          pcw = 0.f;
-          plg = 0.f;
+        pcw = sthr && r < t1 - c0 ? a.cw[(size_t)bh * a.L + c0 + r] : 0.f;
+      }
+      if constexpr (MODE == kK) {
+#pragma unroll
+        for (int i = 0; i < decltype(lq)::NCH; ++i) {
+          const int c = tid + i * NT, row = c / decltype(lq)::CPR;
+          plgr[i] = c < C * decltype(lq)::CPR && c % decltype(lq)::CPR == 0 && row < t1 - c0
+                        ? a.lg[(size_t)bh * a.L + c0 + row] : 0.f;
         }
       }
     };
@@ -1355,21 +1360,17 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       lv.store(sV, tid);
       lg_.store(sG, tid);
       lk.row_bias(sBk, tid, nv, half_ln_m);
-      lq.row_bias(sBq, tid, nv, half_ln_m);
+      if constexpr (MODE == kK)
+        lq.row_bias_shifted(sBq, tid, nv, half_ln_m, plgr);   // bias - log2 D_i; rows past nv: -inf
+      else
+        lq.row_bias(sBq, tid, nv, half_ln_m);
       if constexpr (MODE == kQ2 || MODE == kK) {
         // per-token log2 D_i and c_i of the first walk: the key side divides
         // the query features by D_i (bias - log2 D_i) and weights them by c_i;
         // the second query walk uses s_i/D_i = -c_i (rows past nv: 0)
-        if (sthr) {
-          sC[tid - 64] = pcw;
-          if constexpr (MODE == kK) sRedS[tid - 64] = plg;
-        }
+        if (sthr) sC[tid - 64] = pcw;
       }
       __syncthreads();
-      if constexpr (MODE == kK) {
-        if (tid < C) sBq[tid] -= sRedS[tid];             // rows past nv stay -inf
-        __syncthreads();
-      }
       if (it + 1 < nch) prefetch(QSIDE ? ci + 1 : ci - 1);
 
       f32x16 r1[NDB], r2[NDB];                          // per-token partial outputs (rows d, lane token)
