@@ -1062,6 +1062,36 @@ __device__ __forceinline__ void store_row(E* dst, const float (&v)[DP]) {
   }
 }
 
+// TileLoader::row_bias with a per-row amount subtracted from the FAVOR+ bias
+// of each valid row: shift[i] belongs to the row of the thread's chunk i (used
+// where the thread holds chunk 0 of the row); rows at or past nvalid get -inf.
+template <class E, int D, int TT, int NT>
+__device__ __forceinline__ void row_bias_shifted(const TileLoader<E, D, TT, NT>& t, float* sb, int tid, int nvalid,
+                                                 float half_ln_m, const float (&shift)[TileLoader<E, D, TT, NT>::NCH]) {
+  using TL = TileLoader<E, D, TT, NT>;
+  constexpr int CPR = TL::CPR;
+#pragma unroll
+  for (int i = 0; i < TL::NCH; ++i) {
+    const int c = tid + i * NT;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (sizeof(E) == 2) {
+        const float a = bf16_lo(t.r[i][j]), b = bf16_hi(t.r[i][j]);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      } else {
+        const float a = as_f32(t.r[i][j]);
+        ss = fmaf(a, a, ss);
+      }
+    }
+    ss = group_sum<CPR>(ss);
+    const int row = c / CPR;
+    if (c < TT * CPR && (c % CPR) == 0)
+      sb[row] = row < nvalid ? FMap<FM_POS>::row_bias(ss, half_ln_m) - shift[i] : -INFINITY;
+  }
+}
+
 struct BCausalArgs {
   const void* q;
   const void* k;
@@ -1361,7 +1391,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       lg_.store(sG, tid);
       lk.row_bias(sBk, tid, nv, half_ln_m);
       if constexpr (MODE == kK)
-        lq.row_bias_shifted(sBq, tid, nv, half_ln_m, plgr);   // bias - log2 D_i; rows past nv: -inf
+        row_bias_shifted(lq, sBq, tid, nv, half_ln_m, plgr);   // bias - log2 D_i; rows past nv: -inf
       else
         lq.row_bias(sBq, tid, nv, half_ln_m);
       if constexpr (MODE == kQ2 || MODE == kK) {

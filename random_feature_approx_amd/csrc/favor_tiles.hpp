@@ -121,32 +121,6 @@ struct TileLoader {
         sb[row] = row < nvalid ? FMap<FM>::row_bias(ss, half_ln_m) : -INFINITY;
     }
   }
-  // The same with a per-row amount subtracted from the bias of each valid
-  // row: shift[i] belongs to the row of this thread's chunk i (used where that
-  // thread holds chunk 0 of the row).
-  __device__ __forceinline__ void row_bias_shifted(float* sb, int tid, int nvalid, float half_ln_m,
-                                                   const float (&shift)[NCH]) const {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      int c = tid + i * NT;
-      float ss = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (sizeof(E) == 2) {
-          float a = bf16_lo(r[i][j]), b = bf16_hi(r[i][j]);
-          ss = fmaf(a, a, ss);
-          ss = fmaf(b, b, ss);
-        } else {
-          float a = as_f32(r[i][j]);
-          ss = fmaf(a, a, ss);
-        }
-      }
-      ss = group_sum<CPR>(ss);
-      int row = c / CPR;
-      if (c < TT * CPR && (c % CPR) == 0)
-        sb[row] = row < nvalid ? FMap<FM_POS>::row_bias(ss, half_ln_m) - shift[i] : -INFINITY;
-    }
-  }
 };
 
 // Projection fragment of W (lane = feature f, d-major slots), scaled by the
