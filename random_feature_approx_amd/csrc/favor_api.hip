@@ -155,10 +155,12 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   // (k_causal_x3: one copy per wave)
   if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * sizeof(float) * (p.x3 ? 4 : 1));
   p.total = off;
-  // backward: 4 feature blocks per reduction workgroup, about two
-  // workgroups per compute unit; the causal backward reduces over the spans
+  // backward reductions: one wave per feature block, eight waves per
+  // workgroup (one workgroup per compute unit) for bf16 at d <= 64, else four
+  // (about two per compute unit); the causal backward reduces over the spans
   // of the forward's chunk scan
-  p.bfgroups = (nfb + 3) / 4;
+  p.brnw = (dt == FAVOR_BF16 && d <= 64) ? 8 : 4;
+  p.bfgroups = (nfb + p.brnw - 1) / p.brnw;
   if (causal) {
     int bl = (L + bwd_splits - 1) / bwd_splits;
     bl = (bl + 63) / 64 * 64;
@@ -166,7 +168,8 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
     p.bsplits = (L + bl - 1) / bl;
   } else {
     const int per = p.BH * p.bfgroups;
-    int bs = (target + per - 1) / per;
+    const int btarget = (p.brnw == 8 ? 1 : 2) * num_cus;
+    int bs = (btarget + per - 1) / per;
     if (bs > max_splits) bs = max_splits;
     if (bs < 1) bs = 1;
     int bl = (L + bs - 1) / bs;
@@ -199,10 +202,11 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   bo += align256((size_t)p.BH * m * d * p.esize);
   p.boff_op = bo;
   bo += align256((size_t)p.BH * m * d * p.esize);
-  // causal with more than one feature group: float32 per-token sums carried
+  // causal walks with more than one feature group (the key walk's workgroup
+  // holds four blocks, a query walk's bqnw): float32 per-token sums carried
   // from one group to the next (2 d + 2 per token)
   p.boff_acc = bo;
-  if (causal && p.bfgroups > 1) bo += align256((size_t)p.BH * L * (2 * d + 2) * sizeof(float));
+  if (causal && (nfb > 4 || nfb > p.bqnw)) bo += align256((size_t)p.BH * L * (2 * d + 2) * sizeof(float));
   p.btotal = bo;
   return true;
 }

@@ -159,9 +159,9 @@ struct BRedLds {
   static constexpr int kTotal = 2 * BUF;
 };
 
-template <class Tr, int D, bool WT>
-__global__ __launch_bounds__(256) void k_bred(BRedArgs a) {
-  constexpr int NW = 4, NT = 256, TT = 32;
+template <class Tr, int D, bool WT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_bred(BRedArgs a) {
+  constexpr int NT = NW * 64, TT = 32;
   using E = typename Tr::elem;
   using F = typename Tr::frag;
   using LY = BRedLds<Tr, D>;
@@ -915,6 +915,9 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
                        Tr::VPS == 8 ? b.wtl : nullptr, nrows, D, p.M, p.mt);
     timing_end(FAVOR_KERNEL_BWD_PREP, s);
   }
+  // reduction workgroups: one wave per feature block, NWR blocks (the plan's brnw)
+  constexpr int NWR = (Tr::VPS == 8 && D <= 64) ? 8 : 4;
+  if (p.brnw != NWR) return kErrPlan;
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
   const size_t rlds = BRedLds<Tr, D>::kTotal;
   const int nq = (p.M * D + p.M) / 4;
@@ -930,7 +933,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   {
     BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, false>), rgrid, dim3(256), rlds, s, a);
+    hipLaunchKernelGGL((k_bred<Tr, D, false, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL((k_bcombine<E>), cgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, (E*)b.rows_hi, rlo,
@@ -950,7 +953,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   {
     BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, true>), rgrid, dim3(256), rlds, s, a);
+    hipLaunchKernelGGL((k_bred<Tr, D, true, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL((k_bcombine<E>), cgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, (E*)b.rows_hi, rlo,
@@ -1833,6 +1836,9 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
                        Tr::VPS == 8 ? b.wtl : nullptr, nrows, D, p.M, p.mt);
     timing_end(FAVOR_KERNEL_BWD_PREP, s);
   }
+  // reduction workgroups: one wave per feature block, NWR blocks (the plan's brnw)
+  constexpr int NWR = (Tr::VPS == 8 && D <= 64) ? 8 : 4;
+  if (p.brnw != NWR) return kErrPlan;
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
   const size_t rlds = BRedLds<Tr, D>::kTotal;
   const int nq = (p.M * D + p.M) / 4;
@@ -1849,7 +1855,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   {
     BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, false>), rgrid, dim3(256), rlds, s, a);
+    hipLaunchKernelGGL((k_bred<Tr, D, false, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL(k_bscan, sgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, 0);
@@ -1869,7 +1875,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   {
     BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, true>), rgrid, dim3(256), rlds, s, a);
+    hipLaunchKernelGGL((k_bred<Tr, D, true, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL(k_bscan, sgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, 1);

@@ -48,6 +48,7 @@ struct Plan {
   // its workspace (a separate layout, sized by favor_bwd_workspace_bytes)
   int bsplits, bsplit_len, bfgroups;
   int bqnw;              // causal backward: waves of a query-walk workgroup
+  int brnw;              // backward reductions: waves (feature blocks) per workgroup
   size_t boff_part, boff_partz, boff_zf, boff_lg, boff_cw, boff_wph, boff_wpl, boff_wt, boff_wtl, boff_rows_hi,
       boff_rows_lo, boff_op, boff_acc, btotal;
 };
