@@ -156,10 +156,10 @@ bool make_plan(Plan& p, int B, int H, int L, int d, int m, int Hw, int causal, f
   if (causal && p.fgroups > 1) off += align256((size_t)p.BH * L * sizeof(float) * (p.x3 ? 4 : 1));
   p.total = off;
   // backward reductions: one wave per feature block, eight waves per
-  // workgroup (one workgroup per compute unit) for bf16 at d <= 64, else four
-  // (about two per compute unit); the causal backward reduces over the spans
-  // of the forward's chunk scan
-  p.brnw = (dt == FAVOR_BF16 && d <= 64) ? 8 : 4;
+  // workgroup (one workgroup per compute unit) for bf16 at d <= 64 with more
+  // than four blocks, else four (about two per compute unit); the causal
+  // backward reduces over the spans of the forward's chunk scan
+  p.brnw = (dt == FAVOR_BF16 && d <= 64 && nfb > 4) ? 8 : 4;
   p.bfgroups = (nfb + p.brnw - 1) / p.brnw;
   if (causal) {
     int bl = (L + bwd_splits - 1) / bwd_splits;

@@ -915,11 +915,21 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
                        Tr::VPS == 8 ? b.wtl : nullptr, nrows, D, p.M, p.mt);
     timing_end(FAVOR_KERNEL_BWD_PREP, s);
   }
-  // reduction workgroups: one wave per feature block, NWR blocks (the plan's brnw)
-  constexpr int NWR = (Tr::VPS == 8 && D <= 64) ? 8 : 4;
-  if (p.brnw != NWR) return kErrPlan;
+  // reduction workgroups: one wave per feature block, the plan's brnw blocks
+  // (eight only for bf16 at d <= 64)
+  constexpr bool kRed8 = Tr::VPS == 8 && D <= 64;
+  if (p.brnw != 4 && !(kRed8 && p.brnw == 8)) return kErrPlan;
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
   const size_t rlds = BRedLds<Tr, D>::kTotal;
+  auto launch_bred = [&]<bool WT>(const BRedArgs& ra) {
+    if constexpr (kRed8) {
+      if (p.brnw == 8) {
+        hipLaunchKernelGGL((k_bred<Tr, D, WT, 8>), rgrid, dim3(512), rlds, s, ra);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((k_bred<Tr, D, WT, 4>), rgrid, dim3(256), rlds, s, ra);
+  };
   const int nq = (p.M * D + p.M) / 4;
   const dim3 cgrid((nq + kBQuads - 1) / kBQuads, p.BH);
   E* rlo = Tr::VPS == 8 ? (E*)b.rows_lo : nullptr;
@@ -933,7 +943,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   {
     BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, false, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
+    launch_bred.template operator()<false>(a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL((k_bcombine<E>), cgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, (E*)b.rows_hi, rlo,
@@ -953,7 +963,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   {
     BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, true, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
+    launch_bred.template operator()<true>(a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL((k_bcombine<E>), cgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, (E*)b.rows_hi, rlo,
@@ -1836,11 +1846,21 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
                        Tr::VPS == 8 ? b.wtl : nullptr, nrows, D, p.M, p.mt);
     timing_end(FAVOR_KERNEL_BWD_PREP, s);
   }
-  // reduction workgroups: one wave per feature block, NWR blocks (the plan's brnw)
-  constexpr int NWR = (Tr::VPS == 8 && D <= 64) ? 8 : 4;
-  if (p.brnw != NWR) return kErrPlan;
+  // reduction workgroups: one wave per feature block, the plan's brnw blocks
+  // (eight only for bf16 at d <= 64)
+  constexpr bool kRed8 = Tr::VPS == 8 && D <= 64;
+  if (p.brnw != 4 && !(kRed8 && p.brnw == 8)) return kErrPlan;
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
   const size_t rlds = BRedLds<Tr, D>::kTotal;
+  auto launch_bred = [&]<bool WT>(const BRedArgs& ra) {
+    if constexpr (kRed8) {
+      if (p.brnw == 8) {
+        hipLaunchKernelGGL((k_bred<Tr, D, WT, 8>), rgrid, dim3(512), rlds, s, ra);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((k_bred<Tr, D, WT, 4>), rgrid, dim3(256), rlds, s, ra);
+  };
   const int nq = (p.M * D + p.M) / 4;
   const dim3 sgrid((nq + 255) / 256, p.BH);
   constexpr int NWQ = bcausal_nw<Tr, D, kQ1>(), NWK = bcausal_nw<Tr, D, kK>();
@@ -1855,7 +1875,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   {
     BRedArgs a{t.k, t.v, nullptr, nullptr, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, false, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
+    launch_bred.template operator()<false>(a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL(k_bscan, sgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, 0);
@@ -1875,7 +1895,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   {
     BRedArgs a{t.q, t.g, b.lg, b.cw, b.wph, b.wpl, b.part, b.partz, p.L, p.M, p.H, p.Hw, p.bsplits, p.bsplit_len, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_REDUCE, s);
-    hipLaunchKernelGGL((k_bred<Tr, D, true, NWR>), rgrid, dim3(NWR * 64), rlds, s, a);
+    launch_bred.template operator()<true>(a);
     timing_end(FAVOR_KERNEL_BWD_REDUCE, s);
     timing_begin(FAVOR_KERNEL_BWD_COMBINE, s);
     hipLaunchKernelGGL(k_bscan, sgrid, dim3(256), 0, s, b.part, b.partz, p.bsplits, p.M, D, 1);
