@@ -1041,12 +1041,25 @@ __global__ __launch_bounds__(256) void k_bscan(float* part, float* partz, int sp
     p = (f32x4*)(partz + (size_t)bh * spans * M) + (quad - md4);
     stride = M / 4;
   }
-  f32x4 run = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < spans; ++k) {
-    const int sp = reverse ? spans - 1 - k : k;
-    const f32x4 v = p[(size_t)sp * stride];
-    p[(size_t)sp * stride] = run;
-    run += v;
+  // eight spans' loads issued together, then their prefixes stored (a load
+  // after a store to the same array would wait for the store's round trip)
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 run = zero;
+  for (int k0 = 0; k0 < spans; k0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j, sp = reverse ? spans - 1 - k : k;
+      v[j] = k < spans ? p[(size_t)sp * stride] : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j, sp = reverse ? spans - 1 - k : k;
+      if (k < spans) {
+        p[(size_t)sp * stride] = run;
+        run += v[j];
+      }
+    }
   }
 }
 
