@@ -1141,7 +1141,7 @@ struct BCausalArgs {
   int mt;                // rows of W per head as given; features past them are padding, phi = 0
 };
 
-template <class Tr, int D, int NW>
+template <class Tr, int D, int NW, bool KEY = false>
 struct BCLds {
   using E = typename Tr::elem;
   static constexpr int C = 32;
@@ -1162,7 +1162,12 @@ struct BCLds {
   static constexpr int WTB = WTF * 64 * (int)sizeof(typename Tr::frag);
   static constexpr bool kStageWt = kBase + NW * WTB <= 160 * 1024;
   static constexpr int kWt = kBase;
-  static constexpr int kTotal = kBase + (kStageWt ? NW * WTB : 0);
+  static constexpr int kEndWt = kBase + (kStageWt ? NW * WTB : 0);
+  // key side, where it fits: a second reduction buffer, so that both per-token
+  // outputs (dk, dv) are summed over the waves after one barrier
+  static constexpr bool kRed2 = KEY && kEndWt + NW * C * RSR * 4 <= 160 * 1024;
+  static constexpr int kRedB = kEndWt;
+  static constexpr int kTotal = kEndWt + (kRed2 ? NW * C * RSR * 4 : 0);
 };
 
 // B operand over d in c-row order (k-step s2 of d block db) from one row of
@@ -1260,7 +1265,7 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
   using E = typename Tr::elem;
   using F = typename Tr::frag;
   using SP = Bw<Tr>;
-  using LY = BCLds<Tr, D, NW>;
+  using LY = BCLds<Tr, D, NW, MODE == kK>;
   constexpr bool QSIDE = MODE != kK;
   constexpr int NT = NW * 64;
   constexpr int C = LY::C;
@@ -1743,26 +1748,31 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
           sRedS[(w * C + l32) * 2 + 1] = a2s;
         }
       }
-#pragma unroll
-      for (int round = 0; round < NROUND; ++round) {
+      // each round: this wave's partial outputs into a reduction buffer, one
+      // barrier, then the sums over the waves in wave order; with a second
+      // buffer (key side) both rounds share one barrier
+      constexpr bool ONEBAR = NROUND == 2 && LY::kRed2;
+      auto red_buf = [&](int round) -> float* {
+        if constexpr (ONEBAR) return round == 0 ? sRed : (float*)(smem + LY::kRedB);
+        return sRed;
+      };
+      auto write_round = [&](int round) {
         f32x16 (&rr)[NDB] = round == 0 ? r1 : r2;
-        float* rrow = sRed + (size_t)w * C * RSR + l32 * RSR;
+        float* rrow = red_buf(round) + (size_t)w * C * RSR + l32 * RSR;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             *(f32x4*)(rrow + db * 32 + 8 * g + 4 * hh) =
                 f32x4{rr[db][4 * g], rr[db][4 * g + 1], rr[db][4 * g + 2], rr[db][4 * g + 3]};
-        // LDS-only barriers from here on: __syncthreads would also wait for
-        // the next chunk's tile prefetch and the loads requested above
-        wait_lgkm0();
-        raw_barrier();
+      };
+      auto sum_round = [&](int round) {
         float* vv = round == 0 ? v1 : v2;
 #pragma unroll
         for (int j = 0; j < DP; ++j) vv[j] = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-          const float* src = sRed + (size_t)ww * C * RSR + tq * RSR + d0;
+          const float* src = red_buf(round) + (size_t)ww * C * RSR + tq * RSR + d0;
 #pragma unroll
           for (int j = 0; j < DP; j += 4) {
             const f32x4 x = *(const f32x4*)(src + j);
@@ -1783,9 +1793,27 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
             for (int j = 0; j < DP; ++j) ar[j] = vv[j];
           }
         }
-        if (round + 1 < NROUND) {                        // before the next round overwrites sRed
+      };
+      // LDS-only barriers from here on: __syncthreads would also wait for
+      // the next chunk's tile prefetch and the loads requested above
+      if constexpr (ONEBAR) {
+        write_round(0);
+        write_round(1);
+        wait_lgkm0();
+        raw_barrier();
+        sum_round(0);
+        sum_round(1);
+      } else {
+#pragma unroll
+        for (int round = 0; round < NROUND; ++round) {
+          write_round(round);
           wait_lgkm0();
           raw_barrier();
+          sum_round(round);
+          if (round + 1 < NROUND) {                      // before the next round overwrites sRed
+            wait_lgkm0();
+            raw_barrier();
+          }
         }
       }
       if constexpr (NROUND == 0) {                       // the scalars are in LDS
@@ -1918,7 +1946,7 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   ca.dx = t.dk;
   ca.dy = t.dv;
   ca.fgroups = fgk;
-  const size_t klds = BCLds<Tr, D, NWK>::kTotal;
+  const size_t klds = BCLds<Tr, D, NWK, true>::kTotal;
   timing_begin(FAVOR_KERNEL_BWD_K, s);
   hipLaunchKernelGGL((k_bcausal<Tr, D, kK, NWK>), dim3(p.bsplits, p.BH), dim3(NWK * 64), klds, s, ca);
   timing_end(FAVOR_KERNEL_BWD_K, s);
