@@ -1415,7 +1415,11 @@ __global__ __launch_bounds__(NW * 64, (bcausal_waves<Tr, D, MODE>())) void k_bca
       const int ci = QSIDE ? it : nch - 1 - it;
       const int c0 = chunk0(ci);
       const int nv = min(C, t1 - c0);
-      __syncthreads();                                   // the previous chunk's reductions are done
+      // No barrier before the staging: every read of the previous chunk's
+      // tiles, biases and weights happens in its products, which end at the
+      // barrier of its cross-wave sums; what follows that barrier (the sums,
+      // the outputs) reads only the reduction buffers, which the next writes
+      // reach only after the staging barrier below.
       lq.store_proj(sQ, tid);
       lk.store_proj(sK, tid);
       lv.store(sV, tid);
