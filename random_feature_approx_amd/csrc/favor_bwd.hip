@@ -146,10 +146,12 @@ struct BRedArgs {
   int mt;                // rows of W per head as given; features past them are padding, phi = 0
 };
 
-template <class Tr, int D>
+template <class Tr, int D, int NWR>
 struct BRedLds {
   using E = typename Tr::elem;
-  static constexpr int TT = 32;
+  // tokens per tile: 64 for eight-wave workgroups (every thread stages one
+  // 16-byte chunk per tensor at d = 64), else 32
+  static constexpr int TT = NWR == 8 ? 64 : 32;
   static constexpr int RS = Rows<D, sizeof(E)>::RS;
   static constexpr int kX = 0;
   static constexpr int kY = kX + TT * RS;
@@ -161,10 +163,12 @@ struct BRedLds {
 
 template <class Tr, int D, bool WT, int NW>
 __global__ __launch_bounds__(NW * 64) void k_bred(BRedArgs a) {
-  constexpr int NT = NW * 64, TT = 32;
+  constexpr int NT = NW * 64;
   using E = typename Tr::elem;
   using F = typename Tr::frag;
-  using LY = BRedLds<Tr, D>;
+  using LY = BRedLds<Tr, D, NW>;
+  constexpr int TT = LY::TT;
+  constexpr int NTB = TT / 32;                // 32-token blocks per tile
   using TL = TileLoader<E, D, TT, NT>;
   using SP = Bw<Tr>;
   constexpr int NKD = D / Tr::KS;
@@ -284,39 +288,42 @@ __global__ __launch_bounds__(NW * 64) void k_bred(BRedArgs a) {
     __syncthreads();
     if (tt + 1 < ntiles) load_tile(r0 + TT);
     if (active) {
-      const float* sb = (const float*)(buf + LY::kBias);
-      const float* sw = (const float*)(buf + LY::kW);
-      f32x16 acc;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 b4 = *(const f32x4*)(sb + 8 * g + 4 * hh);
+      for (int tb = 0; tb < NTB; ++tb) {            // 32-token blocks of the tile
+        const float* sb = (const float*)(buf + LY::kBias) + tb * 32;
+        const float* sw = (const float*)(buf + LY::kW) + tb * 32;
+        f32x16 acc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[4 * g + j] = b4[j];
-      }
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 b4 = *(const f32x4*)(sb + 8 * g + 4 * hh);
 #pragma unroll
-      for (int s = 0; s < NKD; ++s) {
-        const F xf = row_frag<Tr, D>(buf + LY::kX + l32 * RS, hh, s);
+          for (int j = 0; j < 4; ++j) acc[4 * g + j] = b4[j];
+        }
 #pragma unroll
-        for (int p = 0; p < SP::NS; ++p) acc = Tr::pmma(xf, wf[p][s], acc);   // P[t][f] + bias[t]
-      }
+        for (int s = 0; s < NKD; ++s) {
+          const F xf = row_frag<Tr, D>(buf + LY::kX + (tb * 32 + l32) * RS, hh, s);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = exp2_fast(acc[r]);
-      if (fb * 32 + 32 > a.mt && fb * 32 + l32 >= a.mt) acc = zero16();   // padding feature (lane)
+          for (int p = 0; p < SP::NS; ++p) acc = Tr::pmma(xf, wf[p][s], acc);   // P[t][f] + bias[t]
+        }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 w4 = *(const f32x4*)(sw + 8 * g + 4 * hh);
+        for (int r = 0; r < 16; ++r) acc[r] = exp2_fast(acc[r]);
+        if (fb * 32 + 32 > a.mt && fb * 32 + l32 >= a.mt) acc = zero16();   // padding feature (lane)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) zs = fmaf(acc[4 * g + j], w4[j], zs);
-      }
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 w4 = *(const f32x4*)(sw + 8 * g + 4 * hh);
 #pragma unroll
-      for (int s2 = 0; s2 < NKT; ++s2) {
-        F pf[SP::NS];
-        SP::split(acc, s2, pf);
+          for (int j = 0; j < 4; ++j) zs = fmaf(acc[4 * g + j], w4[j], zs);
+        }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const F yf = col_frag<Tr, RS>(buf + LY::kY, 0, db * 32, s2, lane);
+        for (int s2 = 0; s2 < NKT; ++s2) {
+          F pf[SP::NS];
+          SP::split(acc, s2, pf);
 #pragma unroll
-          for (int p = 0; p < SP::NS; ++p) st[db] = Tr::mma(pf[p], yf, st[db]);
+          for (int db = 0; db < NDB; ++db) {
+            const F yf = col_frag<Tr, RS>(buf + LY::kY, tb * 32, db * 32, s2, lane);
+#pragma unroll
+            for (int p = 0; p < SP::NS; ++p) st[db] = Tr::mma(pf[p], yf, st[db]);
+          }
         }
       }
     }
@@ -920,15 +927,15 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
   constexpr bool kRed8 = Tr::VPS == 8 && D <= 64;
   if (p.brnw != 4 && !(kRed8 && p.brnw == 8)) return kErrPlan;
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
-  const size_t rlds = BRedLds<Tr, D>::kTotal;
+  constexpr size_t rlds8 = BRedLds<Tr, D, 8>::kTotal, rlds4 = BRedLds<Tr, D, 4>::kTotal;
   auto launch_bred = [&]<bool WT>(const BRedArgs& ra) {
     if constexpr (kRed8) {
       if (p.brnw == 8) {
-        hipLaunchKernelGGL((k_bred<Tr, D, WT, 8>), rgrid, dim3(512), rlds, s, ra);
+        hipLaunchKernelGGL((k_bred<Tr, D, WT, 8>), rgrid, dim3(512), rlds8, s, ra);
         return;
       }
     }
-    hipLaunchKernelGGL((k_bred<Tr, D, WT, 4>), rgrid, dim3(256), rlds, s, ra);
+    hipLaunchKernelGGL((k_bred<Tr, D, WT, 4>), rgrid, dim3(256), rlds4, s, ra);
   };
   const int nq = (p.M * D + p.M) / 4;
   const dim3 cgrid((nq + kBQuads - 1) / kBQuads, p.BH);
@@ -1896,15 +1903,15 @@ static hipError_t bwd_causal_t(const Plan& p, const BwdTensors& t, hipStream_t s
   constexpr bool kRed8 = Tr::VPS == 8 && D <= 64;
   if (p.brnw != 4 && !(kRed8 && p.brnw == 8)) return kErrPlan;
   const dim3 rgrid(p.bsplits, p.bfgroups, p.BH);
-  const size_t rlds = BRedLds<Tr, D>::kTotal;
+  constexpr size_t rlds8 = BRedLds<Tr, D, 8>::kTotal, rlds4 = BRedLds<Tr, D, 4>::kTotal;
   auto launch_bred = [&]<bool WT>(const BRedArgs& ra) {
     if constexpr (kRed8) {
       if (p.brnw == 8) {
-        hipLaunchKernelGGL((k_bred<Tr, D, WT, 8>), rgrid, dim3(512), rlds, s, ra);
+        hipLaunchKernelGGL((k_bred<Tr, D, WT, 8>), rgrid, dim3(512), rlds8, s, ra);
         return;
       }
     }
-    hipLaunchKernelGGL((k_bred<Tr, D, WT, 4>), rgrid, dim3(256), rlds, s, ra);
+    hipLaunchKernelGGL((k_bred<Tr, D, WT, 4>), rgrid, dim3(256), rlds4, s, ra);
   };
   const int nq = (p.M * D + p.M) / 4;
   const dim3 sgrid((nq + 255) / 256, p.BH);
