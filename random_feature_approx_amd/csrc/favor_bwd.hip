@@ -474,6 +474,10 @@ struct BSideImg {
   static constexpr int kWp = 0, kR = kWp + NS * CWP, kZ = kR + NS * CR, kOp = kZ + CZ, kWt = kOp + COP;
   static constexpr int CHUNKS = kWt + NS * CWT;
   static constexpr int BYTES = CHUNKS * 16;
+  // blocks per step of the walk (one barrier per step): two where four images
+  // fit the LDS, else one
+  static constexpr int G = 4 * BYTES <= 150 * 1024 ? 2 : 1;
+  static constexpr int LDS = 2 * G * BYTES;
 };
 
 template <class Tr, int D, bool SIDE_Q, int TB, int NWB>
@@ -547,9 +551,11 @@ __global__ __launch_bounds__(NWB * 64, (bside_waves<Tr, D, SIDE_Q>() * 4 >= NWB 
 
   const char* opb = SIDE_Q ? nullptr : (const char*)a.op + (size_t)bh * a.M * D * ES;
   // ---- the LDS image of feature block fb: copy, then fragment reads --------
-  // image buffers alternate with the step of the walk (not with fb: the
-  // query side walks the blocks twice)
-  auto img = [&](int step) -> char* { return smem + (step & 1) * IMG::BYTES; };
+  // images by position in the walk (not by fb: the query side walks the
+  // blocks twice): IMG::G consecutive blocks form a step, steps alternate
+  // between two sets of buffers
+  constexpr int G = IMG::G;
+  auto img = [&](int it) -> char* { return smem + (((it / G) & 1) * G + it % G) * IMG::BYTES; };
   auto copy_region = [&](char* dst, int nchunks, auto src_of) {
     for (int c0 = w * 64; c0 < nchunks; c0 += NWB * 64) {
       const int c = c0 + lane;
@@ -721,10 +727,23 @@ __global__ __launch_bounds__(NWB * 64, (bside_waves<Tr, D, SIDE_Q>() * 4 >= NWB 
 
   // one step of the block walk: the image of block fb is complete and every
   // wave is done with the other buffer, whose next image is then requested
+  // the images of the blocks of step g (positions g G .. g G + G - 1)
+  auto copy_step = [&](int g, int nit, auto want_wt) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int it = g * G + i;
+      if (it < nit) copy_image(it % nfb, it, want_wt(it));
+    }
+  };
+  // at the first block of a step: its images are complete (own copies waited
+  // for, everyone's after the barrier) and every wave is done with the other
+  // set of buffers, into which the next step's images are then requested
   auto next_image = [&](int it, int nit, auto want_wt) -> const char* {
-    wait_vmcnt<0>();
-    raw_barrier();
-    if (it + 1 < nit) copy_image((it + 1) % nfb, it + 1, want_wt(it + 1));
+    if (it % G == 0) {
+      wait_vmcnt<0>();
+      raw_barrier();
+      copy_step(it / G + 1, nit, want_wt);
+    }
     return img(it);
   };
   if constexpr (SIDE_Q) {
@@ -733,7 +752,7 @@ __global__ __launch_bounds__(NWB * 64, (bside_waves<Tr, D, SIDE_Q>() * 4 >= NWB 
     for (int tb = 0; tb < TB; ++tb) den[tb] = sy[tb] = 0.f;
     // two walks over the blocks (den and s, then dq); W^T only in the second
     auto want_wt = [&](int it) { return it >= nfb; };
-    copy_image(0, 0, false);
+    copy_step(0, 2 * nfb, want_wt);
     for (int fb = 0; fb < nfb; ++fb) {
       const char* im = next_image(fb, 2 * nfb, want_wt);
       if (!active) continue;
@@ -808,9 +827,10 @@ __global__ __launch_bounds__(NWB * 64, (bside_waves<Tr, D, SIDE_Q>() * 4 >= NWB 
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vacc[tb][db] = zero16();
     }
-    copy_image(0, 0, true);
+    auto all_wt = [](int) { return true; };
+    copy_step(0, nfb, all_wt);
     for (int fb = 0; fb < nfb; ++fb) {
-      const char* im = next_image(fb, nfb, [](int) { return true; });
+      const char* im = next_image(fb, nfb, all_wt);
       if (!active) continue;
       const char* opl = im + IMG::kOp * 16;             // dM, operand order, this block
       F wfr[SP::NS][NKD], rf[SP::NS][NKD];
@@ -962,7 +982,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     BSideArgs a{t.q, t.g, b.rows_hi, b.rows_lo, nullptr, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dq, nullptr, b.lg, b.cw,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_Q, s);
-    constexpr size_t lds = 2 * BSideImg<Tr, D, true>::BYTES;
+    constexpr size_t lds = BSideImg<Tr, D, true>::LDS;
     hipLaunchKernelGGL((k_bside<Tr, D, true, TB, NWB>), sgrid, dim3(NWB * 64), lds, s, a);
     timing_end(FAVOR_KERNEL_BWD_Q, s);
   }
@@ -982,7 +1002,7 @@ static hipError_t bwd_noncausal_t(const Plan& p, const BwdTensors& t, hipStream_
     BSideArgs a{t.k, t.v, b.rows_hi, b.rows_lo, b.op, b.zf, b.wph, b.wpl, b.wt, b.wtl, t.dk, t.dv, nullptr, nullptr,
                 p.L, p.M, p.H, p.Hw, tph, total, t.eps, p.mt};
     timing_begin(FAVOR_KERNEL_BWD_K, s);
-    constexpr size_t lds = 2 * BSideImg<Tr, D, false>::BYTES;
+    constexpr size_t lds = BSideImg<Tr, D, false>::LDS;
     hipLaunchKernelGGL((k_bside<Tr, D, false, TB, NWB>), sgrid, dim3(NWB * 64), lds, s, a);
     timing_end(FAVOR_KERNEL_BWD_K, s);
   }
