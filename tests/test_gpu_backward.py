@@ -45,6 +45,7 @@ def _check(gpu, seed, B, H, L, d, m, dtype, heads_w=None, eps=1e-6, causal=False
     ("bf16", 64, 32, 1, 2, 333),        # smallest m
     ("bf16", 64, 512, 1, 2, 777),       # several feature groups
     ("bf16", 32, 128, 1, 2, 260),
+    ("bf16", 32, 256, 1, 2, 300),       # eight-wave reductions with 64-token tiles at d = 32
     ("bf16", 128, 512, 1, 2, 300),
     ("f32", 32, 256, 1, 2, 500),
     ("f32", 64, 96, 1, 2, 129),
@@ -120,6 +121,7 @@ def test_noncausal_backward_long_sampled(gpu):
     ("bf16", 64, 32, 2, 1, 300),        # smallest m
     ("bf16", 64, 512, 1, 1, 257),       # four feature groups
     ("bf16", 32, 128, 1, 2, 333),
+    ("bf16", 32, 256, 1, 2, 1000),      # fused query walk and eight-wave reductions at d = 32
     ("bf16", 128, 256, 1, 1, 200),
     ("f32", 32, 256, 1, 1, 200),
     ("f32", 64, 96, 1, 2, 130),
